@@ -1,0 +1,84 @@
+"""The GEMM error gate: it must accept legitimate rounding and reject the
+cheap ways of getting the dequantisation wrong.
+
+Accept: a GEMM whose weights were rounded to bf16 before the dot product (the
+int4 decode spec's "Precision" section counts this as legitimate) passes on
+every workload.  Reject: the mistakes that spec lists as drop-the-feature
+mutations (nibbles read high-first, one (scale, zero) per row, zero point
+ignored), plus an off-by-one e8m0 bias and a sign-flipped scale.  Mutations are
+planted in the oracle's inputs on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_bit_w4a16_amd import inputs
+
+CASES = [
+    ("tiny_int4_m16", (oracle.INT4_G128, 16, 256, 512, False)),
+    ("decode_gemv_int4_m1", (oracle.INT4_G128, 1, 8192, 3072, True)),
+    ("nvfp4_m16_reduced_n", (oracle.NVFP4, 16, 512, 8192, True)),
+    ("mxfp4_reduced", (oracle.MXFP4, 64, 256, 3072, True)),
+]
+
+
+def _ref(case):
+    return oracle.gemm(case.fmt, case.A, case.packed, case.scales, case.zeros,
+                       case.M, case.N, case.K)
+
+
+@pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
+def test_bf16_weight_rounding_passes_gate(name, cfg):
+    fmt, M, N, K, bf16_out = cfg
+    case = inputs.make_case(fmt, M, N, K, seed=0)
+    C, S = _ref(case)
+    Cb, _ = oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K,
+                        weights_bf16=True)
+    r = oracle.gate_ratio(Cb, C, S, bf16_out)
+    assert r <= 0.5, r
+    if fmt != oracle.INT4_G128:
+        assert r == 0.0  # fp4 weights are exact in bf16
+
+
+def _swap_nibbles(p):
+    return ((p & 0x0F) << 4) | (p >> 4)
+
+
+def _mutations(case):
+    fmt = case.fmt
+    out = {"nibbles_high_first": (case.A, _swap_nibbles(case.packed), case.scales, case.zeros)}
+    if fmt == oracle.INT4_G128:
+        out["zero_point_ignored"] = (case.A, case.packed, case.scales, np.zeros_like(case.zeros))
+        per_row_s = np.repeat(case.scales[:, :1], case.scales.shape[1], axis=1)
+        per_row_z = np.repeat(case.zeros[:, :1], case.zeros.shape[1], axis=1)
+        out["one_scale_zero_per_row"] = (case.A, case.packed, per_row_s, per_row_z)
+        out["scale_sign_flipped"] = (case.A, case.packed, case.scales ^ np.uint16(0x8000), case.zeros)
+    elif fmt == oracle.NVFP4:
+        out["one_scale_per_row"] = (case.A, case.packed,
+                                    np.repeat(case.scales[:, :1], case.scales.shape[1], axis=1), None)
+    else:
+        out["e8m0_bias_off_by_one"] = (case.A, case.packed, case.scales + np.uint8(1), None)
+        out["one_scale_per_row"] = (case.A, case.packed,
+                                    np.repeat(case.scales[:, :1], case.scales.shape[1], axis=1), None)
+    return out
+
+
+@pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
+def test_mutations_fail_gate(name, cfg):
+    fmt, M, N, K, bf16_out = cfg
+    case = inputs.make_case(fmt, M, N, K, seed=1)
+    C, S = _ref(case)
+    for mname, (A, p, s, z) in _mutations(case).items():
+        Cm, _ = oracle.gemm(fmt, A, p, s, z, M, N, K)
+        r = oracle.gate_ratio(Cm, C, S, bf16_out)
+        assert r > 1.0, (mname, r)
+
+
+def test_gate_bound_shape():
+    C = np.array([1.0, -2.0])
+    S = np.array([10.0, 0.0])
+    b = oracle.gate_bound(C, S, bf16_out=False)
+    assert np.allclose(b, [2e-2 + 1e-6, 1e-6])
+    b2 = oracle.gate_bound(C, S, bf16_out=True)
+    assert np.allclose(b2 - b, [2 ** -8, 2 * 2 ** -8])
+    assert oracle.gate_ratio(np.array([np.nan, 0.0]), C, S, False) == float("inf")
