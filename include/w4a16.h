@@ -1,0 +1,120 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 dequantise-GEMM library
+ *
+ *     C[m, n] = sum_k A[m, k] * W[n, k],   W = dequant(packed, scales, zeros)
+ *
+ * i.e. C = A . W^T with bf16 activations and 4-bit weights, fp32
+ * accumulation.  Plain C: pointers, 64-bit sizes and int status codes; no
+ * C++ or framework types cross this boundary.
+ *
+ * Operations and their sources (page titles):
+ *   - The GEMM "C = A @ B^T" with B packed two 4-bit values per byte, shape
+ *     (N, K/2): "example_dequant_gemm_bf16_fp4_hopper.py", kernel factory
+ *     matmul and its prim_func main.
+ *   - Asymmetric int4, group 128: "megakernel_int4_weight_decode.py", section
+ *     "The weight format" -- scale bf16 and zero uint8 per 128 contiguous
+ *     input elements, value = (code - zero) * scale; the contract's nibble
+ *     paragraph -- LOW nibble of byte (n, i) is input 2i, HIGH nibble 2i+1.
+ *   - NVFP4: "Matmul2dFp4" (Mojo), methods run / run_smem_decode -- packed
+ *     (N, K/2) uint8, scales (N, K/16) float8_e4m3fn, value =
+ *     e2m1(code) * |scale|.
+ *   - MXFP4: e2m1 codes with one e8m0 scale byte E per 32 contiguous inputs,
+ *     value = e2m1(code) * 2^(E - 127); same packed layout.
+ *   e2m1: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0; exponent 0
+ *   is subnormal, so the magnitudes are {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *
+ * Memory: every pointer is a DEVICE pointer owned by the caller; the library
+ * never allocates, frees or keeps them.  All arrays are row-major and dense:
+ *   A       bf16  (M, K)                    16-byte aligned
+ *   packed  uint8 (N, K/2)                  16-byte aligned
+ *   scales  int4: bf16 (N, K/128)           2-byte aligned
+ *           NVFP4: e4m3 bytes (N, K/16)     2-byte aligned
+ *           MXFP4: e8m0 bytes (N, K/32)
+ *   zeros   int4: uint8 (N, K/128); must be NULL for NVFP4 / MXFP4
+ *   C       bf16 or fp32 (M, N)             aligned to its element size
+ *   W       bf16 (N, K)                     16-byte aligned (dequant output)
+ * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing);
+ * 0 < K, K % 32 == 0, and K % 128 == 0 for int4; M, N, K < 2^31.
+ * Zero points: the GEMM is exact for zero bytes 0..127 (the format stores
+ * 0..15); the dequantisation takes any byte.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ * enqueue kernels and return; they never synchronise, allocate or read
+ * device memory from the host, so they may be captured into a HIP graph.
+ * Results are deterministic: the same inputs give bit-identical outputs.
+ *
+ * Errors: every argument is checked on the host BEFORE anything is enqueued;
+ * a failed check returns its code and enqueues nothing.  A launch failure
+ * reported by the HIP runtime returns W4A16_ERR_HIP.  The library keeps no
+ * mutable global state and is safe to call from several host threads.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- `format` argument: weight format, OR-ed with option flags ---------- */
+#define W4A16_INT4_G128 0   /* asymmetric int4, bf16 scale + u8 zero per 128 */
+#define W4A16_NVFP4 1       /* e2m1 codes, e4m3 scale per 16                  */
+#define W4A16_MXFP4 2       /* e2m1 codes, e8m0 scale per 32                  */
+#define W4A16_FORMAT_MASK 0xFF
+
+#define W4A16_OUT_BF16 0x000 /* C is bf16, rounded to nearest even (default) */
+#define W4A16_OUT_F32 0x100  /* C is fp32                                    */
+
+/* Kernel choice for w4a16_gemm.  AUTO picks the skinny (split-K, register
+ * decode) kernel for M <= 16 and the LDS-tiled MFMA kernel otherwise; the
+ * other two force one kernel at any M (the skinny kernel then walks M in
+ * slices of 16 rows). */
+#define W4A16_PATH_AUTO 0x0000
+#define W4A16_PATH_SKINNY 0x1000
+#define W4A16_PATH_TILED 0x2000
+#define W4A16_PATH_MASK 0x3000
+
+/* ---- status codes --------------------------------------------------------- */
+#define W4A16_OK 0
+#define W4A16_ERR_FORMAT (-1) /* unknown format or flag bits                 */
+#define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 32 != 0, K not a
+                                 multiple of the group, or a dimension
+                                 >= 2^31                                    */
+#define W4A16_ERR_NULL (-3)   /* a required pointer is NULL, or zeros is
+                                 non-NULL for an fp4 format                 */
+#define W4A16_ERR_ALIGN (-4)  /* a pointer violates its alignment           */
+#define W4A16_ERR_HIP (-5)    /* the HIP runtime rejected a launch          */
+
+/* C = A . dequant(packed, scales, zeros)^T, accumulated in fp32.
+ * format = W4A16_INT4_G128 | W4A16_NVFP4 | W4A16_MXFP4, optionally OR-ed with
+ * W4A16_OUT_F32 and one W4A16_PATH_* flag.  C is fully overwritten.
+ * Accuracy: |C - C_exact| <= 2e-3 * sum_k |A[m,k] W[n,k]| + 1e-6 per element,
+ * plus 2^-8 |C_exact| when C is bf16 (C_exact: exact weights, exact sum). */
+int w4a16_gemm(int format, const void* A, const void* packed, const void* scales,
+               const void* zeros, void* C, int64_t M, int64_t N, int64_t K,
+               void* stream);
+
+/* W = dequant(packed, scales, zeros) as bf16 (N, K): each weight's exact value
+ * rounded once to nearest even (bit-exact; fp4 weights are exact in bf16 at
+ * normal scale ranges).  `format` takes only the format bits.  A checking
+ * path: the GEMM never materialises W. */
+int w4a16_dequant(int format, const void* packed, const void* scales,
+                  const void* zeros, void* W, int64_t N, int64_t K, void* stream);
+
+/* Which kernel w4a16_gemm would launch for these arguments, without launching:
+ * returns W4A16_PATH_SKINNY or W4A16_PATH_TILED, or a negative status if the
+ * format / shape would be rejected.  Host-only. */
+int w4a16_gemm_path(int format, int64_t M, int64_t N, int64_t K);
+
+/* Static, NUL-terminated description of a status code. */
+const char* w4a16_strerror(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int w4a16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

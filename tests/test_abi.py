@@ -1,0 +1,133 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before touching the HIP
+runtime.  No call here reaches a kernel launch (no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_bit_w4a16_amd as w4
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(w4a16_\w+)\s*\(", text, re.M)))
+
+
+def _header_defines():
+    text = open(HEADER).read()
+    out = {}
+    for name, val in re.findall(r"#define\s+(W4A16_\w+)\s+\(?(-?0x[0-9A-Fa-f]+|-?\d+)\)?", text):
+        out[name] = int(val, 0)
+    return out
+
+
+def test_library_exports_every_declared_function():
+    lib = w4.load_library()
+    names = _header_functions()
+    assert set(names) == {"w4a16_gemm", "w4a16_dequant", "w4a16_gemm_path",
+                          "w4a16_strerror", "w4a16_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_python_constants_match_header():
+    d = _header_defines()
+    assert d["W4A16_INT4_G128"] == w4.INT4_G128
+    assert d["W4A16_NVFP4"] == w4.NVFP4
+    assert d["W4A16_MXFP4"] == w4.MXFP4
+    assert d["W4A16_OUT_F32"] == w4.OUT_F32
+    assert d["W4A16_PATH_SKINNY"] == w4.PATH_SKINNY
+    assert d["W4A16_PATH_TILED"] == w4.PATH_TILED
+    for code in ("OK", "ERR_FORMAT", "ERR_SHAPE", "ERR_NULL", "ERR_ALIGN", "ERR_HIP"):
+        assert d["W4A16_" + code] == getattr(w4, code)
+
+
+def test_version_and_strerror():
+    assert w4.version() == 100
+    for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP):
+        assert w4.strerror(code) != "unknown status"
+    assert w4.strerror(12345) == "unknown status"
+
+
+def test_path_choice():
+    assert w4.gemm_path(w4.INT4_G128, 1, 8192, 3072) == "skinny"
+    assert w4.gemm_path(w4.NVFP4, 16, 3072, 8192) == "skinny"
+    assert w4.gemm_path(w4.MXFP4, 17, 64, 64) == "tiled"
+    assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072) == "tiled"
+    assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072, "skinny") == "skinny"
+    assert w4.gemm_path(w4.INT4_G128, 1, 64, 128, "tiled") == "tiled"
+
+
+# fake, aligned device addresses: every call below fails validation (or is a
+# zero-extent no-op) before any pointer could be used
+PA, PB, PS, PZ, PC = (ctypes.c_void_p(0x100000 * i) for i in range(1, 6))
+
+
+def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
+    return w4.load_library().w4a16_gemm(fmt, A, B, S, Z, C, M, N, K, None)
+
+
+@pytest.mark.parametrize("fmt,M,N,K,expect", [
+    (3, 16, 64, 128, w4.ERR_FORMAT),                          # unknown format
+    (w4.INT4_G128 | 0x4000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
+    (w4.INT4_G128 | 0x3000, 16, 64, 128, w4.ERR_FORMAT),      # both paths forced
+    (w4.INT4_G128, -1, 64, 128, w4.ERR_SHAPE),
+    (w4.INT4_G128, 16, -5, 128, w4.ERR_SHAPE),
+    (w4.INT4_G128, 16, 64, 0, w4.ERR_SHAPE),
+    (w4.INT4_G128, 16, 64, 96, w4.ERR_SHAPE),                 # int4 needs K % 128
+    (w4.NVFP4, 16, 64, 48, w4.ERR_SHAPE),                     # K % 32 for 16-byte rows
+    (w4.MXFP4, 16, 64, 2 ** 31, w4.ERR_SHAPE),
+    (w4.MXFP4, 2 ** 31, 64, 64, w4.ERR_SHAPE),
+])
+def test_gemm_rejects_format_and_shape(fmt, M, N, K, expect):
+    Z = PZ if (fmt & 0xFF) == w4.INT4_G128 else None
+    assert _gemm(fmt, Z=Z, M=M, N=N, K=K) == expect
+
+
+def test_gemm_rejects_null_and_alignment():
+    assert _gemm(w4.INT4_G128, A=None) == w4.ERR_NULL
+    assert _gemm(w4.INT4_G128, B=None) == w4.ERR_NULL
+    assert _gemm(w4.INT4_G128, S=None) == w4.ERR_NULL
+    assert _gemm(w4.INT4_G128, C=None) == w4.ERR_NULL
+    assert _gemm(w4.INT4_G128, Z=None) == w4.ERR_NULL           # int4 needs zeros
+    assert _gemm(w4.NVFP4, Z=PZ) == w4.ERR_NULL                  # fp4 takes none
+    odd = ctypes.c_void_p(0x100008)
+    assert _gemm(w4.INT4_G128, A=odd) == w4.ERR_ALIGN
+    assert _gemm(w4.INT4_G128, B=odd) == w4.ERR_ALIGN
+    assert _gemm(w4.INT4_G128, S=ctypes.c_void_p(0x100001)) == w4.ERR_ALIGN
+    assert _gemm(w4.NVFP4, Z=None, S=ctypes.c_void_p(0x100001)) == w4.ERR_ALIGN
+    assert _gemm(w4.INT4_G128 | w4.OUT_F32, C=ctypes.c_void_p(0x100002)) == w4.ERR_ALIGN
+    # MXFP4 scales are single bytes: any address is fine; M = 0 makes it a no-op
+    assert _gemm(w4.MXFP4, Z=None, S=ctypes.c_void_p(0x100001), M=0) == w4.OK
+
+
+def test_zero_extent_is_a_noop():
+    assert _gemm(w4.INT4_G128, M=0) == w4.OK
+    assert _gemm(w4.INT4_G128, N=0) == w4.OK
+    lib = w4.load_library()
+    assert lib.w4a16_dequant(w4.MXFP4, PB, PS, None, PC, 0, 64, None) == w4.OK
+
+
+def test_dequant_rejects_bad_arguments():
+    lib = w4.load_library()
+    assert lib.w4a16_dequant(w4.INT4_G128 | w4.OUT_F32, PB, PS, PZ, PC, 4, 128, None) == w4.ERR_FORMAT
+    assert lib.w4a16_dequant(w4.INT4_G128, PB, PS, PZ, PC, 4, 64, None) == w4.ERR_SHAPE
+    assert lib.w4a16_dequant(w4.INT4_G128, PB, PS, None, PC, 4, 128, None) == w4.ERR_NULL
+    assert lib.w4a16_dequant(w4.MXFP4, PB, PS, PZ, PC, 4, 64, None) == w4.ERR_NULL
+    assert lib.w4a16_dequant(w4.MXFP4, PB, PS, None, ctypes.c_void_p(0x100008), 4, 64,
+                             None) == w4.ERR_ALIGN
+
+
+def test_binding_shape_checks_before_library(monkeypatch):
+    """The binding refuses inconsistent tensors (CPU tensors here: it must
+    never reach the library)."""
+    import torch
+    A = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w4.gemm(w4.INT4_G128, A, torch.zeros(8, 64, dtype=torch.uint8),
+                torch.zeros(8, 1, dtype=torch.bfloat16), torch.zeros(8, 1, dtype=torch.uint8))

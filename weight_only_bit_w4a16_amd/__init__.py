@@ -1,1 +1,166 @@
-"""W4A16 dequantise-GEMM for MI355X (gfx950).  Binding filled in below."""
+"""W4A16 dequantise-GEMM for MI355X (gfx950): Python binding of libw4a16.so.
+
+``C = A . dequant(packed, scales, zeros)^T`` with bf16 activations A (M, K),
+4-bit weights packed (N, K/2) uint8 (low nibble = even k) and fp32
+accumulation.  Formats: ``INT4_G128`` (bf16 scale + uint8 zero per 128 k),
+``NVFP4`` (e2m1 codes, e4m3 scale per 16 k), ``MXFP4`` (e2m1 codes, e8m0
+scale per 32 k).
+
+This module only marshals arguments to the C ABI declared in
+``include/w4a16.h``: it checks that tensor shapes, dtypes and devices agree
+with M, N, K (so no kernel can read past a tensor), then passes raw device
+pointers and the current HIP stream.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback.  PyTorch is used for device
+memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+INT4_G128, NVFP4, MXFP4 = 0, 1, 2
+GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32}
+FORMAT_NAMES = {INT4_G128: "int4_g128", NVFP4: "nvfp4", MXFP4: "mxfp4"}
+OUT_BF16, OUT_F32 = 0x000, 0x100
+PATH_AUTO, PATH_SKINNY, PATH_TILED = 0x0000, 0x1000, 0x2000
+PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
+
+OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a16.so")
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def load_library():
+    """Load the built HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+            "(or python weight_only_bit_w4a16_amd/_build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.w4a16_gemm.argtypes = [I, P, P, P, P, P, I64, I64, I64, P]
+    lib.w4a16_gemm.restype = I
+    lib.w4a16_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
+    lib.w4a16_dequant.restype = I
+    lib.w4a16_gemm_path.argtypes = [I, I64, I64, I64]
+    lib.w4a16_gemm_path.restype = I
+    lib.w4a16_strerror.argtypes = [I]
+    lib.w4a16_strerror.restype = ctypes.c_char_p
+    lib.w4a16_version.argtypes = []
+    lib.w4a16_version.restype = I
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().w4a16_strerror(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().w4a16_version())
+
+
+def gemm_path(fmt: int, M: int, N: int, K: int, path: str = "auto") -> str:
+    """Name of the kernel w4a16_gemm would launch ('skinny' or 'tiled')."""
+    rc = load_library().w4a16_gemm_path(int(fmt) | PATHS[path], M, N, K)
+    if rc < 0:
+        raise W4A16Error(rc, "w4a16_gemm_path")
+    return "skinny" if rc == PATH_SKINNY else "tiled"
+
+
+# ---- argument checks (host side, before any pointer reaches the library) ----
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, shape, itemsize, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.element_size() != itemsize:
+        raise ValueError(f"{name} must have {itemsize}-byte elements, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_weights(fmt, packed, scales, zeros, N, K, device):
+    if fmt not in GROUP:
+        raise ValueError(f"unknown format {fmt}")
+    G = GROUP[fmt]
+    if K % 32 or K % G:
+        raise ValueError(f"K={K} must be a multiple of 32 and of the group size {G}")
+    _check(packed, "packed", (N, K // 2), 1, device)
+    _check(scales, "scales", (N, K // G), 2 if fmt == INT4_G128 else 1, device)
+    if fmt == INT4_G128:
+        if zeros is None:
+            raise ValueError("int4 weights need zeros")
+        _check(zeros, "zeros", (N, K // G), 1, device)
+    elif zeros is not None:
+        raise ValueError("fp4 weights take no zeros")
+
+
+def gemm(fmt: int, A: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+         zeros: torch.Tensor | None = None, out: torch.Tensor | None = None,
+         out_dtype: torch.dtype = torch.bfloat16, path: str = "auto", stream=None) -> torch.Tensor:
+    """C = A . dequant(packed, scales, zeros)^T on the GPU (asynchronous)."""
+    if not A.is_cuda:
+        raise ValueError("A must be a GPU tensor")
+    device = A.device
+    M, K = A.shape
+    N = packed.shape[0]
+    _check(A, "A", (M, K), 2, device)
+    _check_weights(fmt, packed, scales, zeros, N, K, device)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be bf16 or fp32")
+    _check(out, "out", (M, N), out.element_size(), device)
+    flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path]
+    rc = load_library().w4a16_gemm(int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales),
+                                   _ptr(zeros), _ptr(out), M, N, K, _stream_handle(stream))
+    if rc != OK:
+        raise W4A16Error(rc, "w4a16_gemm")
+    return out
+
+
+def dequant(fmt: int, packed: torch.Tensor, scales: torch.Tensor,
+            zeros: torch.Tensor | None = None, out: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """W = dequant(packed, scales, zeros) as bf16 (N, K), bit-exact."""
+    if not packed.is_cuda:
+        raise ValueError("packed must be a GPU tensor")
+    device = packed.device
+    N, K2 = packed.shape
+    K = 2 * K2
+    _check_weights(fmt, packed, scales, zeros, N, K, device)
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=device)
+    _check(out, "out", (N, K), 2, device)
+    rc = load_library().w4a16_dequant(int(fmt), _ptr(packed), _ptr(scales), _ptr(zeros),
+                                      _ptr(out), N, K, _stream_handle(stream))
+    if rc != OK:
+        raise W4A16Error(rc, "w4a16_dequant")
+    return out

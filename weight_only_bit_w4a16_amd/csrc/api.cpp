@@ -1,0 +1,115 @@
+// api.cpp -- the C ABI declared in include/w4a16.h: host-side validation and
+// kernel dispatch.  Every check runs before any HIP call, so a rejected call
+// enqueues nothing (and never touches the HIP runtime).
+#include <stdint.h>
+
+#include "w4a16.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows with 32-bit ints
+
+int group_of(int fmt) { return fmt == W4A16_INT4_G128 ? 128 : fmt == W4A16_NVFP4 ? 16 : 32; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// format, flags and shape checks shared by w4a16_gemm and w4a16_gemm_path
+int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_flags) {
+  const int fmt = format & W4A16_FORMAT_MASK;
+  const int flags = format & ~W4A16_FORMAT_MASK;
+  if (fmt > W4A16_MXFP4) return W4A16_ERR_FORMAT;
+  if (allow_flags) {
+    if (flags & ~(W4A16_OUT_F32 | W4A16_PATH_MASK)) return W4A16_ERR_FORMAT;
+    if ((flags & W4A16_PATH_MASK) == W4A16_PATH_MASK) return W4A16_ERR_FORMAT;
+  } else if (flags) {
+    return W4A16_ERR_FORMAT;
+  }
+  if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_SHAPE;
+  if (K % 32 != 0 || K % group_of(fmt) != 0) return W4A16_ERR_SHAPE;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+// M <= 16 streams the weights once through the skinny kernel; larger M
+// amortises the decode over a 256-row tile.
+int choose_path(int format, int64_t M) {
+  const int forced = format & W4A16_PATH_MASK;
+  if (forced) return forced;
+  return M <= 16 ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_version(void) { return 100; }
+
+const char* w4a16_strerror(int status) {
+  switch (status) {
+    case W4A16_OK: return "success";
+    case W4A16_ERR_FORMAT: return "unknown weight format or flag bits";
+    case W4A16_ERR_SHAPE:
+      return "bad shape: need M, N >= 0, 0 < K < 2^31, K % 32 == 0 and K a multiple of the "
+             "format's group size";
+    case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for an fp4 format";
+    case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
+    case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int w4a16_gemm_path(int format, int64_t M, int64_t N, int64_t K) {
+  const int rc = check_format_shape(format, M, N, K, true);
+  if (rc != W4A16_OK) return rc;
+  return choose_path(format, M);
+}
+
+int w4a16_gemm(int format, const void* A, const void* packed, const void* scales,
+               const void* zeros, void* C, int64_t M, int64_t N, int64_t K, void* stream) {
+  const int rc = check_format_shape(format, M, N, K, true);
+  if (rc != W4A16_OK) return rc;
+  const int fmt = format & W4A16_FORMAT_MASK;
+  const bool out_f32 = (format & W4A16_OUT_F32) != 0;
+  if (!A || !packed || !scales || !C) return W4A16_ERR_NULL;
+  if (fmt == W4A16_INT4_G128 ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(packed, 16)) return W4A16_ERR_ALIGN;
+  if (fmt != W4A16_MXFP4 && !aligned(scales, 2)) return W4A16_ERR_ALIGN;
+  if (!aligned(C, out_f32 ? 4 : 2)) return W4A16_ERR_ALIGN;
+  if (M == 0 || N == 0) return W4A16_OK;
+
+  w4a16::GemmArgs a;
+  a.fmt = fmt;
+  a.out_f32 = out_f32;
+  a.A = static_cast<const uint16_t*>(A);
+  a.packed = static_cast<const uint8_t*>(packed);
+  a.scales = scales;
+  a.zeros = static_cast<const uint8_t*>(zeros);
+  a.C = C;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = choose_path(format, M) == W4A16_PATH_SKINNY ? w4a16::launch_skinny(a)
+                                                                   : w4a16::launch_tiled(a);
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_dequant(int format, const void* packed, const void* scales, const void* zeros, void* W,
+                  int64_t N, int64_t K, void* stream) {
+  const int rc = check_format_shape(format, 0, N, K, false);
+  if (rc != W4A16_OK) return rc;
+  const int fmt = format & W4A16_FORMAT_MASK;
+  if (!packed || !scales || !W) return W4A16_ERR_NULL;
+  if (fmt == W4A16_INT4_G128 ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(W, 16)) return W4A16_ERR_ALIGN;
+  if (fmt != W4A16_MXFP4 && !aligned(scales, 2)) return W4A16_ERR_ALIGN;
+  if (N == 0) return W4A16_OK;
+  const hipError_t e = w4a16::launch_dequant(fmt, static_cast<const uint8_t*>(packed), scales,
+                                             static_cast<const uint8_t*>(zeros),
+                                             static_cast<uint16_t*>(W), N, K,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+// common.hpp -- shared device helpers of the gfx950 W4A16 kernels: vector
+// types, weight-code decoders and scale decoders.
+//
+// Weight formats (page titles):
+//   int4 asymmetric, group 128 ("megakernel_int4_weight_decode.py", "The
+//     weight format"): value = (code - zero) * scale, bf16 scale and uint8
+//     zero per 128 contiguous k; byte (n, i) holds k = 2i in its LOW nibble.
+//   NVFP4 ("Matmul2dFp4", run / run_smem_decode): e2m1 code times the
+//     magnitude of an e4m3 scale per 16 k.
+//   MXFP4: e2m1 code times 2^(E - 127), one e8m0 byte E per 32 k.
+//
+// Every decoder below produces exact values: an int4 weight has at most 12
+// significant bits and an fp4 weight at most 6, so fp32 holds them exactly and
+// one final round-to-nearest-even gives the bf16 weight.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+enum Format : int { kInt4 = 0, kNvfp4 = 1, kMxfp4 = 2 };
+
+template <int FMT>
+struct FormatTraits;
+template <>
+struct FormatTraits<kInt4> {
+  static constexpr int kGroup = 128;
+};
+template <>
+struct FormatTraits<kNvfp4> {
+  static constexpr int kGroup = 16;
+};
+template <>
+struct FormatTraits<kMxfp4> {
+  static constexpr int kGroup = 32;
+};
+
+// ---- bit helpers ------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}
+// (selector 0x0c gives 0x00).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// two fp32 -> two bf16 packed in one dword, round to nearest even
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// ---- scale decoders -----------------------------------------------------------
+
+// e4m3 ("fn" variant: bias 7, no infinities, S.1111.111 = NaN) -> |value| as
+// fp32.  The 7 magnitude bits placed at fp32 bits 26:20 read as
+// 2^(e-127) (1 + m/8) for e >= 1 and as the fp32 subnormal m 2^-129 for e = 0;
+// multiplying by 2^120 (exact) gives 2^(e-7) (1 + m/8) and m 2^-9, the e4m3
+// values.  The magnitude is used, the sign dropped.
+__device__ __forceinline__ float e4m3_magnitude(uint32_t byte) {
+  uint32_t mag = byte & 0x7Fu;
+  float v = __uint_as_float(mag << 20) * 0x1p120f;
+  return mag == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
+}
+
+// e8m0 byte E -> 2^(E - 127) as the fp32 bit pattern E << 23.  The scaled
+// fp4 conversion instructions read only this exponent field, and map a
+// field of 0 to 2^-127, which is exactly the e8m0 meaning of E = 0.
+__device__ __forceinline__ float e8m0_as_exponent_scale(uint32_t E) {
+  return __uint_as_float(E << 23);
+}
+
+// e8m0 byte E -> 2^(E - 127) as an ordinary fp32 value (E = 0 is the fp32
+// subnormal 2^-127, E = 255 is NaN).
+__device__ __forceinline__ float e8m0_value(uint32_t E) {
+  uint32_t bits = (E == 0) ? 0x00400000u : (E << 23);
+  return E == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(bits);
+}
+
+// ---- fp4 decoders -------------------------------------------------------------
+
+// 8 e2m1 codes (one dword, code k in nibble k) times 2^(E-127), E the
+// exponent field of `escale`, to 8 bf16 in k order.  Exact for every code and
+// E in 0..254 (hardware scaled conversion, two codes per instruction).
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16_escale(uint32_t q, float escale) {
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, escale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, escale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, escale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, escale, 3));
+  return r;
+}
+
+// 8 e2m1 codes times an arbitrary fp32 scale (exact e2m1 -> fp32 with unit
+// scale, one exact fp32 multiply, one RNE to bf16 -- exact whenever the
+// product is a bf16 value, e.g. for every e4m3 scale).
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16_fscale(uint32_t q, float scale) {
+  const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+  const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+  const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+  const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+  u32x4_t r;
+  r[0] = pack_bf16x2(v0[0] * scale, v0[1] * scale);
+  r[1] = pack_bf16x2(v1[0] * scale, v1[1] * scale);
+  r[2] = pack_bf16x2(v2[0] * scale, v2[1] * scale);
+  r[3] = pack_bf16x2(v3[0] * scale, v3[1] * scale);
+  return r;
+}
+
+// byte i of x as an exact fp32 (one v_cvt_f32_ubyte<i>)
+template <int I>
+__device__ __forceinline__ float ubyte_f32(uint32_t x) {
+  return (float)((x >> (8 * I)) & 0xFFu);
+}
+
+// ---- int4 decoders -------------------------------------------------------------
+
+// 8 int4 codes (one dword, code k in nibble k) to bf16 (128 + code), in k
+// order: bf16 0x43nn is 128 + nn for nn < 128, so placing each nibble in the
+// low byte of a 0x43 high byte encodes the offset code exactly.
+__device__ __forceinline__ u32x4_t int4x8_to_bf16_offset128(uint32_t q) {
+  const uint32_t s = q >> 4;
+  u32x4_t r;
+  // byte 0 = low nibble of packed byte i (even k), byte 2 = its high nibble
+  r[0] = (perm_b32(s, q, 0x0c040c00u) & 0x000F000Fu) | 0x43004300u;
+  r[1] = (perm_b32(s, q, 0x0c050c01u) & 0x000F000Fu) | 0x43004300u;
+  r[2] = (perm_b32(s, q, 0x0c060c02u) & 0x000F000Fu) | 0x43004300u;
+  r[3] = (perm_b32(s, q, 0x0c070c03u) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+// bf16 -(128 + z), broadcast to 8 lanes' worth (exact for z <= 127).
+__device__ __forceinline__ u32x4_t int4_neg_offset_zero(uint32_t z) {
+  uint32_t h = 0xC300u | z;
+  uint32_t d = h | (h << 16);
+  return u32x4_t{d, d, d, d};
+}
+
+// 8 int4 codes to bf16 weights (code - zero) * scale, each rounded once to
+// nearest even.  The subtraction comes first, as the format defines it (so a
+// zero weight takes the sign of the scale); both steps are exact in fp32 (at
+// most 12 significant bits), so the only rounding is the final bf16 one.
+__device__ __forceinline__ u32x4_t int4x8_to_bf16_weights(uint32_t q, float s, float zf) {
+  const uint32_t lo = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
+  const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+  u32x4_t r;
+  r[0] = pack_bf16x2((ubyte_f32<0>(lo) - zf) * s,
+                     (ubyte_f32<0>(hi) - zf) * s);
+  r[1] = pack_bf16x2((ubyte_f32<1>(lo) - zf) * s,
+                     (ubyte_f32<1>(hi) - zf) * s);
+  r[2] = pack_bf16x2((ubyte_f32<2>(lo) - zf) * s,
+                     (ubyte_f32<2>(hi) - zf) * s);
+  r[3] = pack_bf16x2((ubyte_f32<3>(lo) - zf) * s,
+                     (ubyte_f32<3>(hi) - zf) * s);
+  return r;
+}
+
+// ---- MFMA ---------------------------------------------------------------------
+
+// D(16x16 fp32) += A(16x32 bf16) B(32x16 bf16).  Lane l supplies row l%16 of A
+// and column l%16 of B over the 8 k-slots 8*(l/16) .. +7, and holds D rows
+// 4*(l/16) .. +3 of column l%16.  The k-slot order is immaterial as long as A
+// and B use the same one.
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t d) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), d, 0, 0, 0);
+}
+
+}  // namespace w4a16

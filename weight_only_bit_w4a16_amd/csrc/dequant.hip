@@ -1,0 +1,91 @@
+// dequant.hip -- standalone dequantisation W = dequant(packed, scales, zeros)
+// to bf16 (N, K), the checking path for bit-exactness of the decoders the
+// GEMM kernels share.  One thread turns one 16-byte packed chunk (32 codes of
+// one row, inside one group for every format) into 64 bytes of bf16.
+//
+// Element rules (page titles): int4 -- "megakernel_int4_weight_decode.py",
+// "The weight format": (code - zero) * scale, the subtraction first; NVFP4 --
+// "Matmul2dFp4", run: e2m1 times |e4m3 scale| per 16; MXFP4 -- e2m1 times
+// 2^(E-127) per 32.  Each weight is exact in fp32 and rounded once to bf16.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+template <int FMT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ packed,
+                                                      const void* __restrict__ scales,
+                                                      const uint8_t* __restrict__ zeros,
+                                                      uint16_t* __restrict__ W, int64_t N,
+                                                      int64_t K) {
+  const int64_t chunks_per_row = K / 32;
+  const int64_t total = N * chunks_per_row;
+  constexpr int G = FormatTraits<FMT>::kGroup;
+  const int64_t groups = K / G;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = i / chunks_per_row;
+    const int64_t c = i - n * chunks_per_row;
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(packed + n * (K / 2) + c * 16);
+    u32x4_t out[4];
+    if constexpr (FMT == kInt4) {
+      const int64_t g = (c * 32) / 128;
+      const float s = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(scales)[n * groups + g]);
+      const float zf = (float)zeros[n * groups + g];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) out[d] = int4x8_to_bf16_weights(q[d], s, zf);
+    } else if constexpr (FMT == kNvfp4) {
+      const uint8_t* sp = reinterpret_cast<const uint8_t*>(scales) + n * groups + c * 2;
+      const float s0 = e4m3_magnitude(sp[0]);
+      const float s1 = e4m3_magnitude(sp[1]);
+      out[0] = fp4x8_to_bf16_fscale(q[0], s0);
+      out[1] = fp4x8_to_bf16_fscale(q[1], s0);
+      out[2] = fp4x8_to_bf16_fscale(q[2], s1);
+      out[3] = fp4x8_to_bf16_fscale(q[3], s1);
+    } else {
+      const uint32_t E = reinterpret_cast<const uint8_t*>(scales)[n * groups + c];
+      if (E != 255u) {
+        const float es = e8m0_as_exponent_scale(E);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) out[d] = fp4x8_to_bf16_escale(q[d], es);
+      } else {
+        // NaN scale: every weight of the block is NaN
+#pragma unroll
+        for (int d = 0; d < 4; ++d) out[d] = u32x4_t{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+      }
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(W + n * K + c * 32);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) dst[d] = out[d];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, const uint8_t* zeros,
+                          uint16_t* W, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t total = N * (K / 32);
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;  // grid-stride loop covers the rest
+  switch (fmt) {
+    case kInt4:
+      hipLaunchKernelGGL(dequant_kernel<kInt4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                         packed, scales, zeros, W, N, K);
+      break;
+    case kNvfp4:
+      hipLaunchKernelGGL(dequant_kernel<kNvfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                         packed, scales, zeros, W, N, K);
+      break;
+    default:
+      hipLaunchKernelGGL(dequant_kernel<kMxfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                         packed, scales, zeros, W, N, K);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4a16

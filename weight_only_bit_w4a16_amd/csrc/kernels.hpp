@@ -1,0 +1,33 @@
+// kernels.hpp -- launchers of the gfx950 kernels, called by the C ABI in
+// api.cpp after it has validated every argument.  Each returns the HIP error
+// of its launch (hipSuccess when nothing needed launching).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+struct GemmArgs {
+  int fmt;        // 0 int4 g128, 1 NVFP4, 2 MXFP4
+  bool out_f32;   // C is fp32 (else bf16)
+  const uint16_t* A;
+  const uint8_t* packed;
+  const void* scales;
+  const uint8_t* zeros;
+  void* C;
+  int64_t M, N, K;
+  hipStream_t stream;
+};
+
+hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, const uint8_t* zeros,
+                          uint16_t* W, int64_t N, int64_t K, hipStream_t stream);
+
+// M <= 16 per 16-row slice: split-K over the waves of a workgroup, weights
+// decoded in registers.
+hipError_t launch_skinny(const GemmArgs& a);
+
+// large M: LDS-staged tiles, decode into MFMA B fragments.
+hipError_t launch_tiled(const GemmArgs& a);
+
+}  // namespace w4a16
