@@ -33,8 +33,9 @@
  *   zeros   int4: uint8 (N, K/128); must be NULL for NVFP4 / MXFP4
  *   C       bf16 or fp32 (M, N)             aligned to its element size
  *   W       bf16 (N, K)                     16-byte aligned (dequant output)
- * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing);
- * 0 < K, K % 32 == 0, and K % 128 == 0 for int4; M, N, K < 2^31.
+ * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing and
+ * checks no pointer);
+ * 0 < K <= 2^26, K % 32 == 0, and K % 128 == 0 for int4; M, N < 2^31.
  * Zero points: the GEMM is exact for zero bytes 0..127 (the format stores
  * 0..15); the dequantisation takes any byte.
  *
@@ -79,8 +80,8 @@ extern "C" {
 #define W4A16_OK 0
 #define W4A16_ERR_FORMAT (-1) /* unknown format or flag bits                 */
 #define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 32 != 0, K not a
-                                 multiple of the group, or a dimension
-                                 >= 2^31                                    */
+                                 multiple of the group, M or N >= 2^31, or
+                                 K > 2^26                                   */
 #define W4A16_ERR_NULL (-3)   /* a required pointer is NULL, or zeros is
                                  non-NULL for an fp4 format                 */
 #define W4A16_ERR_ALIGN (-4)  /* a pointer violates its alignment           */

@@ -81,7 +81,7 @@ def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
     (w4.INT4_G128, 16, 64, 0, w4.ERR_SHAPE),
     (w4.INT4_G128, 16, 64, 96, w4.ERR_SHAPE),                 # int4 needs K % 128
     (w4.NVFP4, 16, 64, 48, w4.ERR_SHAPE),                     # K % 32 for 16-byte rows
-    (w4.MXFP4, 16, 64, 2 ** 31, w4.ERR_SHAPE),
+    (w4.MXFP4, 16, 64, 2 ** 26 + 32, w4.ERR_SHAPE),
     (w4.MXFP4, 2 ** 31, 64, 64, w4.ERR_SHAPE),
 ])
 def test_gemm_rejects_format_and_shape(fmt, M, N, K, expect):
@@ -102,8 +102,9 @@ def test_gemm_rejects_null_and_alignment():
     assert _gemm(w4.INT4_G128, S=ctypes.c_void_p(0x100001)) == w4.ERR_ALIGN
     assert _gemm(w4.NVFP4, Z=None, S=ctypes.c_void_p(0x100001)) == w4.ERR_ALIGN
     assert _gemm(w4.INT4_G128 | w4.OUT_F32, C=ctypes.c_void_p(0x100002)) == w4.ERR_ALIGN
-    # MXFP4 scales are single bytes: any address is fine; M = 0 makes it a no-op
+    # zero extents are no-ops that look at no pointer
     assert _gemm(w4.MXFP4, Z=None, S=ctypes.c_void_p(0x100001), M=0) == w4.OK
+    assert _gemm(w4.INT4_G128, A=None, C=None, N=0) == w4.OK
 
 
 def test_zero_extent_is_a_noop():

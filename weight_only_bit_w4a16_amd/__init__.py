@@ -164,3 +164,34 @@ def dequant(fmt: int, packed: torch.Tensor, scales: torch.Tensor,
     if rc != OK:
         raise W4A16Error(rc, "w4a16_dequant")
     return out
+
+
+class PreparedGemm:
+    """One w4a16_gemm call whose tensors were checked and marshalled once.
+
+    Calling it re-issues the C call with the same device pointers on the
+    given (default: current) stream -- for timing loops and graph capture,
+    where the per-call Python checks of :func:`gemm` would dominate.
+    The tensors are kept referenced for the object's lifetime.
+    """
+
+    def __init__(self, fmt: int, A, packed, scales, zeros, out, path: str = "auto"):
+        device = A.device
+        M, K = A.shape
+        N = packed.shape[0]
+        _check(A, "A", (M, K), 2, device)
+        _check_weights(fmt, packed, scales, zeros, N, K, device)
+        _check(out, "out", (M, N), out.element_size(), device)
+        if out.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("out must be bf16 or fp32")
+        self.tensors = (A, packed, scales, zeros, out)
+        flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path]
+        self.kernel = gemm_path(fmt, M, N, K, path)
+        self._fn = load_library().w4a16_gemm
+        self._args = (int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales), _ptr(zeros),
+                      _ptr(out), M, N, K)
+
+    def __call__(self, stream=None):
+        rc = self._fn(*self._args, _stream_handle(stream))
+        if rc != OK:
+            raise W4A16Error(rc, "w4a16_gemm")

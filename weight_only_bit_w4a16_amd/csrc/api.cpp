@@ -9,6 +9,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows with 32-bit ints
+constexpr int64_t kMaxK = (int64_t)1 << 26;    // 16 rows of A fit a 32-bit byte offset
 
 int group_of(int fmt) { return fmt == W4A16_INT4_G128 ? 128 : fmt == W4A16_NVFP4 ? 16 : 32; }
 
@@ -27,7 +28,7 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
   }
   if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_SHAPE;
   if (K % 32 != 0 || K % group_of(fmt) != 0) return W4A16_ERR_SHAPE;
-  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return W4A16_ERR_SHAPE;
+  if (M >= kMaxDim || N >= kMaxDim || K > kMaxK) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
 
@@ -50,8 +51,8 @@ const char* w4a16_strerror(int status) {
     case W4A16_OK: return "success";
     case W4A16_ERR_FORMAT: return "unknown weight format or flag bits";
     case W4A16_ERR_SHAPE:
-      return "bad shape: need M, N >= 0, 0 < K < 2^31, K % 32 == 0 and K a multiple of the "
-             "format's group size";
+      return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^26, K % 32 == 0 and K a multiple "
+             "of the format's group size";
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for an fp4 format";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
     case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
@@ -71,12 +72,12 @@ int w4a16_gemm(int format, const void* A, const void* packed, const void* scales
   if (rc != W4A16_OK) return rc;
   const int fmt = format & W4A16_FORMAT_MASK;
   const bool out_f32 = (format & W4A16_OUT_F32) != 0;
+  if (M == 0 || N == 0) return W4A16_OK;  // nothing is read or written
   if (!A || !packed || !scales || !C) return W4A16_ERR_NULL;
   if (fmt == W4A16_INT4_G128 ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
   if (!aligned(A, 16) || !aligned(packed, 16)) return W4A16_ERR_ALIGN;
   if (fmt != W4A16_MXFP4 && !aligned(scales, 2)) return W4A16_ERR_ALIGN;
   if (!aligned(C, out_f32 ? 4 : 2)) return W4A16_ERR_ALIGN;
-  if (M == 0 || N == 0) return W4A16_OK;
 
   w4a16::GemmArgs a;
   a.fmt = fmt;
@@ -100,11 +101,11 @@ int w4a16_dequant(int format, const void* packed, const void* scales, const void
   const int rc = check_format_shape(format, 0, N, K, false);
   if (rc != W4A16_OK) return rc;
   const int fmt = format & W4A16_FORMAT_MASK;
+  if (N == 0) return W4A16_OK;  // nothing is read or written
   if (!packed || !scales || !W) return W4A16_ERR_NULL;
   if (fmt == W4A16_INT4_G128 ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
   if (!aligned(packed, 16) || !aligned(W, 16)) return W4A16_ERR_ALIGN;
   if (fmt != W4A16_MXFP4 && !aligned(scales, 2)) return W4A16_ERR_ALIGN;
-  if (N == 0) return W4A16_OK;
   const hipError_t e = w4a16::launch_dequant(fmt, static_cast<const uint8_t*>(packed), scales,
                                              static_cast<const uint8_t*>(zeros),
                                              static_cast<uint16_t*>(W), N, K,

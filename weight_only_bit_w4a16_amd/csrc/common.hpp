@@ -65,6 +65,28 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// ---- buffer loads -------------------------------------------------------------
+// A raw buffer resource over [base, base + bytes): loads at an offset past
+// `bytes` return 0 without touching memory, so tails and padding need no
+// branches (and no branch-induced waits between independent loads).  The
+// base must be wave-uniform.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kBufferOOB = 0x80000000u;  // an offset past every buffer used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_b16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_b8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 // ---- scale decoders -----------------------------------------------------------
 
 // e4m3 ("fn" variant: bias 7, no infinities, S.1111.111 = NaN) -> |value| as

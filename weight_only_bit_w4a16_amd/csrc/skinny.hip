@@ -17,10 +17,9 @@
 //     inside the workgroup: no workspace, no atomics, deterministic).
 // Decode per format:
 //   * int4: codes become the exact bf16 values 128 + code; a second MFMA per
-//     step with the constant -(128 + zero) adds sum_k a_k (-(128 + zero)) to
-//     the same accumulator, so the k-block's accumulator holds
-//     sum_k a_k (code_k - zero) exactly as the MFMA sums it; the group scale
-//     multiplies that once per k-block (k-block = int4 group);
+//     step with the constant -(128 + zero) gives sum_k a_k (-(128 + zero)) in
+//     a second accumulator; their sum is sum_k a_k (code_k - zero), which the
+//     group scale multiplies once per k-block (k-block = int4 group);
 //   * NVFP4: e2m1 -> fp32, times |e4m3 scale| (exact), -> bf16 (exact);
 //   * MXFP4: hardware e2m1 conversion scaled by 2^(E-127) (exact).
 #include "common.hpp"
@@ -31,80 +30,128 @@ namespace w4a16 {
 namespace {
 
 constexpr int kMaxWaves = 16;
+constexpr int kAStage = 2;  // 16-byte chunks of A per thread when A is staged in LDS
 
-template <int FMT, bool OUT_F32, int U>
+template <int FMT, bool OUT_F32, int U, bool A_LDS>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const uint8_t* __restrict__ zeros, void* __restrict__ C,
     int M, int N, int K) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];  // arows x K bf16
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int waves = blockDim.x >> 6;
   const int nl = lane & 15;  // weight row within the slice / A row supplied
   const int g = lane >> 4;   // 32-code chunk within the k-block
   const int n0 = blockIdx.x * 16;
   const int m0 = blockIdx.y * 16;
   const int n = n0 + nl;
-  const int nrow = n < N ? n : N - 1;  // clamped: rows past N are computed, never stored
-  const int am = m0 + nl;
-  const bool a_ok = am < M;
   const int chunks = K >> 5;           // 32-code chunks per row
   const int KB = (chunks + 3) >> 2;    // 128-code k-blocks (last may be partial)
   constexpr int G = FormatTraits<FMT>::kGroup;
+  constexpr int SB = (FMT == kInt4) ? 2 : 1;  // bytes per scale
   const int groups = K / G;
 
-  const uint8_t* prow = packed + (int64_t)nrow * (K >> 1);
-  const uint16_t* arow = A + (int64_t)(a_ok ? am : 0) * K;
+  // Buffer descriptors over exactly this workgroup's 16 weight rows and 16 A
+  // rows: rows past N or M, and k past K, read as 0 (hardware range check).
+  const int rows = min(16, N - n0);
+  const int arows = min(16, M - m0);
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
+  const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB,
+                              (uint32_t)(rows * groups * SB));
+  const rsrc_t zr = make_rsrc(FMT == kInt4 ? zeros + (int64_t)n0 * groups : nullptr,
+                              FMT == kInt4 ? (uint32_t)(rows * groups) : 0u);
+
+  // A staging (few rows): the whole workgroup copies its A rows to LDS once.
+  // These loads are issued first, so waiting for them (vmcnt retires in
+  // issue order) does not wait for the weight stream issued after them.
+  u32x4_t astage[kAStage];
+  const int a16 = arows * K / 8;  // 16-byte chunks of this slice of A
+  if constexpr (A_LDS) {
+#pragma unroll
+    for (int i = 0; i < kAStage; ++i) {
+      const int ch = tid + i * (int)blockDim.x;
+      astage[i] = buf_load_b128(ar, ch < a16 ? (uint32_t)ch * 16u : kBufferOOB);
+    }
+  }
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  u32x4_t q[U];
+  u32x4_t a[U][4];
+  uint32_t sraw[U];
+  uint32_t zraw[U];
 
-  for (int kb0 = wave; kb0 < KB; kb0 += waves * U) {
-    u32x4_t q[U];
-    u32x4_t a[U][4];
-    uint32_t sraw[U];
-    uint32_t zraw[U];
-    // ---- issue every load of U k-blocks before any arithmetic -------------
+  // Each wave owns U consecutive k-blocks per pass (contiguous bytes of every
+  // row it reads); pass p covers k-blocks [(p * waves + wave) * U, +U).
+  auto issue = [&](int kbase) {
+    // scales first: vmcnt retires in issue order, so the first k-block's
+    // arithmetic then waits only for its own weights
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = kb0 + u * waves;
+      const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = (kb < KB) && (c < chunks);
-      q[u] = ok ? *reinterpret_cast<const u32x4_t*>(prow + (int64_t)c * 16) : u32x4_t{0, 0, 0, 0};
       if constexpr (FMT == kInt4) {
-        const int gi = (int64_t)nrow * groups + kb;
-        sraw[u] = ok ? reinterpret_cast<const uint16_t*>(scales)[gi] : 0u;
-        zraw[u] = ok ? zeros[gi] : 0u;
+        const uint32_t gi = (uint32_t)(nl * groups + kb);
+        sraw[u] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
+        zraw[u] = buf_load_b8(zr, ok ? gi : kBufferOOB);
       } else if constexpr (FMT == kNvfp4) {
         // the chunk's two e4m3 scales (blocks 2c and 2c+1), one 16-bit load
-        sraw[u] = ok ? reinterpret_cast<const uint16_t*>(
-                           reinterpret_cast<const uint8_t*>(scales) + (int64_t)nrow * groups)[c]
-                     : 0u;
+        sraw[u] = buf_load_b16(sr, ok ? (uint32_t)(nl * groups + 2 * c) : kBufferOOB);
       } else {
-        sraw[u] = ok ? reinterpret_cast<const uint8_t*>(scales)[(int64_t)nrow * groups + c] : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[u][j] = (ok && a_ok)
-                      ? *reinterpret_cast<const u32x4_t*>(arow + (int64_t)c * 32 + 8 * j)
-                      : u32x4_t{0, 0, 0, 0};
+        sraw[u] = buf_load_b8(sr, ok ? (uint32_t)(nl * groups + c) : kBufferOOB);
       }
     }
-    // ---- decode + MFMA ------------------------------------------------------
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int kb = kbase + u;
+      const int c = kb * 4 + g;
+      const bool ok = (kb < KB) && (c < chunks);
+      q[u] = buf_load_b128(wr, ok ? (uint32_t)nl * rowb + (uint32_t)c * 16u : kBufferOOB);
+      if constexpr (!A_LDS) {
+        const uint32_t aoff = ((uint32_t)nl * (uint32_t)K + (uint32_t)c * 32u) * 2u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[u][j] = buf_load_b128(ar, ok ? aoff + 16u * j : kBufferOOB);
+      }
+    }
+    // keep the whole batch of loads in flight: the scheduler may not sink
+    // them next to their uses (that would serialise the memory latencies)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto compute = [&](int kbase) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (A_LDS) {
+        const int kb = kbase + u;
+        const int c = kb * 4 + g;
+        const bool ok = (kb < KB) && (c < chunks) && (nl < arows);
+        const u32x4_t* src =
+            reinterpret_cast<const u32x4_t*>(a_lds + ((size_t)nl * K + (size_t)c * 32) * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[u][j] = ok ? src[j] : u32x4_t{0, 0, 0, 0};
+      }
       if constexpr (FMT == kInt4) {
+        // the +(128 + code) and -(128 + zero) products go to separate
+        // accumulators that follow the same rounding sequence, so a k-block
+        // whose codes all equal the zero point cancels to exactly 0
         const u32x4_t nz = int4_neg_offset_zero(zraw[u]);
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          d = mfma16x16x32(a[u][j], int4x8_to_bf16_offset128(q[u][j]), d);
-          d = mfma16x16x32(a[u][j], nz, d);
+          dp = mfma16x16x32(a[u][j], int4x8_to_bf16_offset128(q[u][j]), dp);
+          dn = mfma16x16x32(a[u][j], nz, dn);
         }
         const float s = bf16_bits_to_f32(sraw[u]);
-        acc[0] = __builtin_fmaf(s, d[0], acc[0]);
-        acc[1] = __builtin_fmaf(s, d[1], acc[1]);
-        acc[2] = __builtin_fmaf(s, d[2], acc[2]);
-        acc[3] = __builtin_fmaf(s, d[3], acc[3]);
+        acc[0] = __builtin_fmaf(s, dp[0] + dn[0], acc[0]);
+        acc[1] = __builtin_fmaf(s, dp[1] + dn[1], acc[1]);
+        acc[2] = __builtin_fmaf(s, dp[2] + dn[2], acc[2]);
+        acc[3] = __builtin_fmaf(s, dp[3] + dn[3], acc[3]);
       } else if constexpr (FMT == kNvfp4) {
         const float s0 = e4m3_magnitude(sraw[u] & 0xFFu);
         const float s1 = e4m3_magnitude(sraw[u] >> 8);
@@ -118,6 +165,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
         for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[u][j], fp4x8_to_bf16_escale(q[u][j], es), acc);
       }
     }
+  };
+
+  int kbase = wave * U;
+  issue(kbase);
+  if constexpr (A_LDS) {
+#pragma unroll
+    for (int i = 0; i < kAStage; ++i) {
+      const int ch = tid + i * (int)blockDim.x;
+      if (ch < a16) reinterpret_cast<u32x4_t*>(a_lds)[ch] = astage[i];
+    }
+    __syncthreads();
+  }
+  compute(kbase);
+  for (kbase += waves * U; kbase < KB; kbase += waves * U) {
+    issue(kbase);
+    compute(kbase);
   }
 
   // ---- split-K reduction across the waves, through LDS ----------------------
@@ -151,14 +214,26 @@ template <int FMT, bool OUT_F32>
 hipError_t launch_fmt(const GemmArgs& a) {
   const int chunks = (int)(a.K >> 5);
   const int KB = (chunks + 3) >> 2;
-  // k-blocks per wave: U loads of 16 B in flight per lane per pass
+  // U consecutive k-blocks per wave per pass: U 16-byte weight loads in
+  // flight per lane
   constexpr int U = 4;
   int waves = (KB + U - 1) / U;
   if (waves > kMaxWaves) waves = kMaxWaves;
   if (waves < 1) waves = 1;
   dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
-  hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U>), grid, dim3(64 * waves), 0, a.stream, a.A,
-                     a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
+  // stage A in LDS when the workgroup's A slice fits its staging registers
+  const int64_t arows = a.M < 16 ? a.M : 16;
+  const int64_t a_bytes = arows * a.K * 2;
+  const bool a_lds = a_bytes <= (int64_t)kAStage * 16 * 64 * waves && a_bytes <= 64 * 1024;
+  if (a_lds) {
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, true>), grid, dim3(64 * waves),
+                       (unsigned)a_bytes, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M,
+                       (int)a.N, (int)a.K);
+  } else {
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, false>), grid, dim3(64 * waves), 0,
+                       a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N,
+                       (int)a.K);
+  }
   return hipGetLastError();
 }
 
