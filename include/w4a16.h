@@ -35,7 +35,7 @@
  *   W       bf16 (N, K)                     16-byte aligned (dequant output)
  * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing and
  * checks no pointer);
- * 0 < K <= 2^26, K % 32 == 0, and K % 128 == 0 for int4; M, N < 2^31.
+ * 0 < K <= 2^22, K % 32 == 0, and K % 128 == 0 for int4; M, N < 2^31.
  * Zero points: the GEMM is exact for zero bytes 0..127 (the format stores
  * 0..15); the dequantisation takes any byte.
  *
@@ -81,7 +81,7 @@ extern "C" {
 #define W4A16_ERR_FORMAT (-1) /* unknown format or flag bits                 */
 #define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 32 != 0, K not a
                                  multiple of the group, M or N >= 2^31, or
-                                 K > 2^26                                   */
+                                 K > 2^22                                   */
 #define W4A16_ERR_NULL (-3)   /* a required pointer is NULL, or zeros is
                                  non-NULL for an fp4 format                 */
 #define W4A16_ERR_ALIGN (-4)  /* a pointer violates its alignment           */

@@ -9,7 +9,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows with 32-bit ints
-constexpr int64_t kMaxK = (int64_t)1 << 26;    // 16 rows of A fit a 32-bit byte offset
+constexpr int64_t kMaxK = (int64_t)1 << 22;    // a 256-row tile of A fits a 32-bit byte offset
 
 int group_of(int fmt) { return fmt == W4A16_INT4_G128 ? 128 : fmt == W4A16_NVFP4 ? 16 : 32; }
 
@@ -51,7 +51,7 @@ const char* w4a16_strerror(int status) {
     case W4A16_OK: return "success";
     case W4A16_ERR_FORMAT: return "unknown weight format or flag bits";
     case W4A16_ERR_SHAPE:
-      return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^26, K % 32 == 0 and K a multiple "
+      return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^22, K % 32 == 0 and K a multiple "
              "of the format's group size";
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for an fp4 format";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";

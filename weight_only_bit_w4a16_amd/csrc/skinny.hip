@@ -22,6 +22,8 @@
 //     group scale multiplies once per k-block (k-block = int4 group);
 //   * NVFP4: e2m1 -> fp32, times |e4m3 scale| (exact), -> bf16 (exact);
 //   * MXFP4: hardware e2m1 conversion scaled by 2^(E-127) (exact).
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,12 +34,16 @@ namespace {
 constexpr int kMaxWaves = 16;
 constexpr int kAStage = 2;  // 16-byte chunks of A per thread when A is staged in LDS
 
-template <int FMT, bool OUT_F32, int U, bool A_LDS>
+// FULL: K % 128 == 0, so every chunk of a k-block below KB exists and the
+// validity of a k-block is the same for the whole wave.
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const uint8_t* __restrict__ zeros, void* __restrict__ C,
     int M, int N, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];  // arows x K bf16
+  // LDS copy of A: arows rows of K bf16, then one row of zeros that lanes
+  // past M (and chunks past K) read instead of branching
+  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -86,6 +92,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
 
   // Each wave owns U consecutive k-blocks per pass (contiguous bytes of every
   // row it reads); pass p covers k-blocks [(p * waves + wave) * U, +U).
+  auto valid = [&](int kb, int c) { return FULL ? (kb < KB) : (kb < KB && c < chunks); };
   auto issue = [&](int kbase) {
     // scales first: vmcnt retires in issue order, so the first k-block's
     // arithmetic then waits only for its own weights
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     for (int u = 0; u < U; ++u) {
       const int kb = kbase + u;
       const int c = kb * 4 + g;
-      const bool ok = (kb < KB) && (c < chunks);
+      const bool ok = valid(kb, c);
       if constexpr (FMT == kInt4) {
         const uint32_t gi = (uint32_t)(nl * groups + kb);
         sraw[u] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     for (int u = 0; u < U; ++u) {
       const int kb = kbase + u;
       const int c = kb * 4 + g;
-      const bool ok = (kb < KB) && (c < chunks);
+      const bool ok = valid(kb, c);
       q[u] = buf_load_b128(wr, ok ? (uint32_t)nl * rowb + (uint32_t)c * 16u : kBufferOOB);
       if constexpr (!A_LDS) {
         const uint32_t aoff = ((uint32_t)nl * (uint32_t)K + (uint32_t)c * 32u) * 2u;
@@ -123,17 +130,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  const int arow = nl < arows ? nl : arows;  // row arows of the LDS copy is zeros
   auto compute = [&](int kbase) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int kb = kbase + u;
+      if (FULL && kb >= KB) break;  // wave-uniform: nothing was loaded
       if constexpr (A_LDS) {
-        const int kb = kbase + u;
         const int c = kb * 4 + g;
-        const bool ok = (kb < KB) && (c < chunks) && (nl < arows);
+        const int col = (FULL || c < chunks) ? c * 32 : 0;
+        const int row = (FULL || c < chunks) ? arow : arows;
         const u32x4_t* src =
-            reinterpret_cast<const u32x4_t*>(a_lds + ((size_t)nl * K + (size_t)c * 32) * 2);
+            reinterpret_cast<const u32x4_t*>(a_lds + ((size_t)row * K + (size_t)col) * 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[u][j] = ok ? src[j] : u32x4_t{0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) a[u][j] = src[j];
       }
       if constexpr (FMT == kInt4) {
         // the +(128 + code) and -(128 + zero) products go to separate
@@ -170,11 +180,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   int kbase = wave * U;
   issue(kbase);
   if constexpr (A_LDS) {
+    // copy the staged rows, then zero row `arows` (a16 .. a16 + K/8 chunks)
 #pragma unroll
     for (int i = 0; i < kAStage; ++i) {
       const int ch = tid + i * (int)blockDim.x;
       if (ch < a16) reinterpret_cast<u32x4_t*>(a_lds)[ch] = astage[i];
     }
+    for (int ch = a16 + tid; ch < a16 + K / 8; ch += blockDim.x)
+      reinterpret_cast<u32x4_t*>(a_lds)[ch] = u32x4_t{0, 0, 0, 0};
     __syncthreads();
   }
   compute(kbase);
@@ -210,31 +223,52 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   }
 }
 
-template <int FMT, bool OUT_F32>
-hipError_t launch_fmt(const GemmArgs& a) {
-  const int chunks = (int)(a.K >> 5);
-  const int KB = (chunks + 3) >> 2;
-  // U consecutive k-blocks per wave per pass: U 16-byte weight loads in
-  // flight per lane
-  constexpr int U = 4;
-  int waves = (KB + U - 1) / U;
-  if (waves > kMaxWaves) waves = kMaxWaves;
-  if (waves < 1) waves = 1;
+template <int FMT, bool OUT_F32, int U>
+hipError_t launch_u(const GemmArgs& a, int waves) {
   dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
   // stage A in LDS when the workgroup's A slice fits its staging registers
   const int64_t arows = a.M < 16 ? a.M : 16;
   const int64_t a_bytes = arows * a.K * 2;
   const bool a_lds = a_bytes <= (int64_t)kAStage * 16 * 64 * waves && a_bytes <= 64 * 1024;
-  if (a_lds) {
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, true>), grid, dim3(64 * waves),
-                       (unsigned)a_bytes, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M,
-                       (int)a.N, (int)a.K);
+  const unsigned lds = (unsigned)(a_bytes + a.K * 2);  // + the zero row
+  const bool full = a.K % 128 == 0;
+  const dim3 block(64 * waves);
+  if (a_lds && full) {
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, true, true>), grid, block, lds, a.stream,
+                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
+  } else if (a_lds) {
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, true, false>), grid, block, lds, a.stream,
+                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
+  } else if (full) {
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, false, true>), grid, block, 0, a.stream,
+                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
   } else {
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, false>), grid, dim3(64 * waves), 0,
-                       a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N,
-                       (int)a.K);
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, false, false>), grid, block, 0, a.stream,
+                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
   }
   return hipGetLastError();
+}
+
+// Work split: each wave takes U consecutive k-blocks per pass (U 16-byte
+// weight loads in flight per lane), and the workgroup has enough waves
+// (at most 16) to cover K in one pass when it can.  W4A16_SKINNY_U (1, 2 or 4)
+// overrides U for tuning.
+template <int FMT, bool OUT_F32>
+hipError_t launch_fmt(const GemmArgs& a) {
+  const int chunks = (int)(a.K >> 5);
+  const int KB = (chunks + 3) >> 2;
+  static const int u_env = [] {
+    const char* e = getenv("W4A16_SKINNY_U");
+    return e ? atoi(e) : 0;
+  }();
+  int U = u_env == 1 || u_env == 2 || u_env == 4 ? u_env : 4;
+  if (!u_env && (KB + 1) / 2 <= kMaxWaves) U = 2;
+  int waves = (KB + U - 1) / U;
+  if (waves > kMaxWaves) waves = kMaxWaves;
+  if (waves < 1) waves = 1;
+  if (U == 1) return launch_u<FMT, OUT_F32, 1>(a, waves);
+  if (U == 2) return launch_u<FMT, OUT_F32, 2>(a, waves);
+  return launch_u<FMT, OUT_F32, 4>(a, waves);
 }
 
 }  // namespace
