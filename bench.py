@@ -70,16 +70,21 @@ KERNEL_SOURCES = {
 
 
 def traffic_from_profile(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/traffic_<kernel>_<workload>.txt (lines "key value"), or None when
+    there is none or the kernel's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                rec[parts[0]] = parts[1]
     if rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(float(rec["hbm_bytes_per_launch"]))
 
 
 def main():
@@ -91,10 +96,13 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight copies to rotate over (0: enough for >= 1 GiB)")
-    ap.add_argument("--m4096-steps", type=int, default=20)
+    ap.add_argument("--m4096-steps", type=int, default=100)
     ap.add_argument("--no-m4096", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 10 times (reference "
+                         "kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -113,6 +121,17 @@ def main():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
     dev = torch.device("cuda", 0)
     w4.load_library()  # fails loudly if the HIP library is not built
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": nbytes, "dispatches": 10}))
+        return
 
     def to_dev(case):
         A = torch.from_numpy(case.A.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -269,7 +288,7 @@ def main():
         A, p, s, z = to_dev(case)
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         call = w4.PreparedGemm(fmt, A, p, s, z, C)
-        t4 = timed([[call]], args.m4096_steps, 3)
+        t4 = timed([[call]], args.m4096_steps, 10)
         tfl = 2.0 * M * N * K / (t4 / args.m4096_steps * 1e-3) / 1e12
         result["m4096"] = {"workload": "mxfp4_m4096", "kernel": call.kernel, "steps": args.m4096_steps,
                            "ms_per_step": round(t4 / args.m4096_steps, 4),

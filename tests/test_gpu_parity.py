@@ -267,3 +267,26 @@ def test_deterministic_and_stream(fmt, M, N, K):
     torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(w4.INT4_G128, 1, 4096, 3072), (w4.NVFP4, 16, 1024, 512),
+                                       (w4.MXFP4, 300, 512, 256)])
+def test_hip_graph_capture_replay(fmt, M, N, K):
+    """The C ABI call is capturable: replays of a captured graph, with eager
+    work and synchronisations between them, match the eager result."""
+    case = inputs.make_case(fmt, M, N, K, seed=21)
+    A, p, s, z = to_dev(case)
+    eager = w4.gemm(fmt, A, p, s, z)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    call = w4.PreparedGemm(fmt, A, p, s, z, out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(4):
+        out.fill_(float("nan"))
+        _ = (A.float() * (i + 1)).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
