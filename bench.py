@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode_gemv_int4_m1", choices=list(WORKLOADS) + [CHAIN])
     ap.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
+    ap.add_argument("--shape", default=None,
+                    help="custom single-GEMM workload 'format,M,N,K' (format 0 int4, 1 nvfp4, "
+                         "2 mxfp4; bf16 out) instead of --workload")
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight copies to rotate over (0: enough for >= 1 GiB)")
     ap.add_argument("--m4096-steps", type=int, default=100)
@@ -104,6 +107,12 @@ def main():
                     help="only run a plain 256 MiB device-to-device copy 10 times (reference "
                          "kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+
+    if args.shape:
+        f, m, n, k = (int(x) for x in args.shape.split(","))
+        name = f"custom_f{f}_m{m}_n{n}_k{k}"
+        WORKLOADS[name] = (f, m, n, k, "bf16")
+        args.workload = name
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -242,7 +251,7 @@ def main():
                   "out": out, "weight_copies": copies, "kernel": kernel}
         workload = args.workload
         weight_bytes = wbytes
-        if args.workload == "mxfp4_m4096":
+        if M > 16:
             value = 2.0 * M * N * K / (ms * 1e-3) / 1e12
             unit = "TFLOP/s"
         else:
@@ -250,7 +259,7 @@ def main():
             unit = "GB/s"
 
     mean_launch_ms = ms / launches_per_step
-    if args.workload == "mxfp4_m4096":
+    if args.workload != CHAIN and WORKLOADS[args.workload][1] > 16:
         fmt, M, N, K, out = WORKLOADS[args.workload]
         ach = 2.0 * M * N * K / (mean_launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
@@ -296,7 +305,7 @@ def main():
                            "frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
 
     # ---- CPU baseline: the oracle on the same workload ------------------------
-    if not args.no_cpu_baseline and args.workload != CHAIN:
+    if not args.no_cpu_baseline and args.workload != CHAIN and not args.shape:
         import oracle
         fmt, M, N, K, out = WORKLOADS[args.workload]
         if args.workload == "mxfp4_m4096":

@@ -178,6 +178,40 @@ __device__ __forceinline__ u32x4_t int4x8_to_bf16_offset128(uint32_t q) {
   return r;
 }
 
+// 8 int4 codes (one dword, code k in nibble k) to their exact bf16 values, in
+// the k order (0, 2, 4, 6, 1, 3, 5, 7).  A code c alone in a byte is the e4m3
+// value c * 2^-9 (subnormal for c < 8, first binade for c >= 8), so the scaled
+// fp8 conversion with a scale of 2^9 yields c exactly, two codes per
+// instruction: seven VALU operations per 8 codes.
+__device__ __forceinline__ u32x4_t int4x8_to_bf16_exact(uint32_t q) {
+  const uint32_t lo = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
+  const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));
+  return r;
+}
+
+// 8 consecutive bf16 values (k order 0..7, two per dword) reordered to the k
+// order (0, 2, 4, 6, 1, 3, 5, 7) of int4x8_to_bf16_exact.
+__device__ __forceinline__ u32x4_t bf16x8_even_odd(u32x4_t a) {
+  u32x4_t r;
+  r[0] = perm_b32(a[1], a[0], 0x05040100u);  // (a0, a2)
+  r[1] = perm_b32(a[3], a[2], 0x05040100u);  // (a4, a6)
+  r[2] = perm_b32(a[1], a[0], 0x07060302u);  // (a1, a3)
+  r[3] = perm_b32(a[3], a[2], 0x07060302u);  // (a5, a7)
+  return r;
+}
+
+// bf16 -z broadcast to 8 lanes' worth (exact for z <= 256).
+__device__ __forceinline__ u32x4_t int4_neg_zero(uint32_t z) {
+  const uint32_t h = __float_as_uint(-(float)z) >> 16;
+  const uint32_t d = h | (h << 16);
+  return u32x4_t{d, d, d, d};
+}
+
 // bf16 -(128 + z), broadcast to 8 lanes' worth (exact for z <= 127).
 __device__ __forceinline__ u32x4_t int4_neg_offset_zero(uint32_t z) {
   uint32_t h = 0xC300u | z;

@@ -16,10 +16,12 @@
 //   * partial sums of the W waves are added through LDS at the end (split-K
 //     inside the workgroup: no workspace, no atomics, deterministic).
 // Decode per format:
-//   * int4: codes become the exact bf16 values 128 + code; a second MFMA per
-//     step with the constant -(128 + zero) gives sum_k a_k (-(128 + zero)) in
-//     a second accumulator; their sum is sum_k a_k (code_k - zero), which the
-//     group scale multiplies once per k-block (k-block = int4 group);
+//   * int4: codes become exact bf16 values -- the codes themselves through the
+//     scaled fp8 converter when A sits in LDS (A is stored in the decoder's
+//     k order), else 128 + code by byte assembly; a second MFMA per step with
+//     the constant -zero (or -(128 + zero)) fills a second accumulator; their
+//     sum is sum_k a_k (code_k - zero), which the group scale multiplies once
+//     per k-block (k-block = int4 group);
 //   * NVFP4: e2m1 -> fp32, times |e4m3 scale| (exact), -> bf16 (exact);
 //   * MXFP4: hardware e2m1 conversion scaled by 2^(E-127) (exact).
 #include <stdlib.h>
@@ -146,15 +148,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
         for (int j = 0; j < 4; ++j) a[u][j] = src[j];
       }
       if constexpr (FMT == kInt4) {
-        // the +(128 + code) and -(128 + zero) products go to separate
-        // accumulators that follow the same rounding sequence, so a k-block
-        // whose codes all equal the zero point cancels to exactly 0
-        const u32x4_t nz = int4_neg_offset_zero(zraw[u]);
+        // the +code (or +(128 + code)) and -zero (or -(128 + zero)) products
+        // go to separate accumulators that follow the same rounding
+        // sequence, so a k-block whose codes all equal the zero point cancels
+        // to exactly 0.  With A in LDS (already in the decoder's k order) the
+        // codes convert exactly without an offset; otherwise the offset-128
+        // encoding keeps A in its natural order.
+        const u32x4_t nz = A_LDS ? int4_neg_zero(zraw[u]) : int4_neg_offset_zero(zraw[u]);
         f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
         f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          dp = mfma16x16x32(a[u][j], int4x8_to_bf16_offset128(q[u][j]), dp);
+          const u32x4_t b = A_LDS ? int4x8_to_bf16_exact(q[u][j]) : int4x8_to_bf16_offset128(q[u][j]);
+          dp = mfma16x16x32(a[u][j], b, dp);
           dn = mfma16x16x32(a[u][j], nz, dn);
         }
         const float s = bf16_bits_to_f32(sraw[u]);
@@ -184,7 +190,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
 #pragma unroll
     for (int i = 0; i < kAStage; ++i) {
       const int ch = tid + i * (int)blockDim.x;
-      if (ch < a16) reinterpret_cast<u32x4_t*>(a_lds)[ch] = astage[i];
+      // int4 codes decode in the k order (0,2,4,6,1,3,5,7) per 8: A follows it
+      const u32x4_t v = FMT == kInt4 ? bf16x8_even_odd(astage[i]) : astage[i];
+      if (ch < a16) reinterpret_cast<u32x4_t*>(a_lds)[ch] = v;
     }
     for (int ch = a16 + tid; ch < a16 + K / 8; ch += blockDim.x)
       reinterpret_cast<u32x4_t*>(a_lds)[ch] = u32x4_t{0, 0, 0, 0};
