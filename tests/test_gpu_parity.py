@@ -213,6 +213,10 @@ RAGGED = [
     (w4.NVFP4, 130, 300, 224),
     (w4.MXFP4, 2, 17, 32), (w4.MXFP4, 9, 64, 96), (w4.MXFP4, 260, 520, 192),
     (w4.MXFP4, 513, 129, 64),
+    # short N / few rows: the skinny kernel splits K inside the MFMA (k-parts),
+    # here with part counts that do not divide the k-blocks evenly
+    (w4.MXFP4, 1, 200, 288), (w4.NVFP4, 2, 100, 480), (w4.INT4_G128, 3, 50, 1280),
+    (w4.INT4_G128, 1, 1024, 3072), (w4.NVFP4, 1, 72, 8192),
 ]
 
 
