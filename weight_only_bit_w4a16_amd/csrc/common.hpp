@@ -87,6 +87,55 @@ __device__ __forceinline__ uint32_t buf_load_b8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
+// Asynchronous global -> LDS copy (gfx950 "buffer_load ... lds"): lane l of
+// the wave reads `size` bytes at voff of the buffer and writes them to LDS
+// dword slot l (16-byte slot l for the 16-byte form) after the wave-uniform
+// LDS base `lds_addr`; 1- and 2-byte loads are zero-extended to the slot.
+// Out-of-range lanes write zeros.  Issued through inline assembly so that
+// the compiler neither waits for the copy nor knows of it: the caller owns the
+// vmcnt accounting (s_waitcnt vmcnt(n) then s_barrier before any wave reads
+// the slots).  m0 carries the LDS base and is restored afterwards.
+__device__ __forceinline__ void lds_dma_b128(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void lds_dma_b16(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_ushort %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void lds_dma_b8(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_ubyte %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
+// 32-bit LDS address of a __shared__ object (the value m0 takes above)
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // ---- scale decoders -----------------------------------------------------------
 
 // e4m3 ("fn" variant: bias 7, no infinities, S.1111.111 = NaN) -> |value| as

@@ -1,6 +1,7 @@
 // tiled.hip -- W4A16 GEMM for many activation rows: C = A . dequant(B)^T with
-// A and the PACKED weights staged through LDS and the weights decoded into
-// bf16 MFMA B fragments in registers, fp32 accumulation.
+// A and the PACKED weights copied straight from global memory into LDS and
+// the weights decoded into bf16 MFMA B fragments in registers, fp32
+// accumulation.
 //
 // Prior art (page titles): the tiled dequant-GEMM of
 // "example_dequant_gemm_bf16_fp4_hopper.py" (matmul / main: shared A and
@@ -12,12 +13,27 @@
 // feeds to its own MFMAs, so no bf16 weight tile ever exists in memory.
 //
 // Workgroup tile 256 x 256 (M x N), k-tile 64, 8 waves as 2 x 4, each wave
-// 128 x 64 = 8 x 4 MFMA 16x16x32 tiles.  Two LDS stages: while the waves
-// multiply stage s, the next k-tile is in flight from global memory to
-// registers, then written to stage s^1.  Inside a k-tile, lane group g (lanes
-// 16g .. 16g+15) owns codes 16g .. 16g+15 of each row: one 8-byte LDS read
-// per B fragment covers both 32-k MFMA steps, and the A fragment of step s is
-// the 8 A values at k = 16g + 8s .. +7 (the same k order for A and B).
+// 128 x 64 = 8 x 4 MFMA 16x16x32 tiles.  A and B k-tiles sit in a ring of
+// three LDS stages filled by asynchronous global -> LDS copies (no staging
+// registers, no LDS stores by the waves): while the waves multiply stage j,
+// the copies of k-tiles j+1 and j+2 are in flight.  Scales arrive the same
+// way, once per scale tile of several k-tiles, in two alternating buffers.
+// Inside a k-tile, lane group g (lanes 16g .. 16g+15) owns codes 16g ..
+// 16g+15 of each row: one 8-byte LDS read per B fragment covers both 32-k
+// MFMA steps, and the A fragment of step s is the 8 A values at k = 16g + 8s
+// .. +7 (the same k order for A and B).
+//
+// LDS layouts.  A copy writes 64 consecutive LDS slots, so each layout is a
+// lane -> source permutation of whole copies; it keeps the lanes of a copy
+// on few, contiguous global runs (global requests) and makes the MFMA-side
+// reads free of bank conflicts:
+//   A: row r of the tile is 128 B = 8 chunks of 8 k; chunk c sits in slot
+//      c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so the 16 rows read by one
+//      lane group at one chunk hit 16 distinct 16-B slots of each 256 B.
+//   B: row r is 32 B = two 16-B halves (codes 32h .. 32h+31); half h sits in
+//      slot h ^ ((r >> 2) & 1) (two lanes fetch one row's 32 contiguous bytes).
+//   scales: per row, E consecutive scale elements (one dword slot each) of a
+//      scale tile; element e sits in slot e ^ f_E(r) (see ScaleTile).
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -28,8 +44,34 @@ namespace w4a16 {
 namespace {
 
 constexpr int BK = 64;
-constexpr int A_LD = BK + 8;        // bf16 elements per LDS row of A (144 B: 16-B slots rotate)
-constexpr int B_LD = BK / 2 + 8;    // bytes per LDS row of packed B (40 B)
+constexpr int kStages = 3;
+
+// Scale tile: each of the BN rows brings E consecutive elements of its scale
+// row (E consecutive lanes, one global run per row), covering kKTiles k-tiles.
+//   MXFP4: 1-byte e8m0 per 32 codes, E = 16 -> 8 k-tiles.
+//   NVFP4: 2-byte element = the e4m3 bytes of two 16-code blocks, E = 8 -> 4 k-tiles.
+//   int4:  2-byte bf16 scale (array 0) and 1-byte zero (array 1) per 128 codes,
+//          E = 8 -> 16 k-tiles.
+// Elements past K, and rows past N, are zero-filled by the copy.
+template <int FMT>
+struct ScaleTile;
+template <>
+struct ScaleTile<kMxfp4> {
+  static constexpr int kElems = 16, kKTiles = 8, kArrays = 1;
+};
+template <>
+struct ScaleTile<kNvfp4> {
+  static constexpr int kElems = 8, kKTiles = 4, kArrays = 1;
+};
+template <>
+struct ScaleTile<kInt4> {
+  static constexpr int kElems = 8, kKTiles = 16, kArrays = 2;
+};
+// slot swizzle of row r: 16 rows reading one element hit 16 distinct banks
+template <int E>
+__device__ __forceinline__ int scale_swz(int r) {
+  return E == 16 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
 
 // Workgroup tile BM x BN = (WGM * TM * 16) x (WGN * TN * 16): WGM x WGN waves,
 // each computing TM x TN MFMA 16x16x32 tiles.
@@ -37,12 +79,31 @@ template <int WGM_, int WGN_, int TM_, int TN_>
 struct TileCfg {
   static constexpr int WGM = WGM_, WGN = WGN_, TM = TM_, TN = TN_;
   static constexpr int BM = WGM * TM * 16, BN = WGN * TN * 16;
-  static constexpr int kThreads = 64 * WGM * WGN;
-  static constexpr int kAChunks = BM * (BK / 8) / kThreads;   // 16-byte A chunks per thread
-  static constexpr int kBChunks = BN * (BK / 32) / kThreads;  // 16-byte B chunks per thread
-  static_assert(kAChunks * kThreads == BM * (BK / 8), "A tile must split evenly");
-  static_assert(kBChunks * kThreads == BN * (BK / 32), "B tile must split evenly");
-  static_assert(BN <= kThreads, "one thread per B row fetches its scales");
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kABytes = BM * BK * 2;  // one stage of A (bf16)
+  static constexpr int kBBytes = BN * BK / 2;  // one stage of packed B
+  // 1-KB copy blocks per wave and k-tile (64 lanes x 16 B)
+  static constexpr int kABlocks = kABytes / 1024 / kWaves;
+  static constexpr int kBBlocks = kBBytes / 1024 / kWaves;
+  static constexpr int kGroupOps = kABlocks + kBBlocks;  // copies per wave per k-tile
+  static_assert(kABlocks * kWaves * 1024 == kABytes, "A stage must split into 1-KB blocks");
+  static_assert(kBBlocks * kWaves * 1024 == kBBytes, "B stage must split into 1-KB blocks");
+  static_assert(kGroupOps <= 15, "vmcnt immediate");
+};
+
+template <int FMT, class CFG>
+struct Layout {
+  using ST = ScaleTile<FMT>;
+  static constexpr int kSArrayBytes = CFG::BN * ST::kElems * 4;
+  static constexpr int kSBytes = ST::kArrays * kSArrayBytes;        // one scale buffer
+  static constexpr int kSBlocks = kSBytes / 256 / CFG::kWaves;      // 64-dword copies per wave
+  static constexpr int kBOff = kStages * CFG::kABytes;
+  static constexpr int kSOff = kBOff + kStages * CFG::kBBytes;
+  static constexpr int kBytes = kSOff + 2 * kSBytes;
+  static_assert(kSBlocks * CFG::kWaves * 256 == kSBytes, "scale buffer must split into copies");
+  static_assert((CFG::BN * ST::kElems) % 64 == 0, "a copy covers whole rows of one array");
+  static_assert(kBytes <= 160 * 1024, "LDS");
 };
 
 // Tile order: workgroups are dealt to the 8 XCDs round-robin by launch
@@ -66,6 +127,13 @@ __device__ __forceinline__ void tile_of(int i, int tiles_m, int tiles_n, int& tm
   tn = (blk % bn) * 8 + in % 8;
 }
 
+// wait until at most N of this wave's copies are outstanding, then barrier
+template <int N>
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  static_assert(N >= 0 && N <= 15, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 template <int FMT, bool OUT_F32, class CFG>
 __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __restrict__ A,
                                                               const uint8_t* __restrict__ packed,
@@ -74,14 +142,15 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
                                                               void* __restrict__ C, int M, int N,
                                                               int K) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
-  constexpr int kThreads = CFG::kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * A_LD];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * B_LD];
-  __shared__ uint32_t Ss[2][BN];  // raw scale (and zero) bytes of each B row for the k-tile
+  constexpr int kABytes = CFG::kABytes, kBBytes = CFG::kBBytes;
+  using L = Layout<FMT, CFG>;
+  using ST = ScaleTile<FMT>;
+  constexpr int E = ST::kElems;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / CFG::WGN;
   const int wn = wave % CFG::WGN;
   const int l16 = lane & 15;
@@ -97,78 +166,90 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
 
   // Buffer descriptors over this workgroup's rows: rows past M / N read as 0.
   const uint32_t arow_b = (uint32_t)K * 2u, brow_b = (uint32_t)K >> 1;
-  const rsrc_t ar = make_rsrc(A + (int64_t)m_base * K, (uint32_t)min(BM, M - m_base) * arow_b);
-  const rsrc_t br = make_rsrc(packed + (int64_t)n_base * brow_b, (uint32_t)min(BN, N - n_base) * brow_b);
   const int brows = min(BN, N - n_base);
+  const rsrc_t ar = make_rsrc(A + (int64_t)m_base * K, (uint32_t)min(BM, M - m_base) * arow_b);
+  const rsrc_t br = make_rsrc(packed + (int64_t)n_base * brow_b, (uint32_t)brows * brow_b);
   constexpr int SB = FMT == kInt4 ? 2 : 1;
   const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n_base * groups * SB,
                               (uint32_t)(brows * groups * SB));
   const rsrc_t zr = make_rsrc(FMT == kInt4 ? zeros + (int64_t)n_base * groups : nullptr,
                               FMT == kInt4 ? (uint32_t)(brows * groups) : 0u);
+  const uint32_t lds0 = lds_address(smem);
+  // Resolve the output pointer's scalar load here: a scalar load still in
+  // flight in the k-loop would turn every partial LDS wait there into a full one.
+  asm volatile("" ::"s"(C));
 
-  // ---- global -> register staging of one k-tile (no use before store) -----------
-  // A: BM rows x 8 chunks of 16 B; B: BN rows x 2 chunks of 16 B; chunk ids
-  // tid + kThreads * i.  Thread t < BN fetches row t's raw scale bytes.
-  u32x4_t ra[CFG::kAChunks];
-  u32x4_t rb[CFG::kBChunks];
-  uint32_t rs0 = 0, rs1 = 0;
+  // ---- per-lane source offsets of this wave's A / B copy blocks (k0 = 0) ----
+  // A block b = rows 8b .. 8b+7: lane -> row 8b + lane/8, LDS slot lane%8,
+  // which holds logical chunk c = slot ^ f(row).
+  uint32_t a_src[CFG::kABlocks];
+  int a_k[CFG::kABlocks];
+#pragma unroll
+  for (int i = 0; i < CFG::kABlocks; ++i) {
+    const int b = wave * CFG::kABlocks + i;
+    const int row = 8 * b + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3) ^ (b & 1);
+    a_src[i] = (uint32_t)row * arow_b + (uint32_t)c * 16u;
+    a_k[i] = 8 * c;
+  }
+  // B block: slot q = 64 bb + lane -> row q / 2, which holds half h = (q & 1) ^ ((row >> 2) & 1)
+  uint32_t b_src[CFG::kBBlocks];
+  int b_k[CFG::kBBlocks];
+#pragma unroll
+  for (int i = 0; i < CFG::kBBlocks; ++i) {
+    const int q = 64 * (wave * CFG::kBBlocks + i) + lane;
+    const int row = q >> 1, h = (q & 1) ^ ((row >> 2) & 1);
+    b_src[i] = (uint32_t)row * brow_b + (uint32_t)h * 16u;
+    b_k[i] = 32 * h;
+  }
 
-  auto load_tile = [&](int kt) {
+  // issue the copies of k-tile kt into stage st (CFG::kGroupOps per wave)
+  auto issue = [&](int kt, int st) {
     const int k0 = kt * BK;
+    const uint32_t a_lds = lds0 + st * kABytes + wave * CFG::kABlocks * 1024;
 #pragma unroll
-    for (int i = 0; i < CFG::kAChunks; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id >> 3, k = k0 + (id & 7) * 8;
-      ra[i] = buf_load_b128(ar, k < K ? (uint32_t)row * arow_b + (uint32_t)k * 2u : kBufferOOB);
-    }
+    for (int i = 0; i < CFG::kABlocks; ++i)
+      lds_dma_b128(ar, a_lds + i * 1024,
+                   k0 + a_k[i] < K ? a_src[i] + (uint32_t)k0 * 2u : kBufferOOB);
+    const uint32_t b_lds = lds0 + L::kBOff + st * kBBytes + wave * CFG::kBBlocks * 1024;
 #pragma unroll
-    for (int i = 0; i < CFG::kBChunks; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id >> 1, k = k0 + (id & 1) * 32;
-      rb[i] = buf_load_b128(br, k < K ? (uint32_t)row * brow_b + (uint32_t)(k >> 1) : kBufferOOB);
-    }
-    if (tid < BN) {
-      const uint32_t rbase = (uint32_t)(tid * groups);
-      if constexpr (FMT == kInt4) {
-        const uint32_t gi = rbase + (uint32_t)(k0 / 128);
-        rs0 = buf_load_b16(sr, gi * 2u);
-        rs1 = buf_load_b8(zr, gi);
+    for (int i = 0; i < CFG::kBBlocks; ++i)
+      lds_dma_b128(br, b_lds + i * 1024,
+                   k0 + b_k[i] < K ? b_src[i] + (uint32_t)(k0 >> 1) : kBufferOOB);
+  };
+
+  // issue the copies of scale tile u into buffer u & 1 (L::kSBlocks per wave):
+  // copy block sb covers rows (sb % bpa) * 64/E .. + 64/E - 1 of array sb / bpa
+  auto issue_scales = [&](int u) {
+    constexpr int bpa = L::kSArrayBytes / 256;  // copy blocks per array
+    const int m = lane / E, i = lane % E;
+    const uint32_t s_lds = lds0 + L::kSOff + (u & 1) * L::kSBytes;
+#pragma unroll
+    for (int c = 0; c < L::kSBlocks; ++c) {
+      const int sb = wave * L::kSBlocks + c;
+      const int arr = sb / bpa;  // wave-uniform
+      const int row = (sb % bpa) * (64 / E) + m;
+      const int e = u * E + (i ^ scale_swz<E>(row));  // element index in the scale row
+      const uint32_t dst = s_lds + sb * 256;
+      if constexpr (FMT == kMxfp4) {
+        lds_dma_b8(sr, dst, e < groups ? (uint32_t)(row * groups + e) : kBufferOOB);
       } else if constexpr (FMT == kNvfp4) {
-        // blocks k0/16 .. +3 (the two 16-bit halves; blocks past K read 0)
-        const uint32_t b = rbase + (uint32_t)(k0 / 16);
-        rs0 = buf_load_b16(sr, b);
-        rs1 = buf_load_b16(sr, k0 + 32 < K ? b + 2u : kBufferOOB);
+        lds_dma_b16(sr, dst, 2 * e < groups ? (uint32_t)(row * groups + 2 * e) : kBufferOOB);
       } else {
-        const uint32_t b = rbase + (uint32_t)(k0 / 32);
-        rs0 = buf_load_b8(sr, b);
-        rs1 = buf_load_b8(sr, k0 + 32 < K ? b + 1u : kBufferOOB);
+        if (arr == 0)
+          lds_dma_b16(sr, dst, e < groups ? (uint32_t)(row * groups + e) * 2u : kBufferOOB);
+        else
+          lds_dma_b8(zr, dst, e < groups ? (uint32_t)(row * groups + e) : kBufferOOB);
       }
     }
   };
 
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < CFG::kAChunks; ++i) {
-      const int id = tid + kThreads * i;
-      *reinterpret_cast<u32x4_t*>(&As[st][(id >> 3) * A_LD + (id & 7) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CFG::kBChunks; ++i) {
-      const int id = tid + kThreads * i;
-      // two 8-byte stores: the LDS row pitch (40 B) is only 8-byte aligned
-      u32x2_t* dst = reinterpret_cast<u32x2_t*>(&Bs[st][(id >> 1) * B_LD + (id & 1) * 16]);
-      dst[0] = u32x2_t{rb[i][0], rb[i][1]};
-      dst[1] = u32x2_t{rb[i][2], rb[i][3]};
-    }
-    if (tid < BN) {
-      if constexpr (FMT == kInt4)
-        Ss[st][tid] = rs0 | (rs1 << 16);   // bf16 scale | zero << 16
-      else if constexpr (FMT == kNvfp4)
-        Ss[st][tid] = rs0 | (rs1 << 16);   // e4m3 bytes of blocks 0..3
-      else
-        Ss[st][tid] = rs0 | (rs1 << 8);    // e8m0 bytes of blocks 0..1
-    }
-  };
+  // ---- per-lane LDS read offsets -------------------------------------------
+  const int fa = (l16 & 7) ^ ((l16 >> 3) & 1);
+  const uint32_t a_rd0 = (uint32_t)(l16 * 128 + (((2 * g) ^ fa) * 16));
+  const uint32_t a_rd1 = (uint32_t)(l16 * 128 + (((2 * g + 1) ^ fa) * 16));
+  const uint32_t b_rd = (uint32_t)((l16 * 2 + ((g >> 1) ^ ((l16 >> 2) & 1))) * 16 + 8 * (g & 1));
+  const int fs = scale_swz<E>(l16);  // rows of a lane differ by multiples of 16
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -176,46 +257,63 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  issue_scales(0);
+  issue(0, 0);
+  if (KT > 1) issue(1, 1);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool has_next = kt + 1 < KT;
-    if (has_next) load_tile(kt + 1);
+  int cur = 0, nxt = 2;  // stage of k-tile j, stage of k-tile j + 2
+  for (int j = 0; j < KT; ++j) {
+    // this wave's copies of k-tile j (and of any scale tile issued before
+    // k-tile j + 1) done -- those of j + 1 may still fly -- and every wave's:
+    // then all waves are past k-tile j - 1, so its stage (= stage of j + 2)
+    // and the scale buffer last read before it may be refilled
+    if (j + 1 < KT)
+      wait_copies_and_barrier<CFG::kGroupOps>();
+    else
+      wait_copies_and_barrier<0>();
+    if (j + 2 < KT) {
+      if ((j + 2) % ST::kKTiles == 0) issue_scales((j + 2) / ST::kKTiles);
+      issue(j + 2, nxt);
+    }
+
+    const uint8_t* As = smem + cur * kABytes + (wm * TM * 16) * 128;
+    const uint8_t* Bs = smem + L::kBOff + cur * kBBytes + (wn * TN * 16) * 32;
+    // scale element of lane group g in this k-tile, and its slot
+    const int jt = j % ST::kKTiles;
+    const int se = FMT == kInt4 ? (jt >> 1) : 2 * jt + (g >> 1);
+    const uint8_t* Ss = smem + L::kSOff + ((j / ST::kKTiles) & 1) * L::kSBytes +
+                        ((wn * TN * 16 + l16) * E + (se ^ fs)) * 4;
 
     // LDS reads first: this k-tile's B fragments (16 codes = 8 bytes per lane
     // per tile, both MFMA steps; codes 16g .. 16g+15 lie in one scale
-    // block), their scale words and the A fragments of step 0; the decode
-    // then overlaps the A reads, and the step-1 A reads overlap the step-0
-    // MFMAs.  (A ragged last k-tile, K % 64 == 32, is zero-filled: A = 0 and
-    // code 0 with a finite scale past K, so both steps run.)
+    // block), their scales and the A fragments of step 0; the decode then
+    // overlaps the A reads, and the step-1 A reads overlap the step-0 MFMAs.
+    // (A ragged last k-tile, K % 64 == 32, is zero-filled: A = 0 and code 0
+    // with a zero scale past K, so both steps run.)
     u32x2_t bq[TN];
-    uint32_t sw[TN];
+    uint32_t sw[TN], zw[TN];
     u32x4_t af0[TM], af1[TM];
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const int row = wn * (TN * 16) + t * 16 + l16;
-      bq[t] = *reinterpret_cast<const u32x2_t*>(&Bs[cur][row * B_LD + 8 * g]);
-      sw[t] = Ss[cur][row];
+      bq[t] = *reinterpret_cast<const u32x2_t*>(Bs + b_rd + t * 16 * 32);
+      sw[t] = *reinterpret_cast<const uint32_t*>(Ss + t * 16 * E * 4);
+      if constexpr (FMT == kInt4)
+        zw[t] = *reinterpret_cast<const uint32_t*>(Ss + t * 16 * E * 4 + L::kSArrayBytes);
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * (TM * 16) + i * 16 + l16;
-      af0[i] = *reinterpret_cast<const u32x4_t*>(&As[cur][row * A_LD + 16 * g]);
-    }
+    for (int i = 0; i < TM; ++i)
+      af0[i] = *reinterpret_cast<const u32x4_t*>(As + i * 16 * 128 + a_rd0);
     __builtin_amdgcn_sched_barrier(0);
     float bs[TN], bz[TN];
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       if constexpr (FMT == kInt4) {
-        bs[t] = bf16_bits_to_f32(sw[t] & 0xFFFFu);
-        bz[t] = (float)(sw[t] >> 16);
+        bs[t] = bf16_bits_to_f32(sw[t]);
+        bz[t] = (float)zw[t];
       } else if constexpr (FMT == kNvfp4) {
-        bs[t] = e4m3_magnitude((sw[t] >> (8 * g)) & 0xFFu);
+        bs[t] = e4m3_magnitude((sw[t] >> (8 * (g & 1))) & 0xFFu);
       } else {
-        bs[t] = e8m0_as_exponent_scale((sw[t] >> (8 * (g >> 1))) & 0xFFu);
+        bs[t] = e8m0_as_exponent_scale(sw[t]);
       }
     }
     auto decode = [&](int s, int t) -> u32x4_t {
@@ -230,10 +328,8 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     // step 0: B column tile t is decoded right before its MFMAs (one decoded
     // fragment live at a time); the step-1 A reads are issued first
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * (TM * 16) + i * 16 + l16;
-      af1[i] = *reinterpret_cast<const u32x4_t*>(&As[cur][row * A_LD + 16 * g + 8]);
-    }
+    for (int i = 0; i < TM; ++i)
+      af1[i] = *reinterpret_cast<const u32x4_t*>(As + i * 16 * 128 + a_rd1);
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const u32x4_t bf = decode(0, t);
@@ -246,12 +342,11 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
 #pragma unroll
       for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(af1[i], bf, acc[i][t]);
     }
-
-    if (has_next) store_tile(cur ^ 1);
-    __syncthreads();
+    cur = cur == kStages - 1 ? 0 : cur + 1;
+    nxt = nxt == kStages - 1 ? 0 : nxt + 1;
   }
 
-  // ---- epilogue: lane holds rows 4g..4g+3 of each 16x16 tile, column l16 ----
+// ---- epilogue: lane holds rows 4g..4g+3 of each 16x16 tile, column l16 ----
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -278,6 +373,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
 // for tuning: it halves the A-fragment LDS reads but doubles the decode)
 using CfgA = TileCfg<2, 4, 8, 4>;
 using CfgB = TileCfg<4, 2, 4, 8>;
+using CfgC = TileCfg<2, 2, 8, 8>;
 
 template <int FMT, bool OUT_F32, class CFG>
 hipError_t launch_cfg(const GemmArgs& a) {
@@ -295,6 +391,7 @@ hipError_t launch_fmt(const GemmArgs& a) {
     return e ? atoi(e) : 0;
   }();
   if (cfg_env == 1) return launch_cfg<FMT, OUT_F32, CfgB>(a);
+  if (cfg_env == 2) return launch_cfg<FMT, OUT_F32, CfgC>(a);
   return launch_cfg<FMT, OUT_F32, CfgA>(a);
 }
 
