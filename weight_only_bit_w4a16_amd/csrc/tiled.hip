@@ -13,10 +13,12 @@
 // feeds to its own MFMAs, so no bf16 weight tile ever exists in memory.
 //
 // Workgroup tile 256 x 256 (M x N), k-tile 64, 8 waves as 2 x 4, each wave
-// 128 x 64 = 8 x 4 MFMA 16x16x32 tiles.  A and B k-tiles sit in a ring of
-// three LDS stages filled by asynchronous global -> LDS copies (no staging
-// registers, no LDS stores by the waves): while the waves multiply stage j,
-// the copies of k-tiles j+1 and j+2 are in flight.  Scales arrive the same
+// 128 x 64 = 8 x 4 MFMA 16x16x32 tiles, each computed transposed (weights as
+// the MFMA's first operand) so that a lane ends up with 4 consecutive output
+// columns of one row.  A and B k-tiles sit in two LDS stages filled by
+// asynchronous global -> LDS copies (no staging registers, no LDS stores by
+// the waves): while the waves multiply stage j, the copies of k-tile j+1 are
+// in flight.  Scales arrive the same
 // way, once per scale tile of several k-tiles, in two alternating buffers.
 // Inside a k-tile, lane group g (lanes 16g .. 16g+15) owns codes 16g ..
 // 16g+15 of each row: one 8-byte LDS read per B fragment covers both 32-k
@@ -44,7 +46,7 @@ namespace w4a16 {
 namespace {
 
 constexpr int BK = 64;
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 
 // Scale tile: each of the BN rows brings E consecutive elements of its scale
 // row (E consecutive lanes, one global run per row), covering kKTiles k-tiles.
@@ -259,21 +261,16 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
 
   issue_scales(0);
   issue(0, 0);
-  if (KT > 1) issue(1, 1);
 
-  int cur = 0, nxt = 2;  // stage of k-tile j, stage of k-tile j + 2
+  int cur = 0, nxt = 1;  // stage of k-tile j, stage of k-tile j + 1
   for (int j = 0; j < KT; ++j) {
-    // this wave's copies of k-tile j (and of any scale tile issued before
-    // k-tile j + 1) done -- those of j + 1 may still fly -- and every wave's:
-    // then all waves are past k-tile j - 1, so its stage (= stage of j + 2)
-    // and the scale buffer last read before it may be refilled
-    if (j + 1 < KT)
-      wait_copies_and_barrier<CFG::kGroupOps>();
-    else
-      wait_copies_and_barrier<0>();
-    if (j + 2 < KT) {
-      if ((j + 2) % ST::kKTiles == 0) issue_scales((j + 2) / ST::kKTiles);
-      issue(j + 2, nxt);
+    // this wave's copies of k-tile j (and of its scale tile) done, and every
+    // wave's: then all waves are past k-tile j - 1, so its stage (= stage of
+    // j + 1) and the scale buffer last read before it may be refilled
+    wait_copies_and_barrier<0>();
+    if (j + 1 < KT) {
+      if ((j + 1) % ST::kKTiles == 0) issue_scales((j + 1) / ST::kKTiles);
+      issue(j + 1, nxt);
     }
 
     const uint8_t* As = smem + cur * kABytes + (wm * TM * 16) * 128;
@@ -334,33 +331,44 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     for (int t = 0; t < TN; ++t) {
       const u32x4_t bf = decode(0, t);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(af0[i], bf, acc[i][t]);
+      for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(bf, af0[i], acc[i][t]);
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const u32x4_t bf = decode(1, t);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(af1[i], bf, acc[i][t]);
+      for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(bf, af1[i], acc[i][t]);
     }
     cur = cur == kStages - 1 ? 0 : cur + 1;
     nxt = nxt == kStages - 1 ? 0 : nxt + 1;
   }
 
-// ---- epilogue: lane holds rows 4g..4g+3 of each 16x16 tile, column l16 ----
+// ---- epilogue: lane holds output row l16 of each 16x16 tile, columns
+// 4g .. 4g+3 (one 8- or 16-byte store when the rows allow aligned vectors)
+  const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & (OUT_F32 ? 15 : 7)) == 0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int m = m_base + wm * (TM * 16) + i * 16 + l16;
+    if (m >= M) continue;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const int n = n_base + wn * (TN * 16) + t * 16 + l16;
-      if (n >= N) continue;
+      const int n0 = n_base + wn * (TN * 16) + t * 16 + 4 * g;
+      const f32x4_t v = acc[i][t];
+      if (vec && n0 < N) {
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(C) + (int64_t)m * N + n0) = v;
+        } else {
+          *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(C) + (int64_t)m * N + n0) =
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m_base + wm * (TM * 16) + i * 16 + 4 * g + r;
-        if (m < M) {
-          if constexpr (OUT_F32) {
-            reinterpret_cast<float*>(C)[(int64_t)m * N + n] = acc[i][t][r];
-          } else {
-            reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n] = (__bf16)acc[i][t][r];
+        for (int r = 0; r < 4; ++r) {
+          if (n0 + r < N) {
+            if constexpr (OUT_F32)
+              reinterpret_cast<float*>(C)[(int64_t)m * N + n0 + r] = v[r];
+            else
+              reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n0 + r] = (__bf16)v[r];
           }
         }
       }
