@@ -35,10 +35,15 @@ namespace {
 
 constexpr int kMaxWaves = 16;
 constexpr int kAStage = 2;  // 16-byte chunks of A per thread when A is staged in LDS
+constexpr int kSStage = 3;  // scale dwords per thread when the scales are staged in LDS
+constexpr int kZStage = 2;  // zero dwords per thread (int4)
 
 // FULL: K % 128 == 0, so every chunk of a k-block below KB exists and the
 // validity of a k-block is the same for the whole wave.
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL>
+// S_LDS: the workgroup's scale (and zero) bytes are copied to LDS once, in
+// a few coalesced copies, instead of per-lane loads per k-block (those cost
+// one memory request per row and k-block, as many as the weights).
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const uint8_t* __restrict__ zeros, void* __restrict__ C,
@@ -73,6 +78,55 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   const rsrc_t zr = make_rsrc(FMT == kInt4 ? zeros + (int64_t)n0 * groups : nullptr,
                               FMT == kInt4 ? (uint32_t)(rows * groups) : 0u);
 
+  // Scale staging: rows n0 .. n0+rows-1 of the scales (and zeros) are one
+  // contiguous block; it is read as dwords from the 4-byte aligned address at
+  // or below its start (delta bytes before it) into registers, issued before
+  // everything else, and written to LDS after the A region once they land.
+  const int am = M < 16 ? M : 16;
+  const uint32_t s_off = A_LDS ? (((uint32_t)(am + 1) * (uint32_t)K * 2u + 15u) & ~15u) : 0u;
+  const uint32_t z_off = s_off + (((16u * (uint32_t)groups * SB + 6u) + 15u) & ~15u);
+  uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
+  uint32_t sst[kSStage], zst[kZStage];
+  if constexpr (S_LDS) {
+    auto window = [&](const uint8_t* start, uint32_t bytes, uint32_t& delta, uint32_t& words) {
+      const uintptr_t al = reinterpret_cast<uintptr_t>(start) & ~(uintptr_t)3;
+      delta = (uint32_t)(reinterpret_cast<uintptr_t>(start) - al);
+      words = (delta + bytes + 3u) / 4u;  // may read <= 3 bytes past the block (same page)
+      return make_rsrc(reinterpret_cast<const void*>(al), words * 4u);
+    };
+    const rsrc_t ss = window(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB,
+                             (uint32_t)(rows * groups * SB), s_delta, s_words);
+#pragma unroll
+    for (int i = 0; i < kSStage; ++i) {
+      const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+      sst[i] = buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB);
+    }
+    if constexpr (FMT == kInt4) {
+      const rsrc_t zs = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), z_delta, z_words);
+#pragma unroll
+      for (int i = 0; i < kZStage; ++i) {
+        const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+        zst[i] = buf_load_b32(zs, w < z_words ? w * 4u : kBufferOOB);
+      }
+    }
+  }
+  auto store_scales = [&]() {
+    if constexpr (S_LDS) {
+#pragma unroll
+      for (int i = 0; i < kSStage; ++i) {
+        const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+        if (w < s_words) reinterpret_cast<uint32_t*>(a_lds + s_off)[w] = sst[i];
+      }
+      if constexpr (FMT == kInt4) {
+#pragma unroll
+        for (int i = 0; i < kZStage; ++i) {
+          const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+          if (w < z_words) reinterpret_cast<uint32_t*>(a_lds + z_off)[w] = zst[i];
+        }
+      }
+    }
+  };
+
   // A staging (few rows): the whole workgroup copies its A rows to LDS once.
   // These loads are issued first, so waiting for them (vmcnt retires in
   // issue order) does not wait for the weight stream issued after them.
@@ -99,7 +153,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     // scales first: vmcnt retires in issue order, so the first k-block's
     // arithmetic then waits only for its own weights
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < (S_LDS ? 0 : U); ++u) {
       const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
@@ -147,6 +201,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[u][j] = src[j];
       }
+      if constexpr (S_LDS) {
+        // this lane's scale (and zero) bytes from the staged block; past K
+        // the weights and A are zero, so any finite scale will do
+        const int c = kb * 4 + g;
+        const bool ok = FULL || c < chunks;
+        const uint8_t* sb = a_lds + s_off + s_delta;
+        if constexpr (FMT == kInt4) {
+          const int gi = nl * groups + (ok ? kb : 0);
+          sraw[u] = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
+          zraw[u] = (a_lds + z_off + z_delta)[gi];
+        } else if constexpr (FMT == kNvfp4) {
+          sraw[u] = *reinterpret_cast<const uint16_t*>(sb + nl * groups + 2 * (ok ? c : 0));
+        } else {
+          sraw[u] = sb[nl * groups + (ok ? c : 0)];
+        }
+      }
       if constexpr (FMT == kInt4) {
         // the +code (or +(128 + code)) and -zero (or -(128 + zero)) products
         // go to separate accumulators that follow the same rounding
@@ -185,7 +255,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
 
   int kbase = wave * U;
   issue(kbase);
+  if constexpr (S_LDS && !A_LDS) {
+    store_scales();
+    __syncthreads();
+  }
   if constexpr (A_LDS) {
+    store_scales();
     // copy the staged rows, then zero row `arows` (a16 .. a16 + K/8 chunks)
 #pragma unroll
     for (int i = 0; i < kAStage; ++i) {
@@ -231,6 +306,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   }
 }
 
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL>
+hipError_t launch_s(const GemmArgs& a, dim3 grid, dim3 block, bool s_lds, unsigned lds_a,
+                    unsigned lds_s) {
+  if (s_lds)
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, true>), grid, block,
+                       lds_a + lds_s, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M,
+                       (int)a.N, (int)a.K);
+  else
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, false>), grid, block, lds_a,
+                       a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N,
+                       (int)a.K);
+  return hipGetLastError();
+}
+
 template <int FMT, bool OUT_F32, int U>
 hipError_t launch_u(const GemmArgs& a, int waves) {
   dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
@@ -238,23 +327,23 @@ hipError_t launch_u(const GemmArgs& a, int waves) {
   const int64_t arows = a.M < 16 ? a.M : 16;
   const int64_t a_bytes = arows * a.K * 2;
   const bool a_lds = a_bytes <= (int64_t)kAStage * 16 * 64 * waves && a_bytes <= 64 * 1024;
-  const unsigned lds = (unsigned)(a_bytes + a.K * 2);  // + the zero row
+  // LDS: A rows + a zero row (16-byte aligned), then the scale and zero windows
+  const unsigned lds_a = a_lds ? (unsigned)(((arows + 1) * a.K * 2 + 15) & ~15) : 0u;
+  constexpr int SB = FMT == kInt4 ? 2 : 1;
+  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
+  const int64_t z_cap = FMT == kInt4 ? 16 * groups + 6 : 0;
+  const int64_t lds_s = s_cap + z_cap;
+  // staged when every dword of the windows has a staging register
+  const int64_t threads = 64 * waves;
+  const bool s_lds = (16 * groups * SB + 6) / 4 <= kSStage * threads &&
+                     (16 * groups + 6) / 4 <= kZStage * threads && lds_s <= 32 * 1024;
   const bool full = a.K % 128 == 0;
   const dim3 block(64 * waves);
-  if (a_lds && full) {
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, true, true>), grid, block, lds, a.stream,
-                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
-  } else if (a_lds) {
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, true, false>), grid, block, lds, a.stream,
-                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
-  } else if (full) {
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, false, true>), grid, block, 0, a.stream,
-                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
-  } else {
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, false, false>), grid, block, 0, a.stream,
-                       a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K);
-  }
-  return hipGetLastError();
+  if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
+  if (a_lds) return launch_s<FMT, OUT_F32, U, true, false>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
+  if (full) return launch_s<FMT, OUT_F32, U, false, true>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
+  return launch_s<FMT, OUT_F32, U, false, false>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
 }
 
 // Work split: each wave takes U consecutive k-blocks per pass (U 16-byte
