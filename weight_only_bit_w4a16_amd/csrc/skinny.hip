@@ -43,7 +43,10 @@ constexpr int kZStage = 2;  // zero dwords per thread (int4)
 // S_LDS: the workgroup's scale (and zero) bytes are copied to LDS once, in
 // a few coalesced copies, instead of per-lane loads per k-block (those cost
 // one memory request per row and k-block, as many as the weights).
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS>
+// A_DMA (with !A_LDS): each wave copies the A rows of its own k-blocks
+// straight into a private LDS region (asynchronous global -> LDS copies of
+// contiguous 256-byte row pieces) instead of per-lane A loads.
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const uint8_t* __restrict__ zeros, void* __restrict__ C,
@@ -85,6 +88,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   const int am = M < 16 ? M : 16;
   const uint32_t s_off = A_LDS ? (((uint32_t)(am + 1) * (uint32_t)K * 2u + 15u) & ~15u) : 0u;
   const uint32_t z_off = s_off + (((16u * (uint32_t)groups * SB + 6u) + 15u) & ~15u);
+  const uint32_t z_cap = FMT == kInt4 ? ((16u * (uint32_t)groups + 6u + 15u) & ~15u) : 0u;
+  // per-wave A regions (A_DMA) after the scale and zero windows
+  const uint32_t a_dma_off = S_LDS ? z_off + z_cap : s_off;
+  const uint32_t a_wave = lds_address(a_lds) + a_dma_off +
+                          (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (uint32_t)(U * 4096);
   uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
   uint32_t sst[kSStage], zst[kZStage];
   if constexpr (S_LDS) {
@@ -169,13 +177,31 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (A_DMA) {
+      // k-block kb -> slot u: rows 4i .. 4i+3 per copy; lane -> row 4i + l/16,
+      // LDS chunk l%16, which holds 16-byte chunk (l%16) ^ row of the row's
+      // 256 bytes (the fragment reads of 16 rows then hit distinct banks)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kb = kbase + u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * i + (lane >> 4);
+          const int ch = (lane & 15) ^ r;
+          const bool ok = kb < KB && (FULL || kb * 128 + 8 * ch < K);
+          lds_dma_b128(ar, a_wave + (uint32_t)(u * 4096 + i * 1024),
+                       ok ? ((uint32_t)r * (uint32_t)K + (uint32_t)kb * 128u + 8u * (uint32_t)ch) * 2u
+                          : kBufferOOB);
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
       q[u] = buf_load_b128(wr, ok ? (uint32_t)nl * rowb + (uint32_t)c * 16u : kBufferOOB);
-      if constexpr (!A_LDS) {
+      if constexpr (!A_LDS && !A_DMA) {
         const uint32_t aoff = ((uint32_t)nl * (uint32_t)K + (uint32_t)c * 32u) * 2u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[u][j] = buf_load_b128(ar, ok ? aoff + 16u * j : kBufferOOB);
@@ -188,10 +214,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
 
   const int arow = nl < arows ? nl : arows;  // row arows of the LDS copy is zeros
   auto compute = [&](int kbase) {
+    // the copies are invisible to the compiler's own waits: wait for all of
+    // this pass's loads (whatever order they were issued in)
+    if constexpr (A_DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = kbase + u;
       if (FULL && kb >= KB) break;  // wave-uniform: nothing was loaded
+      if constexpr (A_DMA) {
+        const uint8_t* src = a_lds + a_dma_off + (size_t)wave * (U * 4096) + u * 4096 + nl * 256;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a[u][j] = *reinterpret_cast<const u32x4_t*>(src + (((4 * g + j) ^ nl) * 16));
+      }
       if constexpr (A_LDS) {
         const int c = kb * 4 + g;
         const int col = (FULL || c < chunks) ? c * 32 : 0;
@@ -306,17 +341,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   }
 }
 
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL>
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA>
 hipError_t launch_s(const GemmArgs& a, dim3 grid, dim3 block, bool s_lds, unsigned lds_a,
                     unsigned lds_s) {
+  const unsigned lds_dma = A_DMA ? block.x / 64 * U * 4096u : 0u;
   if (s_lds)
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, true>), grid, block,
-                       lds_a + lds_s, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M,
-                       (int)a.N, (int)a.K);
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, true, A_DMA>), grid, block,
+                       lds_a + lds_s + lds_dma, a.stream, a.A, a.packed, a.scales, a.zeros, a.C,
+                       (int)a.M, (int)a.N, (int)a.K);
   else
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, false>), grid, block, lds_a,
-                       a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N,
-                       (int)a.K);
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, false, A_DMA>), grid, block,
+                       lds_a + lds_dma, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M,
+                       (int)a.N, (int)a.K);
   return hipGetLastError();
 }
 
@@ -332,7 +368,7 @@ hipError_t launch_u(const GemmArgs& a, int waves) {
   constexpr int SB = FMT == kInt4 ? 2 : 1;
   const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
   const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
-  const int64_t z_cap = FMT == kInt4 ? 16 * groups + 6 : 0;
+  const int64_t z_cap = FMT == kInt4 ? (16 * groups + 6 + 15) & ~15 : 0;
   const int64_t lds_s = s_cap + z_cap;
   // staged when every dword of the windows has a staging register
   const int64_t threads = 64 * waves;
@@ -340,10 +376,18 @@ hipError_t launch_u(const GemmArgs& a, int waves) {
                      (16 * groups + 6) / 4 <= kZStage * threads && lds_s <= 32 * 1024;
   const bool full = a.K % 128 == 0;
   const dim3 block(64 * waves);
-  if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
-  if (a_lds) return launch_s<FMT, OUT_F32, U, true, false>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
-  if (full) return launch_s<FMT, OUT_F32, U, false, true>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
-  return launch_s<FMT, OUT_F32, U, false, false>(a, grid, block, s_lds, lds_a, (unsigned)lds_s);
+  static const bool no_dma = [] {
+    const char* e = getenv("W4A16_SKINNY_NO_ADMA");
+    return e && atoi(e) == 1;
+  }();
+  const bool a_dma = !a_lds && !no_dma && waves * U * 4096 <= 128 * 1024;
+  const unsigned ls = (unsigned)lds_s;
+  if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true, false>(a, grid, block, s_lds, lds_a, ls);
+  if (a_lds) return launch_s<FMT, OUT_F32, U, true, false, false>(a, grid, block, s_lds, lds_a, ls);
+  if (a_dma && full) return launch_s<FMT, OUT_F32, U, false, true, true>(a, grid, block, s_lds, lds_a, ls);
+  if (a_dma) return launch_s<FMT, OUT_F32, U, false, false, true>(a, grid, block, s_lds, lds_a, ls);
+  if (full) return launch_s<FMT, OUT_F32, U, false, true, false>(a, grid, block, s_lds, lds_a, ls);
+  return launch_s<FMT, OUT_F32, U, false, false, false>(a, grid, block, s_lds, lds_a, ls);
 }
 
 // Work split: each wave takes U consecutive k-blocks per pass (U 16-byte
@@ -363,6 +407,11 @@ hipError_t launch_fmt(const GemmArgs& a) {
   int waves = (KB + U - 1) / U;
   if (waves > kMaxWaves) waves = kMaxWaves;
   if (waves < 1) waves = 1;
+  // A rows that do not fit the LDS copy go through per-wave LDS regions of
+  // U k-blocks (4 KB each): keep those within 128 KB
+  const int64_t arows = a.M < 16 ? a.M : 16;
+  const bool a_big = arows * a.K * 2 > (int64_t)kAStage * 16 * 64 * waves || arows * a.K * 2 > 64 * 1024;
+  if (!u_env && a_big && waves * U > 32) U = 32 / waves > 0 ? 32 / waves : 1;
   if (U == 1) return launch_u<FMT, OUT_F32, 1>(a, waves);
   if (U == 2) return launch_u<FMT, OUT_F32, 2>(a, waves);
   return launch_u<FMT, OUT_F32, 4>(a, waves);
