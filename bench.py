@@ -99,7 +99,7 @@ def main():
                          "2 mxfp4; bf16 out) instead of --workload")
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight copies to rotate over (0: enough for >= 1 GiB)")
-    ap.add_argument("--m4096-steps", type=int, default=100)
+    ap.add_argument("--m4096-steps", type=int, default=300)
     ap.add_argument("--no-m4096", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -203,6 +203,27 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
+    def measure_single(fmt, M, N, K, out, steps, warmup):
+        """One GEMM workload timed over `steps` launches that rotate over
+        enough distinct weight copies (>= 1 GiB together) that every launch
+        reads its weights from HBM.  Returns (case, total ms, copies, kernel)."""
+        case = inputs.make_case(fmt, M, N, K, seed=0)
+        A, p, s, z = to_dev(case)
+        _, tbytes = algorithmic_bytes(fmt, M, N, K, out)
+        copies = args.copies or max(1, min(128, math.ceil((1 << 30) / tbytes)))
+        odt = torch.float32 if out == "f32" else torch.bfloat16
+        C = torch.empty((M, N), dtype=odt, device=dev)
+        calls = []
+        for r in range(copies):
+            pr = p if r == 0 else p.clone()
+            sr = s if r == 0 else s.clone()
+            zr = z if (r == 0 or z is None) else z.clone()
+            calls.append([w4.PreparedGemm(fmt, A, pr, sr, zr, C, path=args.path)])
+        total = timed(calls, steps, warmup)
+        kernel = calls[0][0].kernel
+        del calls, C
+        return case, total, copies, kernel
+
     result = {}
     if args.workload == CHAIN:
         shapes = inputs.decoder_chain_shapes()
@@ -230,22 +251,10 @@ def main():
         weight_bytes = wbytes
     else:
         fmt, M, N, K, out = WORKLOADS[args.workload]
-        case = inputs.make_case(fmt, M, N, K, seed=0)
-        A, p, s, z = to_dev(case)
+        case, total_ms, copies, kernel = measure_single(fmt, M, N, K, out, args.steps, args.warmup)
         wbytes, tbytes = algorithmic_bytes(fmt, M, N, K, out)
-        copies = args.copies or max(1, min(128, math.ceil((1 << 30) / tbytes)))
-        odt = torch.float32 if out == "f32" else torch.bfloat16
-        C = torch.empty((M, N), dtype=odt, device=dev)
-        calls = []
-        for r in range(copies):
-            pr = p if r == 0 else p.clone()
-            sr = s if r == 0 else s.clone()
-            zr = z if (r == 0 or z is None) else z.clone()
-            calls.append([w4.PreparedGemm(fmt, A, pr, sr, zr, C, path=args.path)])
-        total_ms = timed(calls, args.steps, args.warmup)
         ms = total_ms / args.steps
         launches_per_step = 1
-        kernel = calls[0][0].kernel
         bytes_per_launch = tbytes
         config = {"workload": args.workload, "format": w4.FORMAT_NAMES[fmt], "M": M, "N": N, "K": K,
                   "out": out, "weight_copies": copies, "kernel": kernel}
@@ -263,7 +272,8 @@ def main():
         fmt, M, N, K, out = WORKLOADS[args.workload]
         ach = 2.0 * M * N * K / (mean_launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profile(kernel, workload)}
     else:
         ach = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -293,13 +303,10 @@ def main():
     # ---- the compute-bound point of the metric: MXFP4 at M = 4096 -------------
     if args.workload == "decode_gemv_int4_m1" and not args.no_m4096:
         fmt, M, N, K, out = WORKLOADS["mxfp4_m4096"]
-        case = inputs.make_case(fmt, M, N, K, seed=0)
-        A, p, s, z = to_dev(case)
-        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        call = w4.PreparedGemm(fmt, A, p, s, z, C)
-        t4 = timed([[call]], args.m4096_steps, 10)
+        _, t4, copies4, kernel4 = measure_single(fmt, M, N, K, out, args.m4096_steps, 10)
         tfl = 2.0 * M * N * K / (t4 / args.m4096_steps * 1e-3) / 1e12
-        result["m4096"] = {"workload": "mxfp4_m4096", "kernel": call.kernel, "steps": args.m4096_steps,
+        result["m4096"] = {"workload": "mxfp4_m4096", "kernel": kernel4, "steps": args.m4096_steps,
+                           "weight_copies": copies4,
                            "ms_per_step": round(t4 / args.m4096_steps, 4),
                            "tflops": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
                            "frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
