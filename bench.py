@@ -101,6 +101,8 @@ def main():
                     help="distinct weight copies to rotate over (0: enough for >= 1 GiB)")
     ap.add_argument("--m4096-steps", type=int, default=300)
     ap.add_argument("--no-m4096", action="store_true")
+    ap.add_argument("--no-ungrouped", action="store_true",
+                    help="decode chain: skip timing the 197 ungrouped launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -229,22 +231,40 @@ def main():
         shapes = inputs.decoder_chain_shapes()
         calls, wbytes, tbytes = [], 0, 0
         out = torch.empty((1, max(n for _, n, _ in shapes)), dtype=torch.bfloat16, device=dev)
+        dev_w, dev_a = [], []
         for i, (name, n, k) in enumerate(shapes):
             case = inputs.make_case(0, 1, n, k, inputs.chain_seed(0, i))
             A, p, s, z = to_dev(case)
+            dev_w.append((p, s, z))
+            dev_a.append(A)
             calls.append(w4.PreparedGemm(0, A, p, s, z, out[:, :n], path=args.path))
             wb, tb = algorithmic_bytes(0, 1, n, k, "bf16")
             wbytes += wb
             tbytes += tb
-        eager_ms = timed([calls], max(1, args.steps // 10), args.warmup) / max(1, args.steps // 10)
-        total_ms = timed([calls], args.steps, args.warmup, graph=True)
+        # the framework's decode step: matrices that read the same input in one launch
+        gcalls, gouts = [], []
+        for grp in inputs.decoder_chain_groups():
+            A = dev_a[grp[0]]
+            if len(grp) == 1:
+                gcalls.append(calls[grp[0]])
+                continue
+            outs = [torch.empty((1, shapes[i][1]), dtype=torch.bfloat16, device=dev) for i in grp]
+            gouts.append(outs)
+            gcalls.append(w4.PreparedGroupedGemm(0, A, [dev_w[i] for i in grp], outs, path=args.path))
+        eager_ms = timed([gcalls], max(1, args.steps // 10), args.warmup) / max(1, args.steps // 10)
+        ungrouped_ms = None if args.no_ungrouped else \
+            timed([calls], args.steps, args.warmup, graph=True) / args.steps
+        total_ms = timed([gcalls], args.steps, args.warmup, graph=True)
         ms = total_ms / args.steps
-        launches_per_step = len(calls)
+        launches_per_step = len(gcalls)
         kernel = calls[0].kernel
-        bytes_per_launch = tbytes / len(calls)
+        bytes_per_launch = tbytes / len(gcalls)
         config = {"workload": CHAIN, "matrices": len(calls), "M": 1, "format": "int4_g128",
-                  "out": "bf16", "launches_per_step": len(calls), "timing": "hip_graph_replay",
-                  "eager_ms_per_step": round(eager_ms, 4)}
+                  "out": "bf16", "launches_per_step": len(gcalls),
+                  "grouping": "per layer [q,k,v] [o] [gate,up] [down], then [lm_head]",
+                  "timing": "hip_graph_replay", "eager_ms_per_step": round(eager_ms, 4),
+                  "ungrouped_launches_per_step": len(calls),
+                  "ungrouped_ms_per_step": None if ungrouped_ms is None else round(ungrouped_ms, 4)}
         value = wbytes / (ms * 1e-3) / 1e9
         unit = "GB/s"
         workload = CHAIN

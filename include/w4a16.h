@@ -96,6 +96,27 @@ int w4a16_gemm(int format, const void* A, const void* packed, const void* scales
                const void* zeros, void* C, int64_t M, int64_t N, int64_t K,
                void* stream);
 
+/* Several weight matrices that share one activation matrix A and one K --
+ * e.g. the q, k and v projections of a decoder layer, or its gate and up
+ * projections, which all multiply the same layer input (page
+ * "megakernel_int4_weight_decode.py": the contract table's seven int4 triples
+ * per layer, each applied as h . W^T; its spec fuses the decode step to cut
+ * the per-kernel overhead its performance section measures, eager vs graph).
+ * For i < count:
+ *     C[i] = A . dequant(packed[i], scales[i], zeros[i])^T,  C[i] (M, N[i]).
+ * `packed`, `scales`, `C` and `N` are HOST arrays of `count` entries (device
+ * pointers / sizes), read during the call only; `zeros` is such an array for
+ * int4 and must be NULL for NVFP4 / MXFP4.  Each member follows the layout,
+ * alignment and accuracy rules of w4a16_gemm.  1 <= count <= W4A16_MAX_GROUP
+ * (else W4A16_ERR_SHAPE); members with N[i] == 0 are skipped and their
+ * pointers not checked.  The skinny path computes all members in ONE launch;
+ * the tiled path launches once per member.  Same error, stream and
+ * determinism behaviour as w4a16_gemm. */
+#define W4A16_MAX_GROUP 8
+int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* packed,
+                       const void* const* scales, const void* const* zeros, void* const* C,
+                       const int64_t* N, int64_t M, int64_t K, void* stream);
+
 /* W = dequant(packed, scales, zeros) as bf16 (N, K): each weight's exact value
  * rounded once to nearest even (bit-exact; fp4 weights are exact in bf16 at
  * normal scale ranges).  `format` takes only the format bits.  A checking

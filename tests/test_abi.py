@@ -29,8 +29,8 @@ def _header_defines():
 def test_library_exports_every_declared_function():
     lib = w4.load_library()
     names = _header_functions()
-    assert set(names) == {"w4a16_gemm", "w4a16_dequant", "w4a16_gemm_path",
-                          "w4a16_strerror", "w4a16_version"}
+    assert set(names) == {"w4a16_gemm", "w4a16_gemm_grouped", "w4a16_dequant",
+                          "w4a16_gemm_path", "w4a16_strerror", "w4a16_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -45,10 +45,11 @@ def test_python_constants_match_header():
     assert d["W4A16_PATH_TILED"] == w4.PATH_TILED
     for code in ("OK", "ERR_FORMAT", "ERR_SHAPE", "ERR_NULL", "ERR_ALIGN", "ERR_HIP"):
         assert d["W4A16_" + code] == getattr(w4, code)
+    assert d["W4A16_MAX_GROUP"] == w4.MAX_GROUP
 
 
 def test_version_and_strerror():
-    assert w4.version() == 100
+    assert w4.version() == 101
     for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP):
         assert w4.strerror(code) != "unknown status"
     assert w4.strerror(12345) == "unknown status"
@@ -132,3 +133,52 @@ def test_binding_shape_checks_before_library(monkeypatch):
     with pytest.raises(ValueError):
         w4.gemm(w4.INT4_G128, A, torch.zeros(8, 64, dtype=torch.uint8),
                 torch.zeros(8, 1, dtype=torch.bfloat16), torch.zeros(8, 1, dtype=torch.uint8))
+
+
+# ---- w4a16_gemm_grouped validation (no call below reaches a launch) ---------
+
+def _grouped(fmt, count=3, N=(64, 32, 48), M=1, K=128, A=PA, packed=True, scales=True,
+             zeros="auto", C=True, Nnull=False, bad=None):
+    n = max(count, 1)
+    mk = lambda base: (ctypes.c_void_p * n)(*[0x100000 * (base + 8 * i) for i in range(n)])
+    P, S, Cs = mk(2), mk(3), mk(5)
+    Z = mk(4) if (zeros == "auto" and fmt == w4.INT4_G128) or zeros is True else None
+    if bad:
+        arr, i, val = bad
+        {"P": P, "S": S, "C": Cs, "Z": Z}[arr][i] = val
+    Ns = None if Nnull else (ctypes.c_int64 * n)(*(list(N) + [64] * n)[:n])
+    return w4.load_library().w4a16_gemm_grouped(
+        fmt, A, count, P if packed else None, S if scales else None, Z, Cs if C else None,
+        Ns, M, 0 if K is None else K, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(fmt=3), w4.ERR_FORMAT),
+    (dict(fmt=w4.INT4_G128, count=0), w4.ERR_SHAPE),
+    (dict(fmt=w4.INT4_G128, count=9), w4.ERR_SHAPE),
+    (dict(fmt=w4.INT4_G128, K=96), w4.ERR_SHAPE),              # int4 needs K % 128
+    (dict(fmt=w4.NVFP4, K=48), w4.ERR_SHAPE),                  # K % 32
+    (dict(fmt=w4.NVFP4, N=(64, -1, 32)), w4.ERR_SHAPE),
+    (dict(fmt=w4.NVFP4, Nnull=True), w4.ERR_NULL),
+    (dict(fmt=w4.NVFP4, A=None), w4.ERR_NULL),
+    (dict(fmt=w4.NVFP4, packed=False), w4.ERR_NULL),
+    (dict(fmt=w4.NVFP4, C=False), w4.ERR_NULL),
+    (dict(fmt=w4.NVFP4, zeros=True), w4.ERR_NULL),             # fp4 takes no zeros
+    (dict(fmt=w4.INT4_G128, zeros=False), w4.ERR_NULL),        # int4 needs zeros
+    (dict(fmt=w4.INT4_G128, bad=("Z", 1, None)), w4.ERR_NULL),
+    (dict(fmt=w4.MXFP4, bad=("S", 2, None)), w4.ERR_NULL),
+    (dict(fmt=w4.MXFP4, bad=("P", 1, 0x100008)), w4.ERR_ALIGN),
+    (dict(fmt=w4.NVFP4, bad=("S", 0, 0x100001)), w4.ERR_ALIGN),
+    (dict(fmt=w4.NVFP4 | w4.OUT_F32, bad=("C", 2, 0x100002)), w4.ERR_ALIGN),
+    (dict(fmt=w4.NVFP4, A=ctypes.c_void_p(0x100008)), w4.ERR_ALIGN),
+])
+def test_grouped_validation(kw, expect):
+    assert _grouped(**kw) == expect
+
+
+def test_grouped_zero_extents_check_no_pointer():
+    # M = 0, or every member with N = 0: a valid no-op, NULL pointers allowed
+    assert _grouped(w4.INT4_G128, M=0, A=None, packed=False, scales=False, C=False, zeros=False) == w4.OK
+    assert _grouped(w4.MXFP4, N=(0, 0, 0), A=None, packed=False, scales=False, C=False) == w4.OK
+    # a skipped member's pointers are not checked, the others still are
+    assert _grouped(w4.NVFP4, N=(64, 0, 32), bad=("P", 1, None), C=False) == w4.ERR_NULL

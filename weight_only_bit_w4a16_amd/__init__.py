@@ -28,6 +28,7 @@ PATH_AUTO, PATH_SKINNY, PATH_TILED = 0x0000, 0x1000, 0x2000
 PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
 
 OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5
+MAX_GROUP = 8  # members of one w4a16_gemm_grouped call
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
@@ -53,6 +54,9 @@ def load_library():
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.w4a16_gemm.argtypes = [I, P, P, P, P, P, I64, I64, I64, P]
     lib.w4a16_gemm.restype = I
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    lib.w4a16_gemm_grouped.argtypes = [I, P, I, PP, PP, PP, PP, ctypes.POINTER(I64), I64, I64, P]
+    lib.w4a16_gemm_grouped.restype = I
     lib.w4a16_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
     lib.w4a16_dequant.restype = I
     lib.w4a16_gemm_path.argtypes = [I, I64, I64, I64]
@@ -144,6 +148,65 @@ def gemm(fmt: int, A: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
     if rc != OK:
         raise W4A16Error(rc, "w4a16_gemm")
     return out
+
+
+def _grouped_args(fmt, A, weights, outs, out_dtype):
+    """Check a grouped call's tensors; return (flags, outs, ctypes arrays)."""
+    if not A.is_cuda:
+        raise ValueError("A must be a GPU tensor")
+    if not 1 <= len(weights) <= MAX_GROUP:
+        raise ValueError(f"a group has 1 .. {MAX_GROUP} weight matrices, got {len(weights)}")
+    device = A.device
+    M, K = A.shape
+    _check(A, "A", (M, K), 2, device)
+    if outs is None:
+        outs = [torch.empty((M, w[0].shape[0]), dtype=out_dtype, device=device) for w in weights]
+    if len(outs) != len(weights):
+        raise ValueError("one output per weight matrix")
+    dt = outs[0].dtype
+    if dt not in (torch.bfloat16, torch.float32) or any(o.dtype != dt for o in outs):
+        raise ValueError("outputs must all be bf16 or all fp32")
+    n = len(weights)
+    arr = lambda: (ctypes.c_void_p * n)()
+    P, S, Z, Cs, Ns = arr(), arr(), arr(), arr(), (ctypes.c_int64 * n)()
+    for i, ((packed, scales, zeros), out) in enumerate(zip(weights, outs)):
+        N = packed.shape[0]
+        _check_weights(fmt, packed, scales, zeros, N, K, device)
+        _check(out, f"out[{i}]", (M, N), out.element_size(), device)
+        P[i], S[i], Cs[i], Ns[i] = packed.data_ptr(), scales.data_ptr(), out.data_ptr(), N
+        Z[i] = zeros.data_ptr() if zeros is not None else None
+    flags = OUT_F32 if dt == torch.float32 else OUT_BF16
+    zarr = Z if fmt == INT4_G128 else None
+    return flags, outs, (P, S, zarr, Cs, Ns), (M, K)
+
+
+def gemm_grouped(fmt: int, A: torch.Tensor, weights, outs=None,
+                 out_dtype: torch.dtype = torch.bfloat16, path: str = "auto", stream=None):
+    """C_i = A . dequant(packed_i, scales_i, zeros_i)^T for every
+    (packed_i, scales_i, zeros_i) in `weights` (all with A's K), in one launch
+    on the skinny path.  Returns the list of outputs (asynchronous)."""
+    flags, outs, (P, S, Z, Cs, Ns), (M, K) = _grouped_args(fmt, A, weights, outs, out_dtype)
+    rc = load_library().w4a16_gemm_grouped(int(fmt) | flags | PATHS[path], _ptr(A), len(weights),
+                                           P, S, Z, Cs, Ns, M, K, _stream_handle(stream))
+    if rc != OK:
+        raise W4A16Error(rc, "w4a16_gemm_grouped")
+    return outs
+
+
+class PreparedGroupedGemm:
+    """One w4a16_gemm_grouped call marshalled once (see :class:`PreparedGemm`)."""
+
+    def __init__(self, fmt: int, A, weights, outs, path: str = "auto"):
+        flags, outs, arrays, (M, K) = _grouped_args(fmt, A, weights, outs, torch.bfloat16)
+        self.tensors = (A, list(weights), outs)
+        self.kernel = gemm_path(fmt, M, int(arrays[4][0]), K, path)
+        self._fn = load_library().w4a16_gemm_grouped
+        self._args = (int(fmt) | flags | PATHS[path], _ptr(A), len(weights), *arrays, M, K)
+
+    def __call__(self, stream=None):
+        rc = self._fn(*self._args, _stream_handle(stream))
+        if rc != OK:
+            raise W4A16Error(rc, "w4a16_gemm_grouped")
 
 
 def dequant(fmt: int, packed: torch.Tensor, scales: torch.Tensor,

@@ -44,7 +44,7 @@ int choose_path(int format, int64_t M) {
 
 extern "C" {
 
-int w4a16_version(void) { return 100; }
+int w4a16_version(void) { return 101; }
 
 const char* w4a16_strerror(int status) {
   switch (status) {
@@ -52,7 +52,7 @@ const char* w4a16_strerror(int status) {
     case W4A16_ERR_FORMAT: return "unknown weight format or flag bits";
     case W4A16_ERR_SHAPE:
       return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^22, K % 32 == 0 and K a multiple "
-             "of the format's group size";
+             "of the format's group size (and 1 <= count <= W4A16_MAX_GROUP for a group)";
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for an fp4 format";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
     case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
@@ -94,6 +94,71 @@ int w4a16_gemm(int format, const void* A, const void* packed, const void* scales
   const hipError_t e = choose_path(format, M) == W4A16_PATH_SKINNY ? w4a16::launch_skinny(a)
                                                                    : w4a16::launch_tiled(a);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* packed,
+                       const void* const* scales, const void* const* zeros, void* const* C,
+                       const int64_t* N, int64_t M, int64_t K, void* stream) {
+  int rc = check_format_shape(format, M, 0, K, true);
+  if (rc != W4A16_OK) return rc;
+  if (count < 1 || count > W4A16_MAX_GROUP) return W4A16_ERR_SHAPE;
+  if (!N) return W4A16_ERR_NULL;
+  for (int i = 0; i < count; ++i)
+    if ((rc = check_format_shape(format, M, N[i], K, true)) != W4A16_OK) return rc;
+  const int fmt = format & W4A16_FORMAT_MASK;
+  const bool out_f32 = (format & W4A16_OUT_F32) != 0;
+  int active = 0;
+  for (int i = 0; i < count; ++i) active += N[i] > 0;
+  if (M == 0 || active == 0) return W4A16_OK;  // nothing is read or written
+  if (!A || !packed || !scales || !C) return W4A16_ERR_NULL;
+  if (fmt == W4A16_INT4_G128 ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
+  if (!aligned(A, 16)) return W4A16_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (N[i] == 0) continue;
+    if (!packed[i] || !scales[i] || !C[i] || (fmt == W4A16_INT4_G128 && !zeros[i]))
+      return W4A16_ERR_NULL;
+    if (!aligned(packed[i], 16)) return W4A16_ERR_ALIGN;
+    if (fmt != W4A16_MXFP4 && !aligned(scales[i], 2)) return W4A16_ERR_ALIGN;
+    if (!aligned(C[i], out_f32 ? 4 : 2)) return W4A16_ERR_ALIGN;
+  }
+
+  if (choose_path(format, M) == W4A16_PATH_SKINNY) {
+    w4a16::GroupedArgs g = {};
+    g.fmt = fmt;
+    g.out_f32 = out_f32;
+    g.A = static_cast<const uint16_t*>(A);
+    for (int i = 0; i < count; ++i) {
+      if (N[i] == 0) continue;
+      g.packed[g.count] = static_cast<const uint8_t*>(packed[i]);
+      g.scales[g.count] = scales[i];
+      g.zeros[g.count] = fmt == W4A16_INT4_G128 ? static_cast<const uint8_t*>(zeros[i]) : nullptr;
+      g.C[g.count] = C[i];
+      g.N[g.count] = N[i];
+      ++g.count;
+    }
+    g.M = M;
+    g.K = K;
+    g.stream = static_cast<hipStream_t>(stream);
+    return w4a16::launch_skinny_grouped(g) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+  }
+  // large M: one tiled launch per member (each already fills the GPU)
+  for (int i = 0; i < count; ++i) {
+    if (N[i] == 0) continue;
+    w4a16::GemmArgs a;
+    a.fmt = fmt;
+    a.out_f32 = out_f32;
+    a.A = static_cast<const uint16_t*>(A);
+    a.packed = static_cast<const uint8_t*>(packed[i]);
+    a.scales = scales[i];
+    a.zeros = fmt == W4A16_INT4_G128 ? static_cast<const uint8_t*>(zeros[i]) : nullptr;
+    a.C = C[i];
+    a.M = M;
+    a.N = N[i];
+    a.K = K;
+    a.stream = static_cast<hipStream_t>(stream);
+    if (w4a16::launch_tiled(a) != hipSuccess) return W4A16_ERR_HIP;
+  }
+  return W4A16_OK;
 }
 
 int w4a16_dequant(int format, const void* packed, const void* scales, const void* zeros, void* W,

@@ -20,12 +20,31 @@ struct GemmArgs {
   hipStream_t stream;
 };
 
+// Several weight matrices sharing one A (and K): member i has its own
+// packed / scales / zeros / C and N[i] output columns.
+constexpr int kMaxGroup = 8;
+struct GroupedArgs {
+  int fmt;
+  bool out_f32;
+  const uint16_t* A;
+  int count;  // 1 .. kMaxGroup, every member with N[i] > 0
+  const uint8_t* packed[kMaxGroup];
+  const void* scales[kMaxGroup];
+  const uint8_t* zeros[kMaxGroup];
+  void* C[kMaxGroup];
+  int64_t N[kMaxGroup];
+  int64_t M, K;
+  hipStream_t stream;
+};
+
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, const uint8_t* zeros,
                           uint16_t* W, int64_t N, int64_t K, hipStream_t stream);
 
 // M <= 16 per 16-row slice: split-K over the waves of a workgroup, weights
 // decoded in registers.
 hipError_t launch_skinny(const GemmArgs& a);
+// the same kernel over all members of a group in one launch
+hipError_t launch_skinny_grouped(const GroupedArgs& a);
 
 // large M: LDS-staged tiles, decode into MFMA B fragments.
 hipError_t launch_tiled(const GemmArgs& a);

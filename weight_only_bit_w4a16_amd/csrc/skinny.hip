@@ -38,6 +38,22 @@ constexpr int kAStage = 2;  // 16-byte chunks of A per thread when A is staged i
 constexpr int kSStage = 3;  // scale dwords per thread when the scales are staged in LDS
 constexpr int kZStage = 2;  // zero dwords per thread (int4)
 
+// The weight matrices of one launch: a single GEMM, or several sharing A and
+// K (member i: packed / scales / zeros / C, N[i] columns).  Workgroup x runs
+// 16 columns of the member whose cumulative tile range holds x.
+struct SkinnyMember {
+  const uint8_t* packed;
+  const void* scales;
+  const uint8_t* zeros;
+  void* C;
+  int N;
+  int tile_end;  // 16-column tiles of members 0 .. this one
+};
+struct SkinnyGroup {
+  SkinnyMember m[kMaxGroup];  // one member's fields are contiguous
+  int count;
+};
+
 // FULL: K % 128 == 0, so every chunk of a k-block below KB exists and the
 // validity of a k-block is the same for the whole wave.
 // S_LDS: the workgroup's scale (and zero) bytes are copied to LDS once, in
@@ -46,11 +62,34 @@ constexpr int kZStage = 2;  // zero dwords per thread (int4)
 // A_DMA (with !A_LDS): each wave copies the A rows of its own k-blocks
 // straight into a private LDS region (asynchronous global -> LDS copies of
 // contiguous 256-byte row pieces) instead of per-lane A loads.
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA>
-__global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
-    const uint16_t* __restrict__ A, const uint8_t* __restrict__ packed,
-    const void* __restrict__ scales, const uint8_t* __restrict__ zeros, void* __restrict__ C,
-    int M, int N, int K) {
+// GROUPED: more than one member (a single GEMM reads member 0 only).
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED>
+__global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* __restrict__ A,
+                                                                SkinnyGroup grp, int M, int K) {
+  // the group member whose columns this workgroup computes (uniform; picked
+  // by selects, not by indexing the argument arrays)
+  int gi = 0;
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int i = 1; i < kMaxGroup; ++i)
+      gi = (i < grp.count && (int)blockIdx.x >= grp.m[i - 1].tile_end) ? i : gi;
+  }
+  const uint8_t* packed = grp.m[0].packed;
+  const void* scales = grp.m[0].scales;
+  const uint8_t* zeros = grp.m[0].zeros;
+  void* C = grp.m[0].C;
+  int N = grp.m[0].N, tile0 = 0;
+#pragma unroll
+  for (int i = 1; i < (GROUPED ? kMaxGroup : 1); ++i) {
+    if (gi == i) {
+      packed = grp.m[i].packed;
+      scales = grp.m[i].scales;
+      zeros = grp.m[i].zeros;
+      C = grp.m[i].C;
+      N = grp.m[i].N;
+      tile0 = grp.m[i - 1].tile_end;
+    }
+  }
   // LDS copy of A: arows rows of K bf16, then one row of zeros that lanes
   // past M (and chunks past K) read instead of branching
   extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
@@ -60,7 +99,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   const int waves = blockDim.x >> 6;
   const int nl = lane & 15;  // weight row within the slice / A row supplied
   const int g = lane >> 4;   // 32-code chunk within the k-block
-  const int n0 = blockIdx.x * 16;
+  const int n0 = ((int)blockIdx.x - tile0) * 16;
   const int m0 = blockIdx.y * 16;
   const int n = n0 + nl;
   const int chunks = K >> 5;           // 32-code chunks per row
@@ -341,24 +380,41 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(
   }
 }
 
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA>
-hipError_t launch_s(const GemmArgs& a, dim3 grid, dim3 block, bool s_lds, unsigned lds_a,
-                    unsigned lds_s) {
-  const unsigned lds_dma = A_DMA ? block.x / 64 * U * 4096u : 0u;
-  if (s_lds)
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, true, A_DMA>), grid, block,
-                       lds_a + lds_s + lds_dma, a.stream, a.A, a.packed, a.scales, a.zeros, a.C,
-                       (int)a.M, (int)a.N, (int)a.K);
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, bool S_LDS>
+hipError_t launch_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim3 block, unsigned lds) {
+  if (grp.count > 1)
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, true>), grid, block,
+                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K);
   else
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, false, A_DMA>), grid, block,
-                       lds_a + lds_dma, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M,
-                       (int)a.N, (int)a.K);
+    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, false>), grid, block,
+                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K);
   return hipGetLastError();
 }
 
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA>
+hipError_t launch_s(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim3 block, bool s_lds,
+                    unsigned lds_a, unsigned lds_s) {
+  const unsigned lds_dma = A_DMA ? block.x / 64 * U * 4096u : 0u;
+  if (s_lds)
+    return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, true>(a, grp, grid, block, lds_a + lds_s + lds_dma);
+  return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, false>(a, grp, grid, block, lds_a + lds_dma);
+}
+
 template <int FMT, bool OUT_F32, int U>
-hipError_t launch_u(const GemmArgs& a, int waves) {
-  dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
+hipError_t launch_u(const GroupedArgs& a, int waves) {
+  SkinnyGroup grp = {};
+  int tiles = 0;
+  for (int i = 0; i < a.count; ++i) {
+    grp.m[i].packed = a.packed[i];
+    grp.m[i].scales = a.scales[i];
+    grp.m[i].zeros = a.zeros[i];
+    grp.m[i].C = a.C[i];
+    grp.m[i].N = (int)a.N[i];
+    tiles += (int)((a.N[i] + 15) / 16);
+    grp.m[i].tile_end = tiles;
+  }
+  grp.count = a.count;
+  dim3 grid((unsigned)tiles, (unsigned)((a.M + 15) / 16));
   // stage A in LDS when the workgroup's A slice fits its staging registers
   const int64_t arows = a.M < 16 ? a.M : 16;
   const int64_t a_bytes = arows * a.K * 2;
@@ -382,12 +438,12 @@ hipError_t launch_u(const GemmArgs& a, int waves) {
   }();
   const bool a_dma = !a_lds && !no_dma && waves * U * 4096 <= 128 * 1024;
   const unsigned ls = (unsigned)lds_s;
-  if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true, false>(a, grid, block, s_lds, lds_a, ls);
-  if (a_lds) return launch_s<FMT, OUT_F32, U, true, false, false>(a, grid, block, s_lds, lds_a, ls);
-  if (a_dma && full) return launch_s<FMT, OUT_F32, U, false, true, true>(a, grid, block, s_lds, lds_a, ls);
-  if (a_dma) return launch_s<FMT, OUT_F32, U, false, false, true>(a, grid, block, s_lds, lds_a, ls);
-  if (full) return launch_s<FMT, OUT_F32, U, false, true, false>(a, grid, block, s_lds, lds_a, ls);
-  return launch_s<FMT, OUT_F32, U, false, false, false>(a, grid, block, s_lds, lds_a, ls);
+  if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true, false>(a, grp, grid, block, s_lds, lds_a, ls);
+  if (a_lds) return launch_s<FMT, OUT_F32, U, true, false, false>(a, grp, grid, block, s_lds, lds_a, ls);
+  if (a_dma && full) return launch_s<FMT, OUT_F32, U, false, true, true>(a, grp, grid, block, s_lds, lds_a, ls);
+  if (a_dma) return launch_s<FMT, OUT_F32, U, false, false, true>(a, grp, grid, block, s_lds, lds_a, ls);
+  if (full) return launch_s<FMT, OUT_F32, U, false, true, false>(a, grp, grid, block, s_lds, lds_a, ls);
+  return launch_s<FMT, OUT_F32, U, false, false, false>(a, grp, grid, block, s_lds, lds_a, ls);
 }
 
 // Work split: each wave takes U consecutive k-blocks per pass (U 16-byte
@@ -395,7 +451,7 @@ hipError_t launch_u(const GemmArgs& a, int waves) {
 // (at most 16) to cover K in one pass when it can.  W4A16_SKINNY_U (1, 2 or 4)
 // overrides U for tuning.
 template <int FMT, bool OUT_F32>
-hipError_t launch_fmt(const GemmArgs& a) {
+hipError_t launch_fmt(const GroupedArgs& a) {
   const int chunks = (int)(a.K >> 5);
   const int KB = (chunks + 3) >> 2;
   static const int u_env = [] {
@@ -419,7 +475,7 @@ hipError_t launch_fmt(const GemmArgs& a) {
 
 }  // namespace
 
-hipError_t launch_skinny(const GemmArgs& a) {
+hipError_t launch_skinny_grouped(const GroupedArgs& a) {
   switch (a.fmt * 2 + (a.out_f32 ? 1 : 0)) {
     case 0: return launch_fmt<kInt4, false>(a);
     case 1: return launch_fmt<kInt4, true>(a);
@@ -428,6 +484,23 @@ hipError_t launch_skinny(const GemmArgs& a) {
     case 4: return launch_fmt<kMxfp4, false>(a);
     default: return launch_fmt<kMxfp4, true>(a);
   }
+}
+
+hipError_t launch_skinny(const GemmArgs& a) {
+  GroupedArgs g = {};
+  g.fmt = a.fmt;
+  g.out_f32 = a.out_f32;
+  g.A = a.A;
+  g.count = 1;
+  g.packed[0] = a.packed;
+  g.scales[0] = a.scales;
+  g.zeros[0] = a.zeros;
+  g.C[0] = a.C;
+  g.N[0] = a.N;
+  g.M = a.M;
+  g.K = a.K;
+  g.stream = a.stream;
+  return launch_skinny_grouped(g);
 }
 
 }  // namespace w4a16

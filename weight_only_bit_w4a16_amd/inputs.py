@@ -119,6 +119,19 @@ def decoder_chain_shapes(layers: int = 28):
     return shapes
 
 
+def decoder_chain_groups(layers: int = 28):
+    """The decode chain's matrices grouped by shared input: per layer [q, k, v]
+    (the normalised layer input), [o], [gate, up] (the normalised attention
+    output), [down]; then [lm_head].  Lists of indices into
+    decoder_chain_shapes(layers)."""
+    groups = []
+    for layer in range(layers):
+        b = 7 * layer
+        groups += [[b, b + 1, b + 2], [b + 3], [b + 4, b + 5], [b + 6]]
+    groups.append([7 * layers])
+    return groups
+
+
 def chain_seed(seed: int, index: int) -> int:
     """Seed of the index-th matrix of the decode chain for chain seed `seed`."""
     return 1000 * seed + index
