@@ -47,11 +47,12 @@ struct SkinnyMember {
   const uint8_t* zeros;
   void* C;
   int N;
-  int tile_end;  // 16-column tiles of members 0 .. this one
+  int tile_end;  // column tiles (of `rows` columns) of members 0 .. this one
 };
 struct SkinnyGroup {
   SkinnyMember m[kMaxGroup];  // one member's fields are contiguous
   int count;
+  int rows;  // weight rows (output columns) per workgroup, 1 .. 16
 };
 
 // FULL: K % 128 == 0, so every chunk of a k-block below KB exists and the
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const int waves = blockDim.x >> 6;
   const int nl = lane & 15;  // weight row within the slice / A row supplied
   const int g = lane >> 4;   // 32-code chunk within the k-block
-  const int n0 = ((int)blockIdx.x - tile0) * 16;
+  const int n0 = ((int)blockIdx.x - tile0) * grp.rows;
   const int m0 = blockIdx.y * 16;
   const int n = n0 + nl;
   const int chunks = K >> 5;           // 32-code chunks per row
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
 
   // Buffer descriptors over exactly this workgroup's 16 weight rows and 16 A
   // rows: rows past N or M, and k past K, read as 0 (hardware range check).
-  const int rows = min(16, N - n0);
+  const int rows = min(grp.rows, N - n0);  // lanes of rows past it read zeros
   const int arows = min(16, M - m0);
   const uint32_t rowb = (uint32_t)(K >> 1);
   const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
     sum[2] += v[2];
     sum[3] += v[3];
   }
-  if (n >= N) return;
+  if (nl >= rows) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 4 * g + i;
@@ -402,6 +403,33 @@ hipError_t launch_s(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim
 
 template <int FMT, bool OUT_F32, int U>
 hipError_t launch_u(const GroupedArgs& a, int waves) {
+  static const int rows_env = [] {  // W4A16_SKINNY_ROWS=1..16 fixes the rows (tuning)
+    const char* e = getenv("W4A16_SKINNY_ROWS");
+    const int r = e ? atoi(e) : 0;
+    return r >= 1 && r <= 16 ? r : 0;
+  }();
+  // Rows per workgroup: 16 unless fewer make the workgroup count fill whole
+  // rounds of 256 (one per CU) better -- e.g. N = 3072 gives 192 workgroups
+  // of 16 rows but 256 of 12.  Lanes of the missing rows read zeros.
+  // A workgroup keeps >= 12 KB of weights (fewer rows would only add
+  // per-workgroup overhead).
+  int rows = 16;
+  if (!rows_env) {
+    const int64_t r_min = (12288 + a.K / 2 - 1) / (a.K / 2);
+    double best = -1.0;
+    for (int r = 16; r >= (r_min > 4 ? (int)(r_min < 16 ? r_min : 16) : 4); --r) {
+      int64_t wgs = 0;
+      for (int i = 0; i < a.count; ++i) wgs += (a.N[i] + r - 1) / r;
+      wgs *= (a.M + 15) / 16;
+      const double fill = (double)wgs / (double)(256 * ((wgs + 255) / 256));
+      if (fill > best + 0.02) {
+        best = fill;
+        rows = r;
+      }
+    }
+  } else {
+    rows = rows_env;
+  }
   SkinnyGroup grp = {};
   int tiles = 0;
   for (int i = 0; i < a.count; ++i) {
@@ -410,10 +438,11 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
     grp.m[i].zeros = a.zeros[i];
     grp.m[i].C = a.C[i];
     grp.m[i].N = (int)a.N[i];
-    tiles += (int)((a.N[i] + 15) / 16);
+    tiles += (int)((a.N[i] + rows - 1) / rows);
     grp.m[i].tile_end = tiles;
   }
   grp.count = a.count;
+  grp.rows = rows;
   dim3 grid((unsigned)tiles, (unsigned)((a.M + 15) / 16));
   // stage A in LDS when the workgroup's A slice fits its staging registers
   const int64_t arows = a.M < 16 ? a.M : 16;
