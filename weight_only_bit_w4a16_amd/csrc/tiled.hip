@@ -36,8 +36,6 @@
 //      slot h ^ ((r >> 2) & 1) (two lanes fetch one row's 32 contiguous bytes).
 //   scales: per row, E consecutive scale elements (one dword slot each) of a
 //      scale tile; element e sits in slot e ^ f_E(r) (see ScaleTile).
-#include <stdlib.h>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -376,12 +374,10 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   }
 }
 
-// the tile configuration in use: 256 x 256, waves 2 (M) x 4 (N), wave tile
-// 128 x 64 (W4A16_TILED_CFG=1 selects waves 4 x 2 with 64 x 128 wave tiles,
-// for tuning: it halves the A-fragment LDS reads but doubles the decode)
-using CfgA = TileCfg<2, 4, 8, 4>;
-using CfgB = TileCfg<4, 2, 4, 8>;
-using CfgC = TileCfg<2, 2, 8, 8>;
+// the tile configuration: 256 x 256, waves 2 (M) x 4 (N), wave tile 128 x 64
+// (64 x 128 wave tiles halve the A-fragment reads but double the decode, and
+// 128 x 128 wave tiles leave one wave per SIMD: both measured slower)
+using Cfg = TileCfg<2, 4, 8, 4>;
 
 template <int FMT, bool OUT_F32, class CFG>
 hipError_t launch_cfg(const GemmArgs& a) {
@@ -394,13 +390,7 @@ hipError_t launch_cfg(const GemmArgs& a) {
 
 template <int FMT, bool OUT_F32>
 hipError_t launch_fmt(const GemmArgs& a) {
-  static const int cfg_env = [] {
-    const char* e = getenv("W4A16_TILED_CFG");
-    return e ? atoi(e) : 0;
-  }();
-  if (cfg_env == 1) return launch_cfg<FMT, OUT_F32, CfgB>(a);
-  if (cfg_env == 2) return launch_cfg<FMT, OUT_F32, CfgC>(a);
-  return launch_cfg<FMT, OUT_F32, CfgA>(a);
+  return launch_cfg<FMT, OUT_F32, Cfg>(a);
 }
 
 }  // namespace
