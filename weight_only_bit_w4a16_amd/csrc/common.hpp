@@ -290,6 +290,15 @@ __device__ __forceinline__ u32x4_t int4x8_to_bf16_weights(uint32_t q, float s, f
   return r;
 }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for this wave's outstanding global loads (the fences carry
+// the local address space alone, so only lgkmcnt is drained).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---- MFMA ---------------------------------------------------------------------
 
 // D(16x16 fp32) += A(16x32 bf16) B(32x16 bf16).  Lane l supplies row l%16 of A

@@ -26,6 +26,10 @@
 //   * MXFP4: hardware e2m1 conversion scaled by 2^(E-127) (exact).
 #include <stdlib.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,19 +43,17 @@ constexpr int kSStage = 3;  // scale dwords per thread when the scales are stage
 constexpr int kZStage = 2;  // zero dwords per thread (int4)
 
 // The weight matrices of one launch: a single GEMM, or several sharing A and
-// K (member i: packed / scales / zeros / C, N[i] columns).  Workgroup x runs
-// 16 columns of the member whose cumulative tile range holds x.
+// K (member i: packed / scales / zeros / C, N[i] columns).  Workgroup
+// (x, y, z) runs columns x * rows .. of member z (none if past its N).
 struct SkinnyMember {
   const uint8_t* packed;
   const void* scales;
   const uint8_t* zeros;
   void* C;
   int N;
-  int tile_end;  // column tiles (of `rows` columns) of members 0 .. this one
 };
 struct SkinnyGroup {
   SkinnyMember m[kMaxGroup];  // one member's fields are contiguous
-  int count;
   int rows;  // weight rows (output columns) per workgroup, 1 .. 16
 };
 
@@ -63,34 +65,20 @@ struct SkinnyGroup {
 // A_DMA (with !A_LDS): each wave copies the A rows of its own k-blocks
 // straight into a private LDS region (asynchronous global -> LDS copies of
 // contiguous 256-byte row pieces) instead of per-lane A loads.
-// GROUPED: more than one member (a single GEMM reads member 0 only).
+// GROUPED: more than one member, blockIdx.z (a single GEMM reads member 0).
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* __restrict__ A,
                                                                 SkinnyGroup grp, int M, int K) {
-  // the group member whose columns this workgroup computes (uniform; picked
-  // by selects, not by indexing the argument arrays)
-  int gi = 0;
-  if constexpr (GROUPED) {
-#pragma unroll
-    for (int i = 1; i < kMaxGroup; ++i)
-      gi = (i < grp.count && (int)blockIdx.x >= grp.m[i - 1].tile_end) ? i : gi;
-  }
-  const uint8_t* packed = grp.m[0].packed;
-  const void* scales = grp.m[0].scales;
-  const uint8_t* zeros = grp.m[0].zeros;
-  void* C = grp.m[0].C;
-  int N = grp.m[0].N, tile0 = 0;
-#pragma unroll
-  for (int i = 1; i < (GROUPED ? kMaxGroup : 1); ++i) {
-    if (gi == i) {
-      packed = grp.m[i].packed;
-      scales = grp.m[i].scales;
-      zeros = grp.m[i].zeros;
-      C = grp.m[i].C;
-      N = grp.m[i].N;
-      tile0 = grp.m[i - 1].tile_end;
-    }
-  }
+  // the group member whose columns this workgroup computes: its fields come
+  // in one scalar load round trip at a workgroup-uniform offset
+  const SkinnyMember& mem = grp.m[GROUPED ? (int)blockIdx.z : 0];
+  const uint8_t* packed = mem.packed;
+  const void* scales = mem.scales;
+  const uint8_t* zeros = mem.zeros;
+  void* C = mem.C;
+  const int N = mem.N;
+  const int n0 = (int)blockIdx.x * grp.rows;
+  if (GROUPED && n0 >= N) return;  // past this member's columns (whole workgroup)
   // LDS copy of A: arows rows of K bf16, then one row of zeros that lanes
   // past M (and chunks past K) read instead of branching
   extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
@@ -100,7 +88,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const int waves = blockDim.x >> 6;
   const int nl = lane & 15;  // weight row within the slice / A row supplied
   const int g = lane >> 4;   // 32-code chunk within the k-block
-  const int n0 = ((int)blockIdx.x - tile0) * grp.rows;
   const int m0 = blockIdx.y * 16;
   const int n = n0 + nl;
   const int chunks = K >> 5;           // 32-code chunks per row
@@ -134,6 +121,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const uint32_t a_wave = lds_address(a_lds) + a_dma_off +
                           (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (uint32_t)(U * 4096);
   uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
+  // staging loads are issued only by waves that hold some in-range slot
+  // (a wave whose first slot is past the block skips the instruction)
+  const uint32_t wave_slot0 = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64u;
   uint32_t sst[kSStage], zst[kZStage];
   if constexpr (S_LDS) {
     auto window = [&](const uint8_t* start, uint32_t bytes, uint32_t& delta, uint32_t& words) {
@@ -147,14 +137,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < kSStage; ++i) {
       const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
-      sst[i] = buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB);
+      sst[i] = wave_slot0 + i * blockDim.x < s_words ? buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB) : 0u;
     }
     if constexpr (FMT == kInt4) {
       const rsrc_t zs = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), z_delta, z_words);
 #pragma unroll
       for (int i = 0; i < kZStage; ++i) {
         const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
-        zst[i] = buf_load_b32(zs, w < z_words ? w * 4u : kBufferOOB);
+        zst[i] = wave_slot0 + i * blockDim.x < z_words ? buf_load_b32(zs, w < z_words ? w * 4u : kBufferOOB) : 0u;
       }
     }
   }
@@ -184,7 +174,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < kAStage; ++i) {
       const int ch = tid + i * (int)blockDim.x;
-      astage[i] = buf_load_b128(ar, ch < a16 ? (uint32_t)ch * 16u : kBufferOOB);
+      astage[i] = (int)(wave_slot0 + i * blockDim.x) < a16
+                      ? buf_load_b128(ar, ch < a16 ? (uint32_t)ch * 16u : kBufferOOB)
+                      : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -381,9 +373,246 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   }
 }
 
+// ---- streaming variant: one workgroup walks many column tiles -------------
+//
+// For launches of several rounds of 16-column tiles.  A workgroup stages A in
+// LDS once and then computes tiles t = blockIdx.x, blockIdx.x + gridDim.x,
+// ... with the same split of K over its waves as the one-tile kernel (so both
+// give the same bits).  Loads run two tiles ahead: while tile s is computed,
+// the weights of tiles s+1 and s+2 are in flight (three register sets) and
+// the scales of tile s+1, loaded one step earlier, go to LDS.  Each step has
+// one barrier, which orders LDS only and never waits for loads in flight.
+// Every load is issued unconditionally (tiles past the last get empty
+// descriptors), so the compiler's wait counts for one tile never include the
+// loads of later tiles.
+// Conditions, checked by the launcher: K % 128 == 0; each wave covers its U
+// k-blocks of a tile in one pass (waves * U >= K / 128); the M <= 16 rows of
+// A fit the staging registers; NS scale dwords per lane (and one zero dword,
+// int4) cover a tile's scale window.
+template <int FMT, bool OUT_F32, int U, int NS>
+__global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uint16_t* __restrict__ A,
+                                                                       SkinnyGroup grp, int M, int K,
+                                                                       int tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int waves = blockDim.x >> 6;
+  const int nl = lane & 15;  // weight row within the tile / A row supplied
+  const int g = lane >> 4;   // 32-code chunk within the k-block
+  const int KB = K >> 7;
+  constexpr int G = FormatTraits<FMT>::kGroup;
+  constexpr int SB = (FMT == kInt4) ? 2 : 1;
+  const int groups = K / G;
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const uint32_t wave_slot0 = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64u;
+  const int kw = __builtin_amdgcn_readfirstlane(wave) * U;  // this wave's first k-block
+
+  // LDS: A (M rows, then a row of zeros), three scale/zero buffers, three
+  // reduction buffers of [waves][64] f32x4
+  const uint32_t s_cap = ((16u * (uint32_t)groups * SB + 6u) + 15u) & ~15u;
+  const uint32_t z_cap = FMT == kInt4 ? ((16u * (uint32_t)groups + 6u + 15u) & ~15u) : 0u;
+  const uint32_t buf0 = ((uint32_t)(M + 1) * (uint32_t)K * 2u + 15u) & ~15u;
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + buf0 + 3u * (s_cap + z_cap));
+
+  // A loads first (vmcnt retires in issue order)
+  const rsrc_t ar = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+  const int a16 = M * K / 8;  // 16-byte chunks of A
+  u32x4_t astage[kAStage];
+#pragma unroll
+  for (int i = 0; i < kAStage; ++i) {
+    const int ch = tid + i * (int)blockDim.x;
+    astage[i] = (int)(wave_slot0 + i * blockDim.x) < a16
+                    ? buf_load_b128(ar, ch < a16 ? (uint32_t)ch * 16u : kBufferOOB)
+                    : u32x4_t{0, 0, 0, 0};
+  }
+
+  // a tile: its place and its weights (in flight or landed)
+  struct Tile {
+    int t, n0, rows, N;
+    void* C;
+    const uint8_t* scales;
+    const uint8_t* zeros;
+    u32x4_t q[U];
+  };
+  // the scale (and zero) window of one tile, in flight in registers
+  struct Scales {
+    uint32_t delta, zdelta, words, zwords;
+    uint32_t s[NS], z;
+  };
+  // t >= tiles: the same loads over empty ranges (they return zeros)
+  auto issue = [&](Tile& T, Scales& S, int t) {
+    const bool live = t < tiles;
+    const uint8_t* packed = grp.m[0].packed;
+    T.scales = reinterpret_cast<const uint8_t*>(grp.m[0].scales);
+    T.zeros = grp.m[0].zeros;
+    T.C = grp.m[0].C;
+    T.N = grp.m[0].N;
+    T.t = t;
+    T.n0 = t * 16;
+    T.rows = live ? min(16, T.N - T.n0) : 0;
+    // the tile's scale (and zero) rows are one contiguous block, read as
+    // dwords from the 4-byte aligned address at or below its start
+    auto window = [&](const uint8_t* start, uint32_t bytes, uint32_t& delta, uint32_t& words) {
+      const uintptr_t al = reinterpret_cast<uintptr_t>(start) & ~(uintptr_t)3;
+      delta = (uint32_t)(reinterpret_cast<uintptr_t>(start) - al);
+      words = bytes ? (delta + bytes + 3u) / 4u : 0u;  // may read <= 3 bytes past the block (same dword)
+      return make_rsrc(reinterpret_cast<const void*>(al), words * 4u);
+    };
+    const rsrc_t ss = window(T.scales + (int64_t)T.n0 * groups * SB, (uint32_t)(T.rows * groups * SB),
+                             S.delta, S.words);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+      S.s[i] = buf_load_b32(ss, w < S.words ? w * 4u : kBufferOOB);
+    }
+    if constexpr (FMT == kInt4) {
+      const rsrc_t zs = window(T.zeros + (int64_t)T.n0 * groups, (uint32_t)(T.rows * groups), S.zdelta, S.zwords);
+      S.z = buf_load_b32(zs, (uint32_t)tid < S.zwords ? (uint32_t)tid * 4u : kBufferOOB);
+    }
+    // weights: rows past the tile's last read as zeros (descriptor range)
+    const rsrc_t wr = make_rsrc(packed + (int64_t)T.n0 * rowb, (uint32_t)T.rows * rowb);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kw + u;
+      T.q[u] = buf_load_b128(wr, kb < KB ? (uint32_t)nl * rowb + (uint32_t)(kb * 4 + g) * 16u : kBufferOOB);
+    }
+    // keep the batch in flight: no load may sink towards its use
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // scale buffer b: the window's dwords, and where its first byte sits
+  uint32_t sdelta[3], zdelta[3];
+  auto store_scales = [&](const Scales& S, int b) {
+    uint32_t* sbuf = reinterpret_cast<uint32_t*>(lds + buf0 + (uint32_t)b * (s_cap + z_cap));
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+      if (w < S.words) sbuf[w] = S.s[i];
+    }
+    if constexpr (FMT == kInt4) {
+      uint32_t* zbuf = reinterpret_cast<uint32_t*>(lds + buf0 + (uint32_t)b * (s_cap + z_cap) + s_cap);
+      if ((uint32_t)tid < S.zwords) zbuf[tid] = S.z;
+    }
+    sdelta[b] = S.delta;
+    zdelta[b] = S.zdelta;
+  };
+  const int arow = nl < M ? nl : M;  // row M of the LDS copy is zeros
+  auto compute = [&](const Tile& T, int b) {
+    const uint8_t* sb = lds + buf0 + (uint32_t)b * (s_cap + z_cap) + sdelta[b];
+    const uint8_t* zb = lds + buf0 + (uint32_t)b * (s_cap + z_cap) + s_cap + zdelta[b];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kw + u;
+      if (kb >= KB) break;  // wave-uniform
+      const int c = kb * 4 + g;
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(lds + ((size_t)arow * K + (size_t)c * 32) * 2);
+      u32x4_t a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = src[j];
+      if constexpr (FMT == kInt4) {
+        // codes exact (A is stored in the decoder's k order); the zero point
+        // goes through a second accumulator with the same rounding sequence,
+        // so a k-block whose codes all equal it cancels to exactly 0
+        const int gi = nl * groups + kb;
+        const float s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
+        const u32x4_t nz = int4_neg_zero(zb[gi]);
+        f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dp = mfma16x16x32(a[j], int4x8_to_bf16_exact(T.q[u][j]), dp);
+          dn = mfma16x16x32(a[j], nz, dn);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(s, dp[i] + dn[i], acc[i]);
+      } else if constexpr (FMT == kNvfp4) {
+        const uint32_t sraw = *reinterpret_cast<const uint16_t*>(sb + nl * groups + 2 * c);
+        const float s0 = e4m3_magnitude(sraw & 0xFFu);
+        const float s1 = e4m3_magnitude(sraw >> 8);
+        acc = mfma16x16x32(a[0], fp4x8_to_bf16_fscale(T.q[u][0], s0), acc);
+        acc = mfma16x16x32(a[1], fp4x8_to_bf16_fscale(T.q[u][1], s0), acc);
+        acc = mfma16x16x32(a[2], fp4x8_to_bf16_fscale(T.q[u][2], s1), acc);
+        acc = mfma16x16x32(a[3], fp4x8_to_bf16_fscale(T.q[u][3], s1), acc);
+      } else {
+        const float es = e8m0_as_exponent_scale(sb[nl * groups + c]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[j], fp4x8_to_bf16_escale(T.q[u][j], es), acc);
+      }
+    }
+    return acc;
+  };
+  // split-K sum over the waves (wave 0, in wave order) and the tile's stores
+  auto reduce_store = [&](const Tile& T, int b) {
+    const f32x4_t* r = red + b * waves * 64 + lane;
+    f32x4_t sum = r[0];
+    for (int w = 1; w < waves; ++w) {
+      const f32x4_t v = r[w * 64];
+      sum[0] += v[0];
+      sum[1] += v[1];
+      sum[2] += v[2];
+      sum[3] += v[3];
+    }
+    if (nl >= T.rows) return;
+    const int n = T.n0 + nl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < M) {
+        if constexpr (OUT_F32) {
+          reinterpret_cast<float*>(T.C)[(int64_t)m * T.N + n] = sum[i];
+        } else {
+          reinterpret_cast<__bf16*>(T.C)[(int64_t)m * T.N + n] = (__bf16)sum[i];
+        }
+      }
+    }
+  };
+
+  // prologue: tiles 0 and 1 of this workgroup in flight, A and tile 0's
+  // scales in LDS
+  Tile T0, T1, T2;
+  Scales S;
+  const int G0 = (int)gridDim.x;
+  issue(T0, S, (int)blockIdx.x);
+#pragma unroll
+  for (int i = 0; i < kAStage; ++i) {
+    const int ch = tid + i * (int)blockDim.x;
+    // int4 codes decode in the k order (0,2,4,6,1,3,5,7) per 8: A follows it
+    const u32x4_t v = FMT == kInt4 ? bf16x8_even_odd(astage[i]) : astage[i];
+    if (ch < a16) reinterpret_cast<u32x4_t*>(lds)[ch] = v;
+  }
+  for (int ch = a16 + tid; ch < a16 + K / 8; ch += blockDim.x)
+    reinterpret_cast<u32x4_t*>(lds)[ch] = u32x4_t{0, 0, 0, 0};
+  store_scales(S, 0);
+  issue(T1, S, (int)blockIdx.x + G0);
+
+  // step s (buffers s % 3): tile s+1's scales (loaded one step ago) to LDS,
+  // tile s+2's loads issued, tile s computed, barrier, tile s reduced
+  auto step = [&](Tile& cur, Tile& far, int b) {
+    store_scales(S, (b + 1) % 3);
+    issue(far, S, cur.t + 2 * G0);
+    red[(b * waves + wave) * 64 + lane] = compute(cur, b);
+    lds_barrier();
+    if (wave == 0) reduce_store(cur, b);
+  };
+  lds_barrier();
+  // a loop with its one exit at the bottom (an exit between steps would
+  // reach the loop head, in the compiler's view, with loads pending in
+  // registers it reuses, and cost a full wait)
+  const int mine = (tiles - (int)blockIdx.x + G0 - 1) / G0;
+  int i = 0;
+  for (; i + 2 < mine; i += 3) {
+    step(T0, T2, 0);
+    step(T1, T0, 1);
+    step(T2, T1, 2);
+  }
+  if (i < mine) step(T0, T2, 0);
+  if (i + 1 < mine) step(T1, T0, 1);
+}
+
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, bool S_LDS>
 hipError_t launch_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim3 block, unsigned lds) {
-  if (grp.count > 1)
+  if (a.count > 1)
     hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, true>), grid, block,
                        lds, a.stream, a.A, grp, (int)a.M, (int)a.K);
   else
@@ -431,19 +660,19 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
     rows = rows_env;
   }
   SkinnyGroup grp = {};
-  int tiles = 0;
+  int64_t max_n = 0;
   for (int i = 0; i < a.count; ++i) {
     grp.m[i].packed = a.packed[i];
     grp.m[i].scales = a.scales[i];
     grp.m[i].zeros = a.zeros[i];
     grp.m[i].C = a.C[i];
     grp.m[i].N = (int)a.N[i];
-    tiles += (int)((a.N[i] + rows - 1) / rows);
-    grp.m[i].tile_end = tiles;
+    max_n = a.N[i] > max_n ? a.N[i] : max_n;
   }
-  grp.count = a.count;
   grp.rows = rows;
-  dim3 grid((unsigned)tiles, (unsigned)((a.M + 15) / 16));
+  // members along z; a member with fewer tiles than the widest has
+  // workgroups that exit at once
+  dim3 grid((unsigned)((max_n + rows - 1) / rows), (unsigned)((a.M + 15) / 16), (unsigned)a.count);
   // stage A in LDS when the workgroup's A slice fits its staging registers
   const int64_t arows = a.M < 16 ? a.M : 16;
   const int64_t a_bytes = arows * a.K * 2;
@@ -475,20 +704,125 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   return launch_s<FMT, OUT_F32, U, false, false, false>(a, grp, grid, block, s_lds, lds_a, ls);
 }
 
+// W4A16_SKINNY_U (1, 2 or 4) overrides the k-blocks per wave (tuning)
+int skinny_u_env() {
+  static const int u = [] {
+    const char* e = getenv("W4A16_SKINNY_U");
+    const int v = e ? atoi(e) : 0;
+    return v == 1 || v == 2 || v == 4 ? v : 0;
+  }();
+  return u;
+}
+
+// k-blocks of 128 per wave: 2 while K fits 16 waves that way, else 4.  The
+// split sets the summation order, so every kernel for few rows uses it.
+int skinny_split_u(int KB) {
+  if (skinny_u_env()) return skinny_u_env();
+  return (KB + 1) / 2 <= kMaxWaves ? 2 : 4;
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// resident workgroups per compute unit of a kernel at a block size and
+// dynamic LDS size (cached; occupancy does not depend on the device here)
+int resident_per_cu(const void* kernel, int threads, unsigned lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, unsigned>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(kernel, threads, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1) n = 1;
+  cache.emplace(key, n);
+  return n;
+}
+
+template <int FMT, bool OUT_F32, int U, int NS>
+hipError_t launch_stream_k(const GroupedArgs& a, const SkinnyGroup& grp, int tiles, int waves, unsigned lds) {
+  const void* kern = reinterpret_cast<const void*>(&skinny_stream_kernel<FMT, OUT_F32, U, NS>);
+  const int resident = resident_per_cu(kern, 64 * waves, lds) * device_cus();
+  const dim3 grid((unsigned)(tiles < resident ? tiles : resident));
+  const dim3 block(64 * waves);
+  hipLaunchKernelGGL((skinny_stream_kernel<FMT, OUT_F32, U, NS>), grid, block, lds, a.stream, a.A, grp, (int)a.M,
+                     (int)a.K, tiles);
+  return hipGetLastError();
+}
+
+// The streaming kernel when its conditions hold and the launch (one weight
+// matrix) has at least `min_tiles` tiles of 16 columns; returns false
+// (nothing launched) otherwise.
+template <int FMT, bool OUT_F32>
+bool try_stream(const GroupedArgs& a, int64_t min_tiles, hipError_t& err) {
+  if (a.count != 1 || a.K % 128 != 0 || a.M > 16) return false;
+  const int KB = (int)(a.K / 128);
+  // the one-tile kernel's split of K (a column's bits never depend on N or
+  // on the grouping)
+  const int U = skinny_split_u(KB);
+  const int waves = (KB + U - 1) / U;
+  if (waves > kMaxWaves) return false;
+  const int64_t threads = 64 * waves;
+  const int64_t a16 = a.M * a.K / 8;
+  if (a16 > kAStage * threads || a.M * a.K * 2 > 64 * 1024) return false;
+  constexpr int SB = FMT == kInt4 ? 2 : 1;
+  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t s_words = (16 * groups * SB + 6) / 4, z_words = (16 * groups + 6) / 4;
+  const int NS = s_words <= threads ? 1 : (s_words <= 2 * threads ? 2 : 0);
+  if (NS == 0 || (FMT == kInt4 && z_words > threads)) return false;
+  const int64_t tiles = (a.N[0] + 15) / 16;
+  if (tiles < min_tiles || tiles < 1) return false;
+  SkinnyGroup grp = {};
+  grp.m[0].packed = a.packed[0];
+  grp.m[0].scales = a.scales[0];
+  grp.m[0].zeros = a.zeros[0];
+  grp.m[0].C = a.C[0];
+  grp.m[0].N = (int)a.N[0];
+  grp.rows = 16;
+  const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
+  const int64_t z_cap = FMT == kInt4 ? (16 * groups + 6 + 15) & ~15 : 0;
+  const unsigned lds = (unsigned)((((a.M + 1) * a.K * 2 + 15) & ~15) + 3 * (s_cap + z_cap) + 3 * threads * 16);
+  if (U == 4)
+    err = NS == 1 ? launch_stream_k<FMT, OUT_F32, 4, 1>(a, grp, (int)tiles, waves, lds)
+                  : launch_stream_k<FMT, OUT_F32, 4, 2>(a, grp, (int)tiles, waves, lds);
+  else if (U == 2)
+    err = NS == 1 ? launch_stream_k<FMT, OUT_F32, 2, 1>(a, grp, (int)tiles, waves, lds)
+                  : launch_stream_k<FMT, OUT_F32, 2, 2>(a, grp, (int)tiles, waves, lds);
+  else
+    err = NS == 1 ? launch_stream_k<FMT, OUT_F32, 1, 1>(a, grp, (int)tiles, waves, lds)
+                  : launch_stream_k<FMT, OUT_F32, 1, 2>(a, grp, (int)tiles, waves, lds);
+  return true;
+}
+
 // Work split: each wave takes U consecutive k-blocks per pass (U 16-byte
 // weight loads in flight per lane), and the workgroup has enough waves
 // (at most 16) to cover K in one pass when it can.  W4A16_SKINNY_U (1, 2 or 4)
 // overrides U for tuning.
 template <int FMT, bool OUT_F32>
 hipError_t launch_fmt(const GroupedArgs& a) {
+  // W4A16_SKINNY_STREAM: 0 never, 1 whenever possible (tuning); default from
+  // 1024 tiles of 16 columns on
+  static const int stream_env = [] {
+    const char* e = getenv("W4A16_SKINNY_STREAM");
+    return e ? atoi(e) : -1;
+  }();
+  if (stream_env != 0) {
+    hipError_t err = hipSuccess;
+    if (try_stream<FMT, OUT_F32>(a, stream_env == 1 ? 1 : 1024, err)) return err;
+  }
   const int chunks = (int)(a.K >> 5);
   const int KB = (chunks + 3) >> 2;
-  static const int u_env = [] {
-    const char* e = getenv("W4A16_SKINNY_U");
-    return e ? atoi(e) : 0;
-  }();
-  int U = u_env == 1 || u_env == 2 || u_env == 4 ? u_env : 4;
-  if (!u_env && (KB + 1) / 2 <= kMaxWaves) U = 2;
+  int U = skinny_split_u(KB);
   int waves = (KB + U - 1) / U;
   if (waves > kMaxWaves) waves = kMaxWaves;
   if (waves < 1) waves = 1;
@@ -496,7 +830,7 @@ hipError_t launch_fmt(const GroupedArgs& a) {
   // U k-blocks (4 KB each): keep those within 128 KB
   const int64_t arows = a.M < 16 ? a.M : 16;
   const bool a_big = arows * a.K * 2 > (int64_t)kAStage * 16 * 64 * waves || arows * a.K * 2 > 64 * 1024;
-  if (!u_env && a_big && waves * U > 32) U = 32 / waves > 0 ? 32 / waves : 1;
+  if (!skinny_u_env() && a_big && waves * U > 32) U = 32 / waves > 0 ? 32 / waves : 1;
   if (U == 1) return launch_u<FMT, OUT_F32, 1>(a, waves);
   if (U == 2) return launch_u<FMT, OUT_F32, 2>(a, waves);
   return launch_u<FMT, OUT_F32, 4>(a, waves);
