@@ -322,9 +322,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
 
   int kbase = wave * U;
   issue(kbase);
+  // LDS-only barriers: each wave's weights stay in flight, and its first
+  // k-block's arithmetic waits for that k-block's load alone
   if constexpr (S_LDS && !A_LDS) {
     store_scales();
-    __syncthreads();
+    lds_barrier();
   }
   if constexpr (A_LDS) {
     store_scales();
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
     }
     for (int ch = a16 + tid; ch < a16 + K / 8; ch += blockDim.x)
       reinterpret_cast<u32x4_t*>(a_lds)[ch] = u32x4_t{0, 0, 0, 0};
-    __syncthreads();
+    lds_barrier();
   }
   compute(kbase);
   for (kbase += waves * U; kbase < KB; kbase += waves * U) {
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   // ---- split-K reduction across the waves, through LDS ----------------------
   __shared__ f32x4_t red[kMaxWaves][64];
   red[wave][lane] = acc;
-  __syncthreads();
+  lds_barrier();
   if (wave != 0) return;
   f32x4_t sum = red[0][lane];
   for (int w = 1; w < waves; ++w) {
