@@ -70,6 +70,10 @@ def _load():
     lib.orc_gemm.restype = I
     lib.orc_gemm_at.argtypes = [I, P, P, P, P, I64, I64, I64, I64, P, P, P, P]
     lib.orc_gemm_at.restype = I
+    lib.orc_activation.argtypes = [I, ctypes.c_double]
+    lib.orc_activation.restype = ctypes.c_double
+    lib.orc_epilogue.argtypes = [I64, I64, P, ctypes.c_double, P, I, ctypes.c_double, P]
+    lib.orc_epilogue.restype = I
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = I
     _lib = lib
@@ -169,6 +173,35 @@ def gemm_at(fmt: int, A_bits, packed, scales, zeros, M: int, N: int, K: int,
     return C, S
 
 
+# ---- fused epilogue ----------------------------------------------------------
+
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
+# Lipschitz constants of the activations (max |act'|): SiLU's derivative peaks
+# at 1.0998 near x = 2.40, the tanh-form GELU's at 1.1289 near x = 1.50
+ACT_LIPSCHITZ = {ACT_NONE: 1.0, ACT_RELU: 1.0, ACT_SILU: 1.1, ACT_GELU_TANH: 1.13}
+
+
+def activation(act: int, x: float) -> float:
+    return float(_load().orc_activation(act, float(x)))
+
+
+def epilogue(C, alpha: float = 1.0, bias=None, act: int = ACT_NONE, beta: float = 0.0, R=None):
+    """y = act(alpha*C + bias[n]) + beta*R, in fp64 (C, R: float arrays (M, N);
+    bias: bf16 bits (N)).  Returns a new array."""
+    y = np.array(C, dtype=np.float64, order="C", copy=True)
+    M, N = y.shape
+    b = None if bias is None else _c(bias, np.uint16)
+    r = None if R is None else _c(np.asarray(R, dtype=np.float64), np.float64)
+    if b is not None and b.shape != (N,):
+        raise ValueError("oracle epilogue: bias must have N elements")
+    if r is not None and r.shape != (M, N):
+        raise ValueError("oracle epilogue: R must be (M, N)")
+    rc = _load().orc_epilogue(M, N, _ptr(y), float(alpha), _ptr(b), int(act), float(beta), _ptr(r))
+    if rc != 0:
+        raise ValueError("oracle epilogue: bad activation")
+    return y
+
+
 def num_threads() -> int:
     return int(_load().orc_num_threads())
 
@@ -187,6 +220,35 @@ def gate_bound(C_ref, S, bf16_out: bool):
     if bf16_out:
         b = b + BF16_OUT_REL * np.abs(np.asarray(C_ref))
     return b
+
+
+def epilogue_gate_bound(C_ref, S, alpha: float, bias, act: int, beta: float, R, Y_ref,
+                        bf16_out: bool):
+    """Per-element allowed |Y_gpu - Y_ref| for y = act(alpha*c + bias) + beta*R:
+    the GEMM bound carried through alpha and the activation's Lipschitz
+    constant, fp32 rounding of the epilogue's operations (2^-20 of the
+    magnitudes involved), and one bf16 rounding of y when stored as bf16."""
+    C_ref = np.asarray(C_ref, dtype=np.float64)
+    pre = abs(alpha) * np.abs(C_ref)
+    if bias is not None:
+        pre = pre + np.abs(bf16_values(np.asarray(bias, dtype=np.uint16)))[None, :]
+    post = np.abs(np.asarray(Y_ref, dtype=np.float64))
+    if R is not None and beta != 0.0:
+        post = post + abs(beta) * np.abs(np.asarray(R, dtype=np.float64))
+    b = (ACT_LIPSCHITZ[act] * abs(alpha) * (GATE_REL * np.asarray(S) + GATE_ABS)
+         + 2.0 ** -20 * (pre + post) + GATE_ABS)
+    if bf16_out:
+        b = b + BF16_OUT_REL * np.abs(np.asarray(Y_ref))
+    return b
+
+
+def epilogue_gate_ratio(Y_test, C_ref, S, alpha, bias, act, beta, R, Y_ref, bf16_out: bool):
+    """max |Y_test - Y_ref| / epilogue bound (<= 1 passes); NaN fails."""
+    err = np.abs(np.asarray(Y_test, dtype=np.float64) - np.asarray(Y_ref))
+    r = err / epilogue_gate_bound(C_ref, S, alpha, bias, act, beta, R, Y_ref, bf16_out)
+    if not np.all(np.isfinite(r)):
+        return float("inf")
+    return float(r.max()) if r.size else 0.0
 
 
 def gate_ratio(C_test, C_ref, S, bf16_out: bool):

@@ -257,6 +257,55 @@ int orc_gemm_at(int fmt, const uint16_t* A, const uint8_t* packed,
   return err;
 }
 
+/* ---- fused epilogue ----------------------------------------------------------
+ *
+ *     y[m, n] = act(alpha * c[m, n] + bias[n]) + beta * R[m, n]
+ *
+ * on the exact (binary64) GEMM value c.  Sources: [TX] "gemm.rst", the
+ * alpha / beta parameters -- D = alpha * A@B + beta * C, and C is not read
+ * when beta is 0 (D starts from C only when beta is 1, else from 0); [MJ]
+ * "Matmul2dFp4", the optional fused per-element (row, col) epilogue; [KB]
+ * "Precision" -- residual adds in fp32 or better.  The pages name no
+ * activation; the ones offered are ReLU, SiLU (x times the logistic
+ * function) and GELU in its tanh form.  Reading: bias is added before the
+ * activation, the residual after it (a transformer's residual stream); R is
+ * read only when present and beta != 0.
+ */
+#define ORC_ACT_NONE 0
+#define ORC_ACT_RELU 1
+#define ORC_ACT_SILU 2
+#define ORC_ACT_GELU_TANH 3
+
+double orc_activation(int act, double x) {
+  switch (act) {
+    case ORC_ACT_NONE: return x;
+    case ORC_ACT_RELU: return x > 0.0 ? x : 0.0;
+    case ORC_ACT_SILU: return x / (1.0 + exp(-x));
+    case ORC_ACT_GELU_TANH: {
+      const double u = sqrt(2.0 / 3.14159265358979323846) * (x + 0.044715 * x * x * x);
+      return 0.5 * x * (1.0 + tanh(u));
+    }
+    default: return NAN;
+  }
+}
+
+/* In place on y (M x N, row-major): y holds c on entry.  bias: bf16 bits (N)
+ * or NULL; R: binary64 (M x N) or NULL.  Returns 0, or -1 on a bad
+ * activation code. */
+int orc_epilogue(int64_t M, int64_t N, double* y, double alpha, const uint16_t* bias,
+                 int act, double beta, const double* R) {
+  if (act < ORC_ACT_NONE || act > ORC_ACT_GELU_TANH) return -1;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double v = alpha * y[m * N + n];
+      if (bias) v += orc_bf16_value(bias[n]);
+      v = orc_activation(act, v);
+      if (R && beta != 0.0) v += beta * R[m * N + n];
+      y[m * N + n] = v;
+    }
+  return 0;
+}
+
 /* Number of threads the parallel loops above use (1 without OpenMP). */
 int orc_num_threads(void) {
 #ifdef _OPENMP
