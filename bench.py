@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--shape", default=None,
                     help="custom single-GEMM workload 'format,M,N,K' (format 0 int4, 1 nvfp4, "
                          "2 mxfp4; bf16 out) instead of --workload")
+    ap.add_argument("--epilogue", default=None, choices=["none", "relu", "silu", "gelu_tanh"],
+                    help="single-GEMM workloads: fuse a bf16 bias, a residual (beta = 1) and this "
+                         "activation into the GEMM (w4a16_gemm_ex); their bytes count as traffic")
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight copies to rotate over (0: enough for >= 1 GiB)")
     ap.add_argument("--m4096-steps", type=int, default=300)
@@ -215,12 +218,18 @@ def main():
         copies = args.copies or max(1, min(128, math.ceil((1 << 30) / tbytes)))
         odt = torch.float32 if out == "f32" else torch.bfloat16
         C = torch.empty((M, N), dtype=odt, device=dev)
+        epi = {}
+        if args.epilogue:
+            g = torch.Generator(device="cpu").manual_seed(1)
+            epi = dict(bias=torch.randn(N, generator=g).to(dev, torch.bfloat16),
+                       residual=torch.randn((M, N), generator=g).to(dev, odt),
+                       alpha=1.0, beta=1.0, activation=args.epilogue)
         calls = []
         for r in range(copies):
             pr = p if r == 0 else p.clone()
             sr = s if r == 0 else s.clone()
             zr = z if (r == 0 or z is None) else z.clone()
-            calls.append([w4.PreparedGemm(fmt, A, pr, sr, zr, C, path=args.path)])
+            calls.append([w4.PreparedGemm(fmt, A, pr, sr, zr, C, path=args.path, **epi)])
         total = timed(calls, steps, warmup)
         kernel = calls[0][0].kernel
         del calls, C
@@ -273,11 +282,16 @@ def main():
         fmt, M, N, K, out = WORKLOADS[args.workload]
         case, total_ms, copies, kernel = measure_single(fmt, M, N, K, out, args.steps, args.warmup)
         wbytes, tbytes = algorithmic_bytes(fmt, M, N, K, out)
+        if args.epilogue:  # + bias (bf16) + residual (C's dtype)
+            tbytes += N * 2 + M * N * (4 if out == "f32" else 2)
         ms = total_ms / args.steps
         launches_per_step = 1
         bytes_per_launch = tbytes
         config = {"workload": args.workload, "format": w4.FORMAT_NAMES[fmt], "M": M, "N": N, "K": K,
                   "out": out, "weight_copies": copies, "kernel": kernel}
+        if args.epilogue:
+            config["epilogue"] = {"bias": "bf16", "residual": out, "beta": 1.0,
+                                  "activation": args.epilogue}
         workload = args.workload
         weight_bytes = wbytes
         if M > 16:
@@ -293,12 +307,12 @@ def main():
         ach = 2.0 * M * N * K / (mean_launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profile(kernel, workload)}
+                "traffic": None if args.epilogue else traffic_from_profile(kernel, workload)}
     else:
         ach = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(kernel, workload)}
+                "traffic": None if args.epilogue else traffic_from_profile(kernel, workload)}
     roof["kernel"] = kernel
     roof["mean_launch_us"] = round(mean_launch_ms * 1e3, 3)
     roof["bytes_per_launch"] = int(bytes_per_launch) if unit == "GB/s" else None

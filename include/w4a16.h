@@ -86,6 +86,9 @@ extern "C" {
                                  non-NULL for an fp4 format                 */
 #define W4A16_ERR_ALIGN (-4)  /* a pointer violates its alignment           */
 #define W4A16_ERR_HIP (-5)    /* the HIP runtime rejected a launch          */
+#define W4A16_ERR_EPILOGUE (-6) /* unknown activation, nonzero reserved field,
+                                   or a residual that overlaps C without
+                                   being C                                  */
 
 /* C = A . dequant(packed, scales, zeros)^T, accumulated in fp32.
  * format = W4A16_INT4_G128 | W4A16_NVFP4 | W4A16_MXFP4, optionally OR-ed with
@@ -95,6 +98,41 @@ extern "C" {
 int w4a16_gemm(int format, const void* A, const void* packed, const void* scales,
                const void* zeros, void* C, int64_t M, int64_t N, int64_t K,
                void* stream);
+
+/* ---- fused epilogue ---------------------------------------------------------
+ * w4a16_gemm_ex applies, per output element, on the fp32 accumulator c:
+ *     C[m,n] = act(alpha * c + bias[n]) + beta * R[m,n]
+ * and rounds once to C's dtype.  The alpha / beta pair is the one of the
+ * gemm primitive on page "gemm.rst" (D = alpha * A@B + beta * C, and C is not
+ * read when beta is 0); the per-element form is the optional (row, col)
+ * epilogue of page "Matmul2dFp4".  The pages name no activation; these are
+ * offered: */
+#define W4A16_ACT_NONE 0
+#define W4A16_ACT_RELU 1      /* max(x, 0)                                   */
+#define W4A16_ACT_SILU 2      /* x / (1 + exp(-x))                           */
+#define W4A16_ACT_GELU_TANH 3 /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+typedef struct w4a16_epilogue {
+  const void* bias;     /* bf16 (N) device array, or NULL (no bias); 2-byte aligned   */
+  const void* residual; /* (M, N) device array in C's dtype, row-major, or NULL; it
+                           may be C itself (in place), else must not overlap C;
+                           read only when beta != 0; aligned like C              */
+  float alpha;          /* multiplies A . W^T (1 for none)                         */
+  float beta;           /* multiplies the residual                                 */
+  int activation;       /* W4A16_ACT_*                                             */
+  int reserved;         /* must be 0                                               */
+} w4a16_epilogue;
+
+/* w4a16_gemm with the fused epilogue `ep` (NULL: exactly w4a16_gemm).  The
+ * epilogue runs in fp32 in the kernel's store (the tiled and both skinny
+ * kernels), so it adds only the bias / residual reads.  Accuracy: the GEMM
+ * bound above times |alpha| and the activation's Lipschitz constant (1, 1.1
+ * for SiLU, 1.13 for GELU), plus 2^-20 of the magnitudes involved and, for
+ * bf16 C, 2^-8 |C_exact|.  Errors as w4a16_gemm, plus W4A16_ERR_EPILOGUE, and
+ * W4A16_ERR_ALIGN for a misaligned bias or residual; `ep` is read during the
+ * call only. */
+int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* scales,
+                  const void* zeros, void* C, int64_t M, int64_t N, int64_t K,
+                  const w4a16_epilogue* ep, void* stream);
 
 /* Several weight matrices that share one activation matrix A and one K --
  * e.g. the q, k and v projections of a decoder layer, or its gate and up

@@ -29,7 +29,7 @@ def _header_defines():
 def test_library_exports_every_declared_function():
     lib = w4.load_library()
     names = _header_functions()
-    assert set(names) == {"w4a16_gemm", "w4a16_gemm_grouped", "w4a16_dequant",
+    assert set(names) == {"w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped", "w4a16_dequant",
                           "w4a16_gemm_path", "w4a16_strerror", "w4a16_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -43,14 +43,23 @@ def test_python_constants_match_header():
     assert d["W4A16_OUT_F32"] == w4.OUT_F32
     assert d["W4A16_PATH_SKINNY"] == w4.PATH_SKINNY
     assert d["W4A16_PATH_TILED"] == w4.PATH_TILED
-    for code in ("OK", "ERR_FORMAT", "ERR_SHAPE", "ERR_NULL", "ERR_ALIGN", "ERR_HIP"):
+    for code in ("OK", "ERR_FORMAT", "ERR_SHAPE", "ERR_NULL", "ERR_ALIGN", "ERR_HIP", "ERR_EPILOGUE"):
         assert d["W4A16_" + code] == getattr(w4, code)
     assert d["W4A16_MAX_GROUP"] == w4.MAX_GROUP
+    for name in ("NONE", "RELU", "SILU", "GELU_TANH"):
+        assert d["W4A16_ACT_" + name] == getattr(w4, "ACT_" + name)
+
+
+def test_epilogue_struct_layout():
+    # struct w4a16_epilogue: two pointers, two floats, two ints
+    assert ctypes.sizeof(w4.Epilogue) == 32
+    assert w4.Epilogue.alpha.offset == 16 and w4.Epilogue.activation.offset == 24
 
 
 def test_version_and_strerror():
-    assert w4.version() == 101
-    for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP):
+    assert w4.version() == 102
+    for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP,
+                 w4.ERR_EPILOGUE):
         assert w4.strerror(code) != "unknown status"
     assert w4.strerror(12345) == "unknown status"
 
@@ -113,6 +122,43 @@ def test_zero_extent_is_a_noop():
     assert _gemm(w4.INT4_G128, N=0) == w4.OK
     lib = w4.load_library()
     assert lib.w4a16_dequant(w4.MXFP4, PB, PS, None, PC, 0, 64, None) == w4.OK
+
+
+def _gemm_ex(ep, fmt=w4.INT4_G128, C=PC, M=16, N=64, K=128):
+    return w4.load_library().w4a16_gemm_ex(fmt, PA, PB, PS, PZ, C, M, N, K,
+                                           None if ep is None else ctypes.byref(ep), None)
+
+
+@pytest.mark.parametrize("fields,fmt,expect", [
+    (dict(activation=4), w4.INT4_G128, w4.ERR_EPILOGUE),           # unknown activation
+    (dict(activation=-1), w4.INT4_G128, w4.ERR_EPILOGUE),
+    (dict(reserved=1), w4.INT4_G128, w4.ERR_EPILOGUE),             # reserved must be 0
+    (dict(bias=0x100001), w4.INT4_G128, w4.ERR_ALIGN),             # bf16 bias, odd address
+    (dict(residual=0x200001, beta=1.0), w4.INT4_G128, w4.ERR_ALIGN),
+    (dict(residual=0x200002, beta=1.0), w4.INT4_G128 | w4.OUT_F32, w4.ERR_ALIGN),  # fp32: 4 B
+    # residual overlapping C (C at 0x500000, 16 x 64 bf16 = 2 KB) without being C
+    (dict(residual=0x500000 + 64, beta=1.0), w4.INT4_G128, w4.ERR_EPILOGUE),
+    (dict(residual=0x500000 - 64, beta=1.0), w4.INT4_G128, w4.ERR_EPILOGUE),
+])
+def test_gemm_ex_rejects_bad_epilogue(fields, fmt, expect):
+    ep = w4.Epilogue(None, None, 1.0, 0.0, 0, 0)
+    for k, v in fields.items():
+        setattr(ep, k, v)
+    assert _gemm_ex(ep, fmt) == expect
+
+
+def test_gemm_ex_validation_order_and_noops():
+    # shape errors come first; a bad activation is caught even at zero extent;
+    # with beta = 0 the residual is not read, so its address is not checked
+    bad = w4.Epilogue(None, None, 1.0, 0.0, 9, 0)
+    assert _gemm_ex(bad, fmt=7) == w4.ERR_FORMAT
+    assert _gemm_ex(bad, M=0) == w4.ERR_EPILOGUE
+    ok = w4.Epilogue(None, 0x500000 + 64, 1.0, 0.0, w4.ACT_SILU, 0)
+    assert _gemm_ex(ok, M=0) == w4.OK
+    assert _gemm_ex(None, M=0, N=0) == w4.OK
+    # a residual that is C itself (in place) and disjoint ones pass validation
+    # (the zero-extent calls never launch)
+    assert _gemm_ex(w4.Epilogue(None, 0x500000, 1.0, 1.0, 0, 0), M=0) == w4.OK
 
 
 def test_dequant_rejects_bad_arguments():

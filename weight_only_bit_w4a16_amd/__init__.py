@@ -27,8 +27,19 @@ OUT_BF16, OUT_F32 = 0x000, 0x100
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0x0000, 0x1000, 0x2000
 PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
 
-OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5
+OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP, ERR_EPILOGUE = 0, -1, -2, -3, -4, -5, -6
 MAX_GROUP = 8  # members of one w4a16_gemm_grouped call
+
+# fused epilogue: C = act(alpha * (A . W^T) + bias[n]) + beta * residual[m, n]
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
+ACTIVATIONS = {"none": ACT_NONE, "relu": ACT_RELU, "silu": ACT_SILU, "gelu_tanh": ACT_GELU_TANH}
+
+
+class Epilogue(ctypes.Structure):
+    """struct w4a16_epilogue of include/w4a16.h."""
+    _fields_ = [("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("activation", ctypes.c_int), ("reserved", ctypes.c_int)]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
@@ -54,6 +65,8 @@ def load_library():
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.w4a16_gemm.argtypes = [I, P, P, P, P, P, I64, I64, I64, P]
     lib.w4a16_gemm.restype = I
+    lib.w4a16_gemm_ex.argtypes = [I, P, P, P, P, P, I64, I64, I64, ctypes.POINTER(Epilogue), P]
+    lib.w4a16_gemm_ex.restype = I
     PP = ctypes.POINTER(ctypes.c_void_p)
     lib.w4a16_gemm_grouped.argtypes = [I, P, I, PP, PP, PP, PP, ctypes.POINTER(I64), I64, I64, P]
     lib.w4a16_gemm_grouped.restype = I
@@ -126,10 +139,34 @@ def _check_weights(fmt, packed, scales, zeros, N, K, device):
         raise ValueError("fp4 weights take no zeros")
 
 
+def _epilogue(bias, residual, alpha, beta, activation, out, M, N, device):
+    """The epilogue struct for these arguments, or None for a plain GEMM."""
+    if bias is None and residual is None and alpha == 1.0 and activation in ("none", ACT_NONE):
+        return None
+    act = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
+    if bias is not None:
+        if bias.dtype != torch.bfloat16:
+            raise ValueError("bias must be bf16")
+        _check(bias, "bias", (N,), 2, device)
+    if residual is not None:
+        if residual.dtype != out.dtype:
+            raise ValueError("residual must have the output's dtype")
+        _check(residual, "residual", (M, N), out.element_size(), device)
+    return Epilogue(None if bias is None else bias.data_ptr(),
+                    None if residual is None else residual.data_ptr(),
+                    float(alpha), float(beta), act, 0)
+
+
 def gemm(fmt: int, A: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
          zeros: torch.Tensor | None = None, out: torch.Tensor | None = None,
-         out_dtype: torch.dtype = torch.bfloat16, path: str = "auto", stream=None) -> torch.Tensor:
-    """C = A . dequant(packed, scales, zeros)^T on the GPU (asynchronous)."""
+         out_dtype: torch.dtype = torch.bfloat16, path: str = "auto", stream=None,
+         bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+         alpha: float = 1.0, beta: float = 1.0, activation="none") -> torch.Tensor:
+    """C = A . dequant(packed, scales, zeros)^T on the GPU (asynchronous).
+
+    With any of bias / residual / alpha / activation set, the fused epilogue
+    C = act(alpha * (A . W^T) + bias[n]) + beta * residual[m, n] is applied
+    in the kernel (residual may be ``out`` itself)."""
     if not A.is_cuda:
         raise ValueError("A must be a GPU tensor")
     device = A.device
@@ -143,8 +180,15 @@ def gemm(fmt: int, A: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
         raise ValueError("out must be bf16 or fp32")
     _check(out, "out", (M, N), out.element_size(), device)
     flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path]
-    rc = load_library().w4a16_gemm(int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales),
-                                   _ptr(zeros), _ptr(out), M, N, K, _stream_handle(stream))
+    ep = _epilogue(bias, residual, alpha, beta, activation, out, M, N, device)
+    lib = load_library()
+    if ep is None:
+        rc = lib.w4a16_gemm(int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales),
+                            _ptr(zeros), _ptr(out), M, N, K, _stream_handle(stream))
+    else:
+        rc = lib.w4a16_gemm_ex(int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales),
+                               _ptr(zeros), _ptr(out), M, N, K, ctypes.byref(ep),
+                               _stream_handle(stream))
     if rc != OK:
         raise W4A16Error(rc, "w4a16_gemm")
     return out
@@ -238,7 +282,9 @@ class PreparedGemm:
     The tensors are kept referenced for the object's lifetime.
     """
 
-    def __init__(self, fmt: int, A, packed, scales, zeros, out, path: str = "auto"):
+    def __init__(self, fmt: int, A, packed, scales, zeros, out, path: str = "auto",
+                 bias=None, residual=None, alpha: float = 1.0, beta: float = 1.0,
+                 activation="none"):
         device = A.device
         M, K = A.shape
         N = packed.shape[0]
@@ -247,12 +293,18 @@ class PreparedGemm:
         _check(out, "out", (M, N), out.element_size(), device)
         if out.dtype not in (torch.bfloat16, torch.float32):
             raise ValueError("out must be bf16 or fp32")
-        self.tensors = (A, packed, scales, zeros, out)
+        self.tensors = (A, packed, scales, zeros, out, bias, residual)
         flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path]
         self.kernel = gemm_path(fmt, M, N, K, path)
-        self._fn = load_library().w4a16_gemm
+        self._ep = _epilogue(bias, residual, alpha, beta, activation, out, M, N, device)
+        lib = load_library()
         self._args = (int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales), _ptr(zeros),
                       _ptr(out), M, N, K)
+        if self._ep is None:
+            self._fn = lib.w4a16_gemm
+        else:
+            self._fn = lib.w4a16_gemm_ex
+            self._args = self._args + (ctypes.byref(self._ep),)
 
     def __call__(self, stream=None):
         rc = self._fn(*self._args, _stream_handle(stream))

@@ -44,7 +44,7 @@ int choose_path(int format, int64_t M) {
 
 extern "C" {
 
-int w4a16_version(void) { return 101; }
+int w4a16_version(void) { return 102; }
 
 const char* w4a16_strerror(int status) {
   switch (status) {
@@ -56,6 +56,9 @@ const char* w4a16_strerror(int status) {
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for an fp4 format";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
     case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case W4A16_ERR_EPILOGUE:
+      return "bad epilogue: unknown activation, nonzero reserved field, or a residual that "
+             "overlaps C without being C";
     default: return "unknown status";
   }
 }
@@ -68,8 +71,17 @@ int w4a16_gemm_path(int format, int64_t M, int64_t N, int64_t K) {
 
 int w4a16_gemm(int format, const void* A, const void* packed, const void* scales,
                const void* zeros, void* C, int64_t M, int64_t N, int64_t K, void* stream) {
+  return w4a16_gemm_ex(format, A, packed, scales, zeros, C, M, N, K, nullptr, stream);
+}
+
+int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* scales,
+                  const void* zeros, void* C, int64_t M, int64_t N, int64_t K,
+                  const w4a16_epilogue* ep, void* stream) {
   const int rc = check_format_shape(format, M, N, K, true);
   if (rc != W4A16_OK) return rc;
+  if (ep && (ep->activation < W4A16_ACT_NONE || ep->activation > W4A16_ACT_GELU_TANH ||
+             ep->reserved != 0))
+    return W4A16_ERR_EPILOGUE;
   const int fmt = format & W4A16_FORMAT_MASK;
   const bool out_f32 = (format & W4A16_OUT_F32) != 0;
   if (M == 0 || N == 0) return W4A16_OK;  // nothing is read or written
@@ -77,9 +89,28 @@ int w4a16_gemm(int format, const void* A, const void* packed, const void* scales
   if (fmt == W4A16_INT4_G128 ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
   if (!aligned(A, 16) || !aligned(packed, 16)) return W4A16_ERR_ALIGN;
   if (fmt != W4A16_MXFP4 && !aligned(scales, 2)) return W4A16_ERR_ALIGN;
-  if (!aligned(C, out_f32 ? 4 : 2)) return W4A16_ERR_ALIGN;
+  const uintptr_t es = out_f32 ? 4 : 2;
+  if (!aligned(C, es)) return W4A16_ERR_ALIGN;
+  w4a16::Epilogue epi = {};
+  if (ep) {
+    const bool res = ep->residual && ep->beta != 0.0f;
+    if (ep->bias && !aligned(ep->bias, 2)) return W4A16_ERR_ALIGN;
+    if (res && !aligned(ep->residual, es)) return W4A16_ERR_ALIGN;
+    if (res && ep->residual != C) {
+      const uintptr_t r0 = (uintptr_t)ep->residual, c0 = (uintptr_t)C;
+      const uintptr_t bytes = (uintptr_t)M * (uintptr_t)N * es;
+      if (r0 < c0 + bytes && c0 < r0 + bytes) return W4A16_ERR_EPILOGUE;
+    }
+    epi.bias = static_cast<const uint16_t*>(ep->bias);
+    epi.res = res ? ep->residual : nullptr;
+    epi.alpha = ep->alpha;
+    epi.beta = ep->beta;
+    epi.act = ep->activation;
+    epi.on = 1;
+  }
 
   w4a16::GemmArgs a;
+  a.epi = epi;
   a.fmt = fmt;
   a.out_f32 = out_f32;
   a.A = static_cast<const uint16_t*>(A);
@@ -145,6 +176,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
   for (int i = 0; i < count; ++i) {
     if (N[i] == 0) continue;
     w4a16::GemmArgs a;
+    a.epi = w4a16::Epilogue{};
     a.fmt = fmt;
     a.out_f32 = out_f32;
     a.A = static_cast<const uint16_t*>(A);

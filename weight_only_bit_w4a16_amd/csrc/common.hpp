@@ -299,6 +299,47 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- fused epilogue -------------------------------------------------------------
+
+// Activations in fp32, branch-free, from the hardware base-2 exponential and
+// reciprocal (each about 1 ulp): with sigma(x) = 1 / (1 + 2^(-x log2 e)),
+//   SiLU(x) = x sigma(x);
+//   GELU, tanh form: 0.5 x (1 + tanh(u)) = x sigma(2u), u = sqrt(2/pi) (x + 0.044715 x^3)
+// (since 1 + tanh(u) = 2 sigma(2u)).  Saturation is exact: 2^(+large) = inf
+// gives sigma = 0, 2^(-large) = 0 gives sigma = 1.
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+__device__ __forceinline__ float act_silu(float v) { return v * sigmoid_fast(v); }
+__device__ __forceinline__ float act_gelu_tanh(float v) {
+  const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * v, v * v, v);
+  return v * sigmoid_fast(2.f * u);
+}
+__device__ __forceinline__ float act_relu(float v) { return v > 0.f ? v : 0.f; }
+
+// C[m, n] = act(alpha * c + bias[n]) + beta * R[m, n] on the fp32 accumulator
+// c, given the operands already loaded (b = bias[n] or 0, r = R[m, n] or
+// unused); the caller stores the result once (fp32, or bf16 RNE).
+template <class E>
+__device__ __forceinline__ float epilogue_value(const E& e, float c, float b, float r) {
+  float v = __builtin_fmaf(e.alpha, c, b);
+  if (e.act == 1) {
+    v = act_relu(v);
+  } else if (e.act == 2) {
+    v = act_silu(v);
+  } else if (e.act == 3) {
+    v = act_gelu_tanh(v);
+  }
+  return e.res ? __builtin_fmaf(e.beta, r, v) : v;
+}
+
+// one residual element (C's dtype) as fp32
+template <bool OUT_F32>
+__device__ __forceinline__ float residual_at(const void* res, int64_t mn) {
+  return OUT_F32 ? reinterpret_cast<const float*>(res)[mn]
+                 : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(res)[mn]);
+}
+
 // ---- MFMA ---------------------------------------------------------------------
 
 // D(16x16 fp32) += A(16x32 bf16) B(32x16 bf16).  Lane l supplies row l%16 of A

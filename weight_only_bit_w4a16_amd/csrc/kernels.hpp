@@ -8,6 +8,17 @@
 
 namespace w4a16 {
 
+// Fused epilogue on the fp32 accumulator c: C = act(alpha * c + bias[n]) +
+// beta * R[m, n] (bias bf16 (N) or null; R (M, N) in C's dtype, read only
+// when non-null and beta != 0).  `on` false: C = c.
+struct Epilogue {
+  const uint16_t* bias;
+  const void* res;
+  float alpha, beta;
+  int act;  // 0 none, 1 ReLU, 2 SiLU, 3 GELU (tanh form)
+  int on;
+};
+
 struct GemmArgs {
   int fmt;        // 0 int4 g128, 1 NVFP4, 2 MXFP4
   bool out_f32;   // C is fp32 (else bf16)
@@ -18,6 +29,7 @@ struct GemmArgs {
   void* C;
   int64_t M, N, K;
   hipStream_t stream;
+  Epilogue epi;
 };
 
 // Several weight matrices sharing one A (and K): member i has its own
@@ -35,6 +47,7 @@ struct GroupedArgs {
   int64_t N[kMaxGroup];
   int64_t M, K;
   hipStream_t stream;
+  Epilogue epi;  // single-matrix launches only (count == 1)
 };
 
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, const uint8_t* zeros,

@@ -68,7 +68,8 @@ struct SkinnyGroup {
 // GROUPED: more than one member, blockIdx.z (a single GEMM reads member 0).
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* __restrict__ A,
-                                                                SkinnyGroup grp, int M, int K) {
+                                                                SkinnyGroup grp, int M, int K,
+                                                                Epilogue epi) {
   // the group member whose columns this workgroup computes: its fields come
   // in one scalar load round trip at a workgroup-uniform offset
   const SkinnyMember& mem = grp.m[GROUPED ? (int)blockIdx.z : 0];
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   // rows: rows past N or M, and k past K, read as 0 (hardware range check).
   const int rows = min(grp.rows, N - n0);  // lanes of rows past it read zeros
   const int arows = min(16, M - m0);
+
   const uint32_t rowb = (uint32_t)(K >> 1);
   const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
@@ -353,6 +355,42 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   red[wave][lane] = acc;
   lds_barrier();
   if (wave != 0) return;
+  // the plain store and the fused epilogue are separate paths (one uniform
+  // branch; the plain path carries no epilogue code)
+  if (!epi.on) {
+    f32x4_t sum = red[0][lane];
+    for (int w = 1; w < waves; ++w) {
+      const f32x4_t v = red[w][lane];
+      sum[0] += v[0];
+      sum[1] += v[1];
+      sum[2] += v[2];
+      sum[3] += v[3];
+    }
+    if (nl >= rows) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 4 * g + i;
+      if (m < M) {
+        if constexpr (OUT_F32) {
+          reinterpret_cast<float*>(C)[(int64_t)m * N + n] = sum[i];
+        } else {
+          reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n] = (__bf16)sum[i];
+        }
+      }
+    }
+    return;
+  }
+  // epilogue operands first, all in one round trip (the residual may alias
+  // C, so the compiler could not hoist them over the stores itself)
+  float epi_b = 0.f, epi_r[4] = {0.f, 0.f, 0.f, 0.f};
+  if (nl < rows) {
+    if (epi.bias) epi_b = bf16_bits_to_f32(epi.bias[n]);
+    if (epi.res) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i < arows) epi_r[i] = residual_at<OUT_F32>(epi.res, (int64_t)(m0 + 4 * g + i) * N + n);
+    }
+  }
   f32x4_t sum = red[0][lane];
   for (int w = 1; w < waves; ++w) {
     const f32x4_t v = red[w][lane];
@@ -366,10 +404,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 4 * g + i;
     if (m < M) {
+      const int64_t mn = (int64_t)m * N + n;
+      const float v = epilogue_value(epi, sum[i], epi_b, epi_r[i]);
       if constexpr (OUT_F32) {
-        reinterpret_cast<float*>(C)[(int64_t)m * N + n] = sum[i];
+        reinterpret_cast<float*>(C)[mn] = v;
       } else {
-        reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n] = (__bf16)sum[i];
+        reinterpret_cast<__bf16*>(C)[mn] = (__bf16)v;
       }
     }
   }
@@ -394,7 +434,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
 template <int FMT, bool OUT_F32, int U, int NS>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uint16_t* __restrict__ A,
                                                                        SkinnyGroup grp, int M, int K,
-                                                                       int tiles) {
+                                                                       int tiles, Epilogue epi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -546,6 +586,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
   };
   // split-K sum over the waves (wave 0, in wave order) and the tile's stores
   auto reduce_store = [&](const Tile& T, int b) {
+    // epilogue operands first (one round trip; the residual may alias C)
+    float eb = 0.f, er[4] = {0.f, 0.f, 0.f, 0.f};
+    if (epi.on && nl < T.rows) {
+      const int n = T.n0 + nl;
+      if (epi.bias) eb = bf16_bits_to_f32(epi.bias[n]);
+      if (epi.res) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * g + i < M) er[i] = residual_at<OUT_F32>(epi.res, (int64_t)(4 * g + i) * T.N + n);
+      }
+    }
     const f32x4_t* r = red + b * waves * 64 + lane;
     f32x4_t sum = r[0];
     for (int w = 1; w < waves; ++w) {
@@ -561,10 +612,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
       if (m < M) {
+        const int64_t mn = (int64_t)m * T.N + n;
+        const float v = epi.on ? epilogue_value(epi, sum[i], eb, er[i]) : sum[i];
         if constexpr (OUT_F32) {
-          reinterpret_cast<float*>(T.C)[(int64_t)m * T.N + n] = sum[i];
+          reinterpret_cast<float*>(T.C)[mn] = v;
         } else {
-          reinterpret_cast<__bf16*>(T.C)[(int64_t)m * T.N + n] = (__bf16)sum[i];
+          reinterpret_cast<__bf16*>(T.C)[mn] = (__bf16)v;
         }
       }
     }
@@ -616,10 +669,10 @@ template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, bool 
 hipError_t launch_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim3 block, unsigned lds) {
   if (a.count > 1)
     hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, true>), grid, block,
-                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K);
+                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
   else
     hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, false>), grid, block,
-                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K);
+                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
   return hipGetLastError();
 }
 
@@ -758,7 +811,7 @@ hipError_t launch_stream_k(const GroupedArgs& a, const SkinnyGroup& grp, int til
   const dim3 grid((unsigned)(tiles < resident ? tiles : resident));
   const dim3 block(64 * waves);
   hipLaunchKernelGGL((skinny_stream_kernel<FMT, OUT_F32, U, NS>), grid, block, lds, a.stream, a.A, grp, (int)a.M,
-                     (int)a.K, tiles);
+                     (int)a.K, tiles, a.epi);
   return hipGetLastError();
 }
 
@@ -865,6 +918,7 @@ hipError_t launch_skinny(const GemmArgs& a) {
   g.M = a.M;
   g.K = a.K;
   g.stream = a.stream;
+  g.epi = a.epi;
   return launch_skinny_grouped(g);
 }
 

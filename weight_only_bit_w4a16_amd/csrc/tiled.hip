@@ -140,7 +140,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
                                                               const void* __restrict__ scales,
                                                               const uint8_t* __restrict__ zeros,
                                                               void* __restrict__ C, int M, int N,
-                                                              int K) {
+                                                              int K, Epilogue epi) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
   constexpr int kABytes = CFG::kABytes, kBBytes = CFG::kBBytes;
   using L = Layout<FMT, CFG>;
@@ -344,29 +344,142 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
 // ---- epilogue: lane holds output row l16 of each 16x16 tile, columns
 // 4g .. 4g+3 (one 8- or 16-byte store when the rows allow aligned vectors)
   const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & (OUT_F32 ? 15 : 7)) == 0);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m_base + wm * (TM * 16) + i * 16 + l16;
-    if (m >= M) continue;
+  // Fused epilogue, in batches of kRB row blocks: the batch's residual is
+  // loaded first (it may alias C, so the compiler could not hoist its loads
+  // over the stores itself), alpha * c + bias and the activation run while
+  // it is in flight, then the residual is added and the batch stored.  Loads
+  // are unconditional at clamped indices (values past M / N come from a valid
+  // element and are never stored), and each choice between code paths is
+  // made once per batch, not per element, so the loads issue as one group.
+  constexpr int kRW = OUT_F32 ? 4 : 2;                // residual words per (row block, column group)
+  constexpr int kRB = OUT_F32 ? TM / 4 : TM / 2;      // 32 registers of residual per batch
+  f32x4_t eb[TN];
+  if (epi.on && epi.bias) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int n0 = n_base + wn * (TN * 16) + t * 16 + 4 * g;
-      const f32x4_t v = acc[i][t];
-      if (vec && n0 < N) {
-        if constexpr (OUT_F32) {
-          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(C) + (int64_t)m * N + n0) = v;
-        } else {
-          *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(C) + (int64_t)m * N + n0) =
-              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        }
-      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (n0 + r < N) {
-            if constexpr (OUT_F32)
-              reinterpret_cast<float*>(C)[(int64_t)m * N + n0 + r] = v[r];
-            else
-              reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n0 + r] = (__bf16)v[r];
+      for (int r = 0; r < 4; ++r) eb[t][r] = bf16_bits_to_f32(epi.bias[min(n0 + r, N - 1)]);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) eb[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const bool res_vec = vec && epi.res &&
+                       (reinterpret_cast<uintptr_t>(epi.res) & (OUT_F32 ? 15 : 7)) == 0;
+#pragma unroll
+  for (int i0 = 0; i0 < TM; i0 += kRB) {
+    uint32_t rw[kRB][TN][kRW];
+    if (epi.on && epi.res && res_vec) {
+      // N % 4 == 0: the four columns of a group are all in range or all out
+#pragma unroll
+      for (int j = 0; j < kRB; ++j) {
+        const int m = min(m_base + wm * (TM * 16) + (i0 + j) * 16 + l16, M - 1);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          const int n0 = n_base + wn * (TN * 16) + t * 16 + 4 * g;
+          const int64_t mn = (int64_t)m * N + min(n0, N - 4);
+          if constexpr (OUT_F32) {
+            const u32x4_t q = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(epi.res) + mn);
+#pragma unroll
+            for (int w = 0; w < kRW; ++w) rw[j][t][w] = q[w];
+          } else {
+            const u32x2_t q = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(epi.res) + mn);
+            rw[j][t][0] = q[0];
+            rw[j][t][1] = q[1];
+          }
+        }
+      }
+    } else if (epi.on && epi.res) {
+#pragma unroll
+      for (int j = 0; j < kRB; ++j) {
+        const int m = min(m_base + wm * (TM * 16) + (i0 + j) * 16 + l16, M - 1);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          const int n0 = n_base + wn * (TN * 16) + t * 16 + 4 * g;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t mn = (int64_t)m * N + min(n0 + r, N - 1);
+            if constexpr (OUT_F32) {
+              rw[j][t][r] = reinterpret_cast<const uint32_t*>(epi.res)[mn];
+            } else {
+              const uint32_t h = reinterpret_cast<const uint16_t*>(epi.res)[mn];
+              if (r & 1)
+                rw[j][t][r >> 1] |= h << 16;
+              else
+                rw[j][t][r >> 1] = h;
+            }
+          }
+        }
+      }
+    }
+    if (epi.on) {
+#pragma unroll
+      for (int j = 0; j < kRB; ++j)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i0 + j][t][r] = __builtin_fmaf(epi.alpha, acc[i0 + j][t][r], eb[t][r]);
+      if (epi.act == 1) {
+#pragma unroll
+        for (int j = 0; j < kRB; ++j)
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i0 + j][t][r] = act_relu(acc[i0 + j][t][r]);
+      } else if (epi.act == 2) {
+#pragma unroll
+        for (int j = 0; j < kRB; ++j)
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i0 + j][t][r] = act_silu(acc[i0 + j][t][r]);
+      } else if (epi.act == 3) {
+#pragma unroll
+        for (int j = 0; j < kRB; ++j)
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i0 + j][t][r] = act_gelu_tanh(acc[i0 + j][t][r]);
+      }
+      if (epi.res) {
+#pragma unroll
+        for (int j = 0; j < kRB; ++j)
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float res = OUT_F32 ? __uint_as_float(rw[j][t][r])
+                                        : bf16_bits_to_f32((rw[j][t][r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+              acc[i0 + j][t][r] = __builtin_fmaf(epi.beta, res, acc[i0 + j][t][r]);
+            }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) {
+      const int i = i0 + j;
+      const int m = m_base + wm * (TM * 16) + i * 16 + l16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int n0 = n_base + wn * (TN * 16) + t * 16 + 4 * g;
+        const f32x4_t v = acc[i][t];
+        if (vec && n0 < N) {
+          if constexpr (OUT_F32) {
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(C) + (int64_t)m * N + n0) = v;
+          } else {
+            *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(C) + (int64_t)m * N + n0) =
+                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (n0 + r < N) {
+              if constexpr (OUT_F32)
+                reinterpret_cast<float*>(C)[(int64_t)m * N + n0 + r] = v[r];
+              else
+                reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n0 + r] = (__bf16)v[r];
+            }
           }
         }
       }
@@ -384,7 +497,7 @@ hipError_t launch_cfg(const GemmArgs& a) {
   const int64_t tiles = ((a.N + CFG::BN - 1) / CFG::BN) * ((a.M + CFG::BM - 1) / CFG::BM);
   hipLaunchKernelGGL((tiled_kernel<FMT, OUT_F32, CFG>), dim3((unsigned)tiles), dim3(CFG::kThreads),
                      0, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N,
-                     (int)a.K);
+                     (int)a.K, a.epi);
   return hipGetLastError();
 }
 
