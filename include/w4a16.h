@@ -68,9 +68,10 @@ extern "C" {
 #define W4A16_OUT_F32 0x100  /* C is fp32                                    */
 
 /* Kernel choice for w4a16_gemm.  AUTO picks the skinny (split-K, register
- * decode) kernel for M <= 16 and the LDS-tiled MFMA kernel otherwise; the
- * other two force one kernel at any M (the skinny kernel then walks M in
- * slices of 16 rows). */
+ * decode) kernel for M <= 16, and also for M <= 192 when the tiled kernel's
+ * 256 x 256 tiles would number fewer than 256 (one per CU); the LDS-tiled
+ * MFMA kernel otherwise.  The other two force one kernel at any M (the
+ * skinny kernel then walks M in slices of 16 rows). */
 #define W4A16_PATH_AUTO 0x0000
 #define W4A16_PATH_SKINNY 0x1000
 #define W4A16_PATH_TILED 0x2000

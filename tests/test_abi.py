@@ -67,7 +67,11 @@ def test_version_and_strerror():
 def test_path_choice():
     assert w4.gemm_path(w4.INT4_G128, 1, 8192, 3072) == "skinny"
     assert w4.gemm_path(w4.NVFP4, 16, 3072, 8192) == "skinny"
-    assert w4.gemm_path(w4.MXFP4, 17, 64, 64) == "tiled"
+    # 17 <= M <= 192 takes the skinny kernel while the tiled grid has < 256 tiles
+    assert w4.gemm_path(w4.MXFP4, 17, 64, 64) == "skinny"
+    assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "skinny"
+    assert w4.gemm_path(w4.INT4_G128, 193, 8192, 3072) == "tiled"
+    assert w4.gemm_path(w4.INT4_G128, 64, 65536, 3072) == "tiled"   # 256 tiles
     assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072) == "tiled"
     assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072, "skinny") == "skinny"
     assert w4.gemm_path(w4.INT4_G128, 1, 64, 128, "tiled") == "tiled"

@@ -74,8 +74,15 @@ def test_grouped_skips_empty_member():
 
 @pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.NVFP4])
 def test_grouped_tiled_path(fmt):
-    # M > 16: one tiled launch per member
-    _check_group(fmt, 40, [96, 200], 384, 3, torch.bfloat16, "auto")
+    # the tiled kernel: one launch per member
+    _check_group(fmt, 40, [96, 200], 384, 3, torch.bfloat16, "tiled")
+
+
+@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.MXFP4])
+def test_grouped_mid_m_takes_skinny(fmt):
+    # 16 < M <= 192 with few tiles: one skinny launch over 16-row slices
+    assert w4.gemm_path(fmt, 40, 200, 384) == "skinny"
+    _check_group(fmt, 40, [96, 200], 384, 6, torch.bfloat16, "auto")
 
 
 @pytest.mark.parametrize("members", [("q", "k", "v"), ("gate", "up")])

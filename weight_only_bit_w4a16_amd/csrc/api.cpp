@@ -32,12 +32,18 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
   return W4A16_OK;
 }
 
-// M <= 16 streams the weights once through the skinny kernel; larger M
-// amortises the decode over a 256-row tile.
-int choose_path(int format, int64_t M) {
+// The skinny kernel reads the weights once per 16-row slice of A; the tiled
+// kernel reads them once per 256-row tile but runs the whole of K inside each
+// 256 x 256 tile.  With fewer tiles than CUs the tiled kernel leaves CUs idle
+// and spends its MFMA work on padding rows, so the skinny kernel is faster up
+// to M ~ 200 (measured at N = 8192, K = 3072: M = 64 29 us vs 97 us; M = 192
+// 81 vs 101; M = 256 106 vs 103).  N: the widest matrix of the launch.
+int choose_path(int format, int64_t M, int64_t N) {
   const int forced = format & W4A16_PATH_MASK;
   if (forced) return forced;
-  return M <= 16 ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
+  if (M <= 16) return W4A16_PATH_SKINNY;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return M <= 192 && tiles < 256 ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
 }
 
 }  // namespace
@@ -66,7 +72,7 @@ const char* w4a16_strerror(int status) {
 int w4a16_gemm_path(int format, int64_t M, int64_t N, int64_t K) {
   const int rc = check_format_shape(format, M, N, K, true);
   if (rc != W4A16_OK) return rc;
-  return choose_path(format, M);
+  return choose_path(format, M, N);
 }
 
 int w4a16_gemm(int format, const void* A, const void* packed, const void* scales,
@@ -122,7 +128,7 @@ int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* sca
   a.N = N;
   a.K = K;
   a.stream = static_cast<hipStream_t>(stream);
-  const hipError_t e = choose_path(format, M) == W4A16_PATH_SKINNY ? w4a16::launch_skinny(a)
+  const hipError_t e = choose_path(format, M, N) == W4A16_PATH_SKINNY ? w4a16::launch_skinny(a)
                                                                    : w4a16::launch_tiled(a);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
@@ -153,7 +159,9 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     if (!aligned(C[i], out_f32 ? 4 : 2)) return W4A16_ERR_ALIGN;
   }
 
-  if (choose_path(format, M) == W4A16_PATH_SKINNY) {
+  int64_t max_n = 0;
+  for (int i = 0; i < count; ++i) max_n = N[i] > max_n ? N[i] : max_n;
+  if (choose_path(format, M, max_n) == W4A16_PATH_SKINNY) {
     w4a16::GroupedArgs g = {};
     g.fmt = fmt;
     g.out_f32 = out_f32;
