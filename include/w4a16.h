@@ -36,8 +36,8 @@
  * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing and
  * checks no pointer);
  * 0 < K <= 2^22, K % 32 == 0, and K % 128 == 0 for int4; M, N < 2^31.
- * Zero points: the GEMM is exact for zero bytes 0..127 (the format stores
- * 0..15); the dequantisation takes any byte.
+ * Zero points: the GEMM and the dequantisation take any zero byte 0..255
+ * (the format stores 0..15).
  *
  * Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls only
  * enqueue kernels and return; they never synchronise, allocate or read
@@ -68,13 +68,18 @@ extern "C" {
 #define W4A16_OUT_F32 0x100  /* C is fp32                                    */
 
 /* Kernel choice for w4a16_gemm.  AUTO picks the skinny (split-K, register
- * decode) kernel for M <= 16, and also for M <= 192 when the tiled kernel's
- * 256 x 256 tiles would number fewer than 256 (one per CU); the LDS-tiled
- * MFMA kernel otherwise.  The other two force one kernel at any M (the
- * skinny kernel then walks M in slices of 16 rows). */
+ * decode) kernel for M <= 16.  Above that, the mid kernel (tiles of 32
+ * columns x up to 64 rows, split-K, each weight decoded once per tile) when it
+ * has at least 160 workgroups and M <= 384 while the LDS-tiled MFMA kernel
+ * would have fewer than 256 tiles of 256 x 256 (M <= 48 when it would have
+ * more), the skinny kernel when the mid kernel would have fewer workgroups,
+ * and the tiled kernel otherwise.  The others force one kernel at any M (the
+ * skinny kernel then walks M in slices of 16 rows, the mid kernel in tiles of
+ * 32 to 64). */
 #define W4A16_PATH_AUTO 0x0000
 #define W4A16_PATH_SKINNY 0x1000
 #define W4A16_PATH_TILED 0x2000
+#define W4A16_PATH_MID 0x3000
 #define W4A16_PATH_MASK 0x3000
 
 /* ---- status codes --------------------------------------------------------- */
@@ -164,8 +169,8 @@ int w4a16_dequant(int format, const void* packed, const void* scales,
                   const void* zeros, void* W, int64_t N, int64_t K, void* stream);
 
 /* Which kernel w4a16_gemm would launch for these arguments, without launching:
- * returns W4A16_PATH_SKINNY or W4A16_PATH_TILED, or a negative status if the
- * format / shape would be rejected.  Host-only. */
+ * returns W4A16_PATH_SKINNY, W4A16_PATH_MID or W4A16_PATH_TILED, or a
+ * negative status if the format / shape would be rejected.  Host-only. */
 int w4a16_gemm_path(int format, int64_t M, int64_t N, int64_t K);
 
 /* Static, NUL-terminated description of a status code. */

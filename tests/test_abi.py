@@ -43,6 +43,7 @@ def test_python_constants_match_header():
     assert d["W4A16_OUT_F32"] == w4.OUT_F32
     assert d["W4A16_PATH_SKINNY"] == w4.PATH_SKINNY
     assert d["W4A16_PATH_TILED"] == w4.PATH_TILED
+    assert d["W4A16_PATH_MID"] == w4.PATH_MID
     for code in ("OK", "ERR_FORMAT", "ERR_SHAPE", "ERR_NULL", "ERR_ALIGN", "ERR_HIP", "ERR_EPILOGUE"):
         assert d["W4A16_" + code] == getattr(w4, code)
     assert d["W4A16_MAX_GROUP"] == w4.MAX_GROUP
@@ -57,7 +58,7 @@ def test_epilogue_struct_layout():
 
 
 def test_version_and_strerror():
-    assert w4.version() == 102
+    assert w4.version() == 103
     for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP,
                  w4.ERR_EPILOGUE):
         assert w4.strerror(code) != "unknown status"
@@ -67,14 +68,24 @@ def test_version_and_strerror():
 def test_path_choice():
     assert w4.gemm_path(w4.INT4_G128, 1, 8192, 3072) == "skinny"
     assert w4.gemm_path(w4.NVFP4, 16, 3072, 8192) == "skinny"
-    # 17 <= M <= 192 takes the skinny kernel while the tiled grid has < 256 tiles
+    # 17 <= M <= 384 with a small tiled grid: the mid kernel when it has >= 160
+    # workgroups of 32 columns x 64 rows, else the skinny kernel
     assert w4.gemm_path(w4.MXFP4, 17, 64, 64) == "skinny"
-    assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "skinny"
-    assert w4.gemm_path(w4.INT4_G128, 193, 8192, 3072) == "tiled"
-    assert w4.gemm_path(w4.INT4_G128, 64, 65536, 3072) == "tiled"   # 256 tiles
+    assert w4.gemm_path(w4.INT4_G128, 64, 1024, 3072) == "skinny"
+    assert w4.gemm_path(w4.NVFP4, 64, 3072, 8192) == "skinny"        # 96 workgroups
+    assert w4.gemm_path(w4.NVFP4, 65, 3072, 8192) == "mid"           # 192
+    assert w4.gemm_path(w4.INT4_G128, 17, 5120, 3072) == "mid"       # 160
+    assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "mid"
+    assert w4.gemm_path(w4.INT4_G128, 384, 8192, 3072) == "mid"
+    assert w4.gemm_path(w4.INT4_G128, 385, 8192, 3072) == "tiled"
+    # a large tiled grid (>= 256 tiles): the mid kernel up to 48 rows
+    assert w4.gemm_path(w4.INT4_G128, 48, 65536, 3072) == "mid"
+    assert w4.gemm_path(w4.INT4_G128, 49, 65536, 3072) == "tiled"
     assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072) == "tiled"
     assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072, "skinny") == "skinny"
     assert w4.gemm_path(w4.INT4_G128, 1, 64, 128, "tiled") == "tiled"
+    assert w4.gemm_path(w4.NVFP4, 1, 64, 128, "mid") == "mid"
+    assert w4.gemm_path(w4.NVFP4, 4096, 64, 128, "mid") == "mid"
 
 
 # fake, aligned device addresses: every call below fails validation (or is a
@@ -89,7 +100,7 @@ def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
 @pytest.mark.parametrize("fmt,M,N,K,expect", [
     (3, 16, 64, 128, w4.ERR_FORMAT),                          # unknown format
     (w4.INT4_G128 | 0x4000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
-    (w4.INT4_G128 | 0x3000, 16, 64, 128, w4.ERR_FORMAT),      # both paths forced
+    (w4.INT4_G128 | 0x8000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
     (w4.INT4_G128, -1, 64, 128, w4.ERR_SHAPE),
     (w4.INT4_G128, 16, -5, 128, w4.ERR_SHAPE),
     (w4.INT4_G128, 16, 64, 0, w4.ERR_SHAPE),

@@ -4,7 +4,7 @@ C = act(alpha * (A . W^T) + bias[n]) + beta * R[m, n] must match the oracle's
 binary64 GEMM followed by its binary64 epilogue within the epilogue bound
 (the GEMM gate carried through alpha and the activation's Lipschitz constant,
 fp32 rounding of the epilogue, one bf16 rounding of bf16 output).  Covered:
-every activation on the skinny kernel, the tiled kernel and the streaming
+every activation on the skinny, mid and tiled kernels and the streaming
 skinny variant (single matrices of >= 1024 column tiles), both output dtypes,
 bias and residual on and off, the residual being the output itself (in
 place), beta = 0 with a residual that must not be read, and alpha = 0.
@@ -21,9 +21,11 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
 ACTS = ["none", "relu", "silu", "gelu_tanh"]
 
-# (fmt, M, N, K, path): skinny, tiled, and a launch the streaming variant takes
+# (fmt, M, N, K, path): skinny, mid, tiled, and a launch the streaming
+# variant takes
 SHAPES = {
     "skinny": (w4.INT4_G128, 3, 200, 384, "skinny"),
+    "mid": (w4.MXFP4, 40, 136, 320, "mid"),
     "tiled": (w4.NVFP4, 40, 136, 256, "tiled"),
     "stream": (w4.INT4_G128, 1, 16384, 256, "auto"),
 }
@@ -96,7 +98,7 @@ def test_epilogue_in_place_residual(kernel):
     _check(kernel, fmt, M, N, K, path, "silu", torch.bfloat16, True, True, 1.0, 1.0, in_place=True)
 
 
-@pytest.mark.parametrize("kernel", ["skinny", "tiled"])
+@pytest.mark.parametrize("kernel", ["skinny", "mid", "tiled"])
 def test_epilogue_partial_features(kernel):
     fmt, M, N, K, path = SHAPES[kernel]
     _check(kernel, fmt, M, N, K, path, "none", torch.float32, True, False, 1.0, 0.0)     # bias only
@@ -105,7 +107,7 @@ def test_epilogue_partial_features(kernel):
     _check(kernel, fmt, M, N, K, path, "gelu_tanh", torch.float32, True, False, 0.0, 0.0)  # alpha 0
 
 
-@pytest.mark.parametrize("kernel", ["skinny", "tiled"])
+@pytest.mark.parametrize("kernel", ["skinny", "mid", "tiled"])
 def test_epilogue_beta_zero_does_not_read_residual(kernel):
     fmt, M, N, K, path = SHAPES[kernel]
     case = inputs.make_case(fmt, M, N, K, 5)

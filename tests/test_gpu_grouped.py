@@ -79,10 +79,21 @@ def test_grouped_tiled_path(fmt):
 
 
 @pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.MXFP4])
-def test_grouped_mid_m_takes_skinny(fmt):
-    # 16 < M <= 192 with few tiles: one skinny launch over 16-row slices
-    assert w4.gemm_path(fmt, 40, 200, 384) == "skinny"
-    _check_group(fmt, 40, [96, 200], 384, 6, torch.bfloat16, "auto")
+def test_grouped_mid_m(fmt):
+    # the mid kernel: one launch per member
+    _check_group(fmt, 40, [96, 200], 384, 6, torch.bfloat16, "mid")
+
+
+def test_grouped_mid_m_auto():
+    # 16 < M <= 384 and a wide member: the mid kernel, chosen for the widest
+    assert w4.gemm_path(w4.NVFP4, 40, 5120, 256) == "mid"
+    _check_group(w4.NVFP4, 40, [5120, 1024], 256, 7, torch.bfloat16, "auto")
+
+
+@pytest.mark.parametrize("fmt", [w4.NVFP4, w4.MXFP4])
+def test_grouped_mid_m_forced_skinny(fmt):
+    # the skinny kernel over 16-row slices, all members in one launch
+    _check_group(fmt, 40, [96, 0, 200], 384, 8, torch.float32, "skinny")
 
 
 @pytest.mark.parametrize("members", [("q", "k", "v"), ("gate", "up")])

@@ -155,7 +155,7 @@ def _workload_ref(name, seed):
     return _REF_CACHE[(name, seed)]
 
 
-@pytest.mark.parametrize("path", ["auto", "skinny", "tiled"])
+@pytest.mark.parametrize("path", ["auto", "skinny", "mid", "tiled"])
 @pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_gemm_workloads_full(name, seed, path):
@@ -220,7 +220,7 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("path", ["skinny", "tiled"])
+@pytest.mark.parametrize("path", ["skinny", "mid", "tiled"])
 @pytest.mark.parametrize("fmt,M,N,K", RAGGED)
 def test_gemm_ragged(fmt, M, N, K, path):
     case = inputs.make_case(fmt, M, N, K, seed=M * 7 + N * 3 + K)
@@ -230,7 +230,7 @@ def test_gemm_ragged(fmt, M, N, K, path):
         check_gate(C, Cref, S, odt == torch.bfloat16, f"ragged {fmt} {M}x{N}x{K} {path} {odt}")
 
 
-@pytest.mark.parametrize("path", ["skinny", "tiled"])
+@pytest.mark.parametrize("path", ["skinny", "mid", "tiled"])
 def test_gemm_degenerate(path):
     # every int4 code equal to its zero point -> exactly 0
     M, N, K = 4, 48, 256
@@ -246,6 +246,23 @@ def test_gemm_degenerate(path):
         assert np.all(run_gemm(case, torch.float32, path) == 0)
 
 
+@pytest.mark.parametrize("path,M,K", [
+    ("skinny", 1, 512),     # A staged in LDS (even / odd k order)
+    ("skinny", 16, 4096),   # A too large for the LDS copy: natural k order
+    ("mid", 40, 512), ("tiled", 40, 512)])
+def test_gemm_int4_any_zero_byte(path, M, K):
+    # zero points across the whole byte range (the format itself stores 0..15)
+    N = 96
+    case = inputs.make_case(w4.INT4_G128, M, N, K, seed=11 + M)
+    rng = np.random.default_rng(12 + M)
+    case.zeros[:] = rng.integers(0, 256, size=case.zeros.shape, dtype=np.uint8)
+    case.zeros.flat[:4] = [0, 127, 128, 255]
+    Cref, S = oracle.gemm(w4.INT4_G128, case.A, case.packed, case.scales, case.zeros, M, N, K)
+    for odt in (torch.float32, torch.bfloat16):
+        C = run_gemm(case, odt, path)
+        check_gate(C, Cref, S, odt == torch.bfloat16, f"int4 zeros 0..255 {M}x{N}x{K} {path} {odt}")
+
+
 def test_gemm_zero_extent():
     case = inputs.make_case(w4.MXFP4, 0, 64, 64, seed=0)
     A, p, s, _ = to_dev(case)
@@ -259,7 +276,7 @@ def test_gemm_zero_extent():
 # ---- determinism and streams --------------------------------------------------------
 
 @pytest.mark.parametrize("fmt,M,N,K", [(w4.INT4_G128, 1, 8192, 3072), (w4.NVFP4, 16, 3072, 8192),
-                                       (w4.MXFP4, 512, 1024, 3072)])
+                                       (w4.INT4_G128, 64, 8192, 3072), (w4.MXFP4, 512, 1024, 3072)])
 def test_deterministic_and_stream(fmt, M, N, K):
     case = inputs.make_case(fmt, M, N, K, seed=9)
     A, p, s, z = to_dev(case)
@@ -274,7 +291,7 @@ def test_deterministic_and_stream(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [(w4.INT4_G128, 1, 4096, 3072), (w4.NVFP4, 16, 1024, 512),
-                                       (w4.MXFP4, 300, 512, 256)])
+                                       (w4.NVFP4, 64, 1024, 512), (w4.MXFP4, 300, 512, 256)])
 def test_hip_graph_capture_replay(fmt, M, N, K):
     """The C ABI call is capturable: replays of a captured graph, with eager
     work and synchronisations between them, match the eager result."""

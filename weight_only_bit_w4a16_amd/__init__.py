@@ -24,8 +24,8 @@ INT4_G128, NVFP4, MXFP4 = 0, 1, 2
 GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32}
 FORMAT_NAMES = {INT4_G128: "int4_g128", NVFP4: "nvfp4", MXFP4: "mxfp4"}
 OUT_BF16, OUT_F32 = 0x000, 0x100
-PATH_AUTO, PATH_SKINNY, PATH_TILED = 0x0000, 0x1000, 0x2000
-PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "tiled": PATH_TILED}
+PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_MID = 0x0000, 0x1000, 0x2000, 0x3000
+PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "mid": PATH_MID, "tiled": PATH_TILED}
 
 OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP, ERR_EPILOGUE = 0, -1, -2, -3, -4, -5, -6
 MAX_GROUP = 8  # members of one w4a16_gemm_grouped call
@@ -95,7 +95,7 @@ def gemm_path(fmt: int, M: int, N: int, K: int, path: str = "auto") -> str:
     rc = load_library().w4a16_gemm_path(int(fmt) | PATHS[path], M, N, K)
     if rc < 0:
         raise W4A16Error(rc, "w4a16_gemm_path")
-    return "skinny" if rc == PATH_SKINNY else "tiled"
+    return {PATH_SKINNY: "skinny", PATH_MID: "mid", PATH_TILED: "tiled"}[rc]
 
 
 # ---- argument checks (host side, before any pointer reaches the library) ----

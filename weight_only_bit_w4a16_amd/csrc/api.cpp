@@ -22,7 +22,6 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
   if (fmt > W4A16_MXFP4) return W4A16_ERR_FORMAT;
   if (allow_flags) {
     if (flags & ~(W4A16_OUT_F32 | W4A16_PATH_MASK)) return W4A16_ERR_FORMAT;
-    if ((flags & W4A16_PATH_MASK) == W4A16_PATH_MASK) return W4A16_ERR_FORMAT;
   } else if (flags) {
     return W4A16_ERR_FORMAT;
   }
@@ -32,25 +31,40 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
   return W4A16_OK;
 }
 
-// The skinny kernel reads the weights once per 16-row slice of A; the tiled
-// kernel reads them once per 256-row tile but runs the whole of K inside each
-// 256 x 256 tile.  With fewer tiles than CUs the tiled kernel leaves CUs idle
-// and spends its MFMA work on padding rows, so the skinny kernel is faster up
-// to M ~ 200 (measured at N = 8192, K = 3072: M = 64 29 us vs 97 us; M = 192
-// 81 vs 101; M = 256 106 vs 103).  N: the widest matrix of the launch.
+// The skinny kernel reads and decodes the weights once per 16-row slice of
+// A; the mid kernel once per tile of up to 64 rows, but each of its
+// workgroups (32 columns) reads all of A through its CU's L1, which caps a
+// workgroup at ~15 us for 64 rows x K = 3072 however few run; the tiled
+// kernel runs the whole of K inside each 256 x 256 tile and leaves CUs idle
+// when its tiles number fewer than the CUs.  Measured (us, K = 3072 unless
+// noted): N = 8192, M = 64: skinny 30, mid 17, tiled 97; M = 384: 162 / 88 /
+// 104; N = 1024, M = 64: 4.8 / 15 / 96; N = 3072, K = 8192, M = 64: 23 / 36 /
+// 250, M = 128: 42 / 38 / 253; N = 128256, M = 32: 242 / 144 / 219, M = 64:
+// 445 / 242 / 225.  So: the mid kernel when it has >= 160 workgroups (and
+// at most 384 rows while the tiled grid is small; at most 48 rows when it is
+// not), else the skinny kernel below 385 rows.  N: the widest matrix.
 int choose_path(int format, int64_t M, int64_t N) {
   const int forced = format & W4A16_PATH_MASK;
   if (forced) return forced;
   if (M <= 16) return W4A16_PATH_SKINNY;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  return M <= 192 && tiles < 256 ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
+  const int64_t mid_wgs = ((N + 31) / 32) * ((M + 63) / 64);
+  if (tiles >= 256) return M <= 48 ? W4A16_PATH_MID : W4A16_PATH_TILED;
+  if (M > 384) return W4A16_PATH_TILED;
+  return mid_wgs >= 160 ? W4A16_PATH_MID : W4A16_PATH_SKINNY;
+}
+
+hipError_t launch_path(int path, const w4a16::GemmArgs& a) {
+  if (path == W4A16_PATH_SKINNY) return w4a16::launch_skinny(a);
+  if (path == W4A16_PATH_MID) return w4a16::launch_mid(a);
+  return w4a16::launch_tiled(a);
 }
 
 }  // namespace
 
 extern "C" {
 
-int w4a16_version(void) { return 102; }
+int w4a16_version(void) { return 103; }
 
 const char* w4a16_strerror(int status) {
   switch (status) {
@@ -128,9 +142,7 @@ int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* sca
   a.N = N;
   a.K = K;
   a.stream = static_cast<hipStream_t>(stream);
-  const hipError_t e = choose_path(format, M, N) == W4A16_PATH_SKINNY ? w4a16::launch_skinny(a)
-                                                                   : w4a16::launch_tiled(a);
-  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+  return launch_path(choose_path(format, M, N), a) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
 int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* packed,
@@ -161,7 +173,8 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
 
   int64_t max_n = 0;
   for (int i = 0; i < count; ++i) max_n = N[i] > max_n ? N[i] : max_n;
-  if (choose_path(format, M, max_n) == W4A16_PATH_SKINNY) {
+  const int path = choose_path(format, M, max_n);
+  if (path == W4A16_PATH_SKINNY) {
     w4a16::GroupedArgs g = {};
     g.fmt = fmt;
     g.out_f32 = out_f32;
@@ -180,7 +193,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     g.stream = static_cast<hipStream_t>(stream);
     return w4a16::launch_skinny_grouped(g) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
   }
-  // large M: one tiled launch per member (each already fills the GPU)
+  // larger M: one mid or tiled launch per member
   for (int i = 0; i < count; ++i) {
     if (N[i] == 0) continue;
     w4a16::GemmArgs a;
@@ -196,7 +209,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     a.N = N[i];
     a.K = K;
     a.stream = static_cast<hipStream_t>(stream);
-    if (w4a16::launch_tiled(a) != hipSuccess) return W4A16_ERR_HIP;
+    if (launch_path(path, a) != hipSuccess) return W4A16_ERR_HIP;
   }
   return W4A16_OK;
 }

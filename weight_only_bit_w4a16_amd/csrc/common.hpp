@@ -204,29 +204,24 @@ __device__ __forceinline__ float ubyte_f32(uint32_t x) {
 
 // ---- int4 decoders -------------------------------------------------------------
 
-// bitfield insert: (mask & a) | (~mask & b) in one instruction (the compiler
-// otherwise splits this into two, since gfx9 VOP3 cannot take two literals)
-__device__ __forceinline__ uint32_t bfi_b32(uint32_t mask, uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
-  return r;
-}
-
-// 8 int4 codes (one dword, code k in nibble k) to bf16 (128 + code), in k
-// order: bf16 0x43nn is 128 + nn for nn < 128, so placing each nibble in the
-// low byte of a 0x43 high byte encodes the offset code exactly.  Nine VALU
-// operations per 8 codes: one shift, then per output dword a byte permute
-// (packed byte i and its copy shifted right by 4) and a bitfield insert of
-// the two nibbles into 0x43004300.
-__device__ __forceinline__ u32x4_t int4x8_to_bf16_offset128(uint32_t q) {
-  const uint32_t s = q >> 4;
-  const uint32_t c43 = 0x43004300u;
+// 8 int4 codes (one dword, code k in nibble k) to their exact bf16 values in
+// natural k order.  The even-k and odd-k nibbles are masked into bytes, two
+// byte permutes put them back in k order (k0 k1 k2 k3 | k4 k5 k6 k7), and
+// each byte, read as the e4m3 value code * 2^-9, is converted with a scale of
+// 2^9, exactly, two codes per instruction: nine VALU operations per 8 codes.
+// Only compiler-visible instructions: a VALU write hidden in inline assembly
+// escapes the compiler's hazard checks, and an MFMA reading its result too
+// soon afterwards sees the register's old value.
+__device__ __forceinline__ u32x4_t int4x8_to_bf16_natural(uint32_t q) {
+  const uint32_t lo = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
+  const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+  const uint32_t p0 = perm_b32(hi, lo, 0x05010400u);  // bytes k0 k1 k2 k3
+  const uint32_t p1 = perm_b32(hi, lo, 0x07030602u);  // bytes k4 k5 k6 k7
   u32x4_t r;
-  // byte 0 = low nibble of packed byte i (even k), byte 2 = its high nibble
-  r[0] = bfi_b32(0x000F000Fu, perm_b32(s, q, 0x0c040c00u), c43);
-  r[1] = bfi_b32(0x000F000Fu, perm_b32(s, q, 0x0c050c01u), c43);
-  r[2] = bfi_b32(0x000F000Fu, perm_b32(s, q, 0x0c060c02u), c43);
-  r[3] = bfi_b32(0x000F000Fu, perm_b32(s, q, 0x0c070c03u), c43);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p0, 512.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p0, 512.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p1, 512.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p1, 512.0f, true));
   return r;
 }
 
@@ -257,17 +252,10 @@ __device__ __forceinline__ u32x4_t bf16x8_even_odd(u32x4_t a) {
   return r;
 }
 
-// bf16 -z broadcast to 8 lanes' worth (exact for z <= 256).
+// bf16 -z broadcast to 8 lanes' worth (exact for every zero byte, z <= 255).
 __device__ __forceinline__ u32x4_t int4_neg_zero(uint32_t z) {
   const uint32_t h = __float_as_uint(-(float)z) >> 16;
   const uint32_t d = h | (h << 16);
-  return u32x4_t{d, d, d, d};
-}
-
-// bf16 -(128 + z), broadcast to 8 lanes' worth (exact for z <= 127).
-__device__ __forceinline__ u32x4_t int4_neg_offset_zero(uint32_t z) {
-  uint32_t h = 0xC300u | z;
-  uint32_t d = h | (h << 16);
   return u32x4_t{d, d, d, d};
 }
 

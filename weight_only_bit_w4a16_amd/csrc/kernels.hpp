@@ -59,6 +59,10 @@ hipError_t launch_skinny(const GemmArgs& a);
 // the same kernel over all members of a group in one launch
 hipError_t launch_skinny_grouped(const GroupedArgs& a);
 
+// 16 < M <= ~192: 32-column x 32..64-row tiles, split-K over the waves of a
+// workgroup, each weight decoded once for all of the tile's rows.
+hipError_t launch_mid(const GemmArgs& a);
+
 // large M: LDS-staged tiles, decode into MFMA B fragments.
 hipError_t launch_tiled(const GemmArgs& a);
 

@@ -1,0 +1,371 @@
+// mid.hip -- W4A16 GEMM for a middle number of activation rows (about 16 < M
+// <= 192): tiles of 32 output columns x 16*MS rows (MS = 2, 3 or 4).
+//
+// At decode-batch sizes the tiled kernel's 256 x 256 tiles leave most CUs idle
+// (N / 256 of them) and spend their MFMA work on padding rows, while the
+// skinny kernel handles 16 rows at a time and so loads and decodes every
+// weight once per 16-row slice.  Here a workgroup covers 32 weight rows (two
+// 16-column slices) and MS 16-row slices of A: each weight is loaded and
+// decoded once and feeds MS MFMA chains.  The waves split K (U 128-code
+// k-blocks per wave and pass) and meet in LDS for a fixed-order sum.
+//
+//   * weights: lane l owns row 16h + l%16 of column slice h (h = 0, 1) and
+//     chunk l/16 (32 codes) of each k-block: one 16-byte load per lane, slice
+//     and k-block, the same operand layout as the skinny kernel;
+//   * A: the lane supplies row 16s + l%16 of row slice s over the same 32 k,
+//     loaded straight from memory (A is small and read once per workgroup, so
+//     it is served from L2);
+//   * int4: codes decode exactly in natural k order, and a second MFMA per
+//     step with the constant -zero fills a second accumulator with the same
+//     rounding sequence, so a k-block whose codes all equal the zero point
+//     cancels to exactly 0; the group scale multiplies once per k-block.
+//     fp4: the scale is applied exactly in the decode;
+//   * scales (and zeros) of the workgroup's 32 rows are one contiguous block:
+//     copied once to LDS with coalesced dword loads when it fits the staging
+//     registers (S_LDS), else each lane loads its own with its weights.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kMidMaxWaves = 12;
+constexpr int kMidCols = 32;   // output columns (weight rows) per workgroup
+constexpr int kMidSStage = 4;  // staged scale / zero dwords per thread, at most
+
+template <int FMT>
+constexpr int mid_sb() { return FMT == kInt4 ? 2 : 1; }  // scale bytes
+
+// scale (zero) window capacity in bytes: 32 rows plus the <= 3-byte lead of
+// the dword-aligned start and the <= 3-byte tail of its last dword
+__host__ __device__ constexpr uint32_t mid_cap(uint32_t bytes) { return (bytes + 6u + 15u) & ~15u; }
+
+template <int FMT, bool OUT_F32, int U, int MS, bool S_LDS>
+__global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* __restrict__ A,
+                                                               const uint8_t* __restrict__ packed,
+                                                               const void* __restrict__ scales,
+                                                               const uint8_t* __restrict__ zeros,
+                                                               void* __restrict__ C, int M, int N, int K,
+                                                               Epilogue epi) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int waves = blockDim.x >> 6;
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = (int)blockIdx.x * kMidCols;
+  const int m0 = (int)blockIdx.y * 16 * MS;
+  const int KC = K >> 5;          // 32-code chunks (K % 32 == 0)
+  const int KB = (KC + 3) >> 2;   // k-blocks, the last one possibly partial
+  constexpr int G = FormatTraits<FMT>::kGroup;
+  constexpr int SB = mid_sb<FMT>();
+  const int groups = K / G;
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const int rows = min(kMidCols, N - n0);
+  const int arows = min(16 * MS, M - m0);
+  const uint32_t wave_slot0 = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64u;
+  const int kw = __builtin_amdgcn_readfirstlane(wave) * U;
+
+  const uint32_t s_cap = S_LDS ? mid_cap((uint32_t)(kMidCols * groups * SB)) : 0u;
+  const uint32_t z_cap = S_LDS && FMT == kInt4 ? mid_cap((uint32_t)(kMidCols * groups)) : 0u;
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + s_cap + z_cap);  // [waves][MS * 2][64]
+
+  const uint8_t* s_base = reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB;
+  const uint8_t* z_base = FMT == kInt4 ? zeros + (int64_t)n0 * groups : nullptr;
+  // S_LDS: the windows' dwords, read from the 4-byte aligned address at or
+  // below each block (at most 3 bytes past its end, in the same dword)
+  uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
+  uint32_t sst[kMidSStage], zst[kMidSStage];
+  // direct: per-lane scale / zero loads over the same blocks
+  rsrc_t sr, zr;
+  if constexpr (S_LDS) {
+    auto window = [&](const uint8_t* start, uint32_t bytes, uint32_t& delta, uint32_t& words) {
+      const uintptr_t al = reinterpret_cast<uintptr_t>(start) & ~(uintptr_t)3;
+      delta = (uint32_t)(reinterpret_cast<uintptr_t>(start) - al);
+      words = (delta + bytes + 3u) / 4u;
+      return make_rsrc(reinterpret_cast<const void*>(al), words * 4u);
+    };
+    const rsrc_t ss = window(s_base, (uint32_t)(rows * groups * SB), s_delta, s_words);
+#pragma unroll
+    for (int i = 0; i < kMidSStage; ++i) {
+      const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+      sst[i] = wave_slot0 + i * blockDim.x < s_words ? buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB) : 0u;
+    }
+    if constexpr (FMT == kInt4) {
+      const rsrc_t zs = window(z_base, (uint32_t)(rows * groups), z_delta, z_words);
+#pragma unroll
+      for (int i = 0; i < kMidSStage; ++i) {
+        const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+        zst[i] = wave_slot0 + i * blockDim.x < z_words ? buf_load_b32(zs, w < z_words ? w * 4u : kBufferOOB) : 0u;
+      }
+    }
+  } else {
+    sr = make_rsrc(s_base, (uint32_t)(rows * groups * SB));
+    if constexpr (FMT == kInt4) zr = make_rsrc(z_base, (uint32_t)(rows * groups));
+  }
+
+  // weight rows past N, A rows past M and chunks past K read as 0
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
+
+  f32x4_t acc[MS][2];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) acc[s][0] = acc[s][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t q[U][2];
+  uint32_t sraw[U][2], zraw[U][2];
+
+  // weights (and, direct, their scales) of one pass, issued together; every
+  // load is issued (out of range past K), so no branch splits the waits
+  auto issue = [&](int kbase) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kbase + u;
+      const int c = kb * 4 + g;
+      const bool ok = c < KC;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t r = (uint32_t)(16 * h + nl);
+        q[u][h] = buf_load_b128(wr, ok ? r * rowb + (uint32_t)c * 16u : kBufferOOB);
+        if constexpr (!S_LDS) {
+          if constexpr (FMT == kInt4) {
+            const uint32_t gi = r * (uint32_t)groups + (uint32_t)kb;
+            sraw[u][h] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
+            zraw[u][h] = buf_load_b8(zr, ok ? gi : kBufferOOB);
+          } else if constexpr (FMT == kNvfp4) {
+            sraw[u][h] = buf_load_b16(sr, ok ? r * (uint32_t)groups + 2u * (uint32_t)c : kBufferOOB);
+          } else {
+            sraw[u][h] = buf_load_b8(sr, ok ? r * (uint32_t)groups + (uint32_t)c : kBufferOOB);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const uint8_t* sb = lds + s_delta;
+  const uint8_t* zb = lds + s_cap + z_delta;
+  auto compute = [&](int kbase) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kbase + u;
+      if (kb >= KB) break;  // wave-uniform
+      const int c = kb * 4 + g;
+      const bool ok = c < KC;
+      const int cc = ok ? c : 0;  // LDS reads stay inside the window
+      // both column slices decoded once, to bf16 MFMA operands
+      u32x4_t b[2][4];
+      float sc[2];
+      u32x4_t nz[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 16 * h + nl;
+        if constexpr (FMT == kInt4) {
+          const int gi = r * groups + kb;
+          uint32_t sbits, z;
+          if constexpr (S_LDS) {
+            sbits = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
+            z = zb[gi];
+          } else {
+            sbits = sraw[u][h];
+            z = zraw[u][h];
+          }
+          sc[h] = bf16_bits_to_f32(sbits);
+          nz[h] = int4_neg_zero(z);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_natural(q[u][h][j]);
+        } else if constexpr (FMT == kNvfp4) {
+          const uint32_t s2 = S_LDS ? *reinterpret_cast<const uint16_t*>(sb + r * groups + 2 * cc) : sraw[u][h];
+          const float s0 = e4m3_magnitude(s2 & 0xFFu), s1 = e4m3_magnitude(s2 >> 8);
+          b[h][0] = fp4x8_to_bf16_fscale(q[u][h][0], s0);
+          b[h][1] = fp4x8_to_bf16_fscale(q[u][h][1], s0);
+          b[h][2] = fp4x8_to_bf16_fscale(q[u][h][2], s1);
+          b[h][3] = fp4x8_to_bf16_fscale(q[u][h][3], s1);
+        } else {
+          const float es = e8m0_as_exponent_scale(S_LDS ? (uint32_t)sb[r * groups + cc] : sraw[u][h]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[h][j] = fp4x8_to_bf16_escale(q[u][h][j], es);
+        }
+      }
+      // every row slice of A meets both decoded column slices
+#pragma unroll
+      for (int s = 0; s < MS; ++s) {
+        const uint32_t off = ((uint32_t)(16 * s + nl) * (uint32_t)K + (uint32_t)c * 32u) * 2u;
+        u32x4_t a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = buf_load_b128(ar, ok ? off + 16u * j : kBufferOOB);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if constexpr (FMT == kInt4) {
+            f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              dp = mfma16x16x32(a[j], b[h][j], dp);
+              dn = mfma16x16x32(a[j], nz[h], dn);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[s][h][i] = __builtin_fmaf(sc[h], dp[i] + dn[i], acc[s][h][i]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[s][h] = mfma16x16x32(a[j], b[h][j], acc[s][h]);
+          }
+        }
+      }
+    }
+  };
+
+  int kbase = kw;
+  issue(kbase);
+  if constexpr (S_LDS) {
+    // scales to LDS; an LDS-only barrier leaves the weights in flight
+#pragma unroll
+    for (int i = 0; i < kMidSStage; ++i) {
+      const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
+      if (w < s_words) reinterpret_cast<uint32_t*>(lds)[w] = sst[i];
+      if constexpr (FMT == kInt4) {
+        if (w < z_words) reinterpret_cast<uint32_t*>(lds + s_cap)[w] = zst[i];
+      }
+    }
+    lds_barrier();
+  }
+  compute(kbase);
+  for (kbase += waves * U; kbase < KB; kbase += waves * U) {
+    issue(kbase);
+    compute(kbase);
+  }
+
+  // ---- split-K sum over the waves through LDS: output block p = (row slice
+  // s, column slice h) is summed in wave order and stored by wave p % waves ----
+  constexpr int P = MS * 2;
+#pragma unroll
+  for (int s = 0; s < MS; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) red[(wave * P + s * 2 + h) * 64 + lane] = acc[s][h];
+  lds_barrier();
+  for (int p = wave; p < P; p += waves) {
+    const int s = p >> 1, h = p & 1;
+    const int n = n0 + 16 * h + nl;
+    const bool col_ok = 16 * h + nl < rows;
+    // epilogue operands first, in one round trip (the residual may alias C)
+    float eb = 0.f, er[4] = {0.f, 0.f, 0.f, 0.f};
+    if (epi.on && col_ok) {
+      if (epi.bias) eb = bf16_bits_to_f32(epi.bias[n]);
+      if (epi.res) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 16 * s + 4 * g + i;
+          if (m < M) er[i] = residual_at<OUT_F32>(epi.res, (int64_t)m * N + n);
+        }
+      }
+    }
+    f32x4_t sum = red[p * 64 + lane];
+    for (int w = 1; w < waves; ++w) {
+      const f32x4_t v = red[(w * P + p) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += v[i];
+    }
+    if (!col_ok) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 16 * s + 4 * g + i;
+      if (m < M) {
+        const int64_t mn = (int64_t)m * N + n;
+        const float v = epi.on ? epilogue_value(epi, sum[i], eb, er[i]) : sum[i];
+        if constexpr (OUT_F32) {
+          reinterpret_cast<float*>(C)[mn] = v;
+        } else {
+          reinterpret_cast<__bf16*>(C)[mn] = (__bf16)v;
+        }
+      }
+    }
+  }
+}
+
+// launch shape of one call: k-blocks per wave and pass, waves, row slices
+struct MidPlan {
+  int U, waves, MS;
+  bool s_lds;
+  unsigned lds;
+};
+
+MidPlan mid_plan(int fmt, int64_t M, int64_t K) {
+  MidPlan p;
+  const int KB = (int)((K / 32 + 3) / 4);
+  // 2 k-blocks per wave while K fits the waves that way, else 4; passes over
+  // K balanced so every wave gets the same number of k-blocks, within one
+  p.U = (KB + 1) / 2 <= kMidMaxWaves ? 2 : 4;
+  const int per_pass = kMidMaxWaves * p.U;
+  const int passes = (KB + per_pass - 1) / per_pass;
+  p.waves = (KB + p.U * passes - 1) / (p.U * passes);
+  // rows: as few 64-row tiles as cover M, then as few 16-row slices per tile
+  const int64_t slices = (M + 15) / 16;
+  const int64_t row_tiles = (slices + 3) / 4;
+  p.MS = (int)((slices + row_tiles - 1) / row_tiles);
+  if (p.MS < 2) p.MS = 2;
+  // scale windows in LDS when every dword has a staging register
+  const int64_t groups = K / (fmt == 0 ? 128 : fmt == 1 ? 16 : 32);
+  const int64_t sb = fmt == 0 ? 2 : 1;
+  const int64_t slots = (int64_t)kMidSStage * 64 * p.waves;
+  const int64_t s_cap = mid_cap((uint32_t)(kMidCols * groups * sb));
+  const int64_t z_cap = fmt == 0 ? mid_cap((uint32_t)(kMidCols * groups)) : 0;
+  const int64_t red = (int64_t)p.waves * p.MS * 2 * 1024;
+  p.s_lds = s_cap / 4 <= slots && z_cap / 4 <= slots && s_cap + z_cap + red <= 160 * 1024;
+  p.lds = (unsigned)((p.s_lds ? s_cap + z_cap : 0) + red);
+  return p;
+}
+
+// row tiles go along grid y, at most 65535 per launch: taller A is split
+// into launches over consecutive row ranges (offset A, C and the residual)
+template <int FMT, bool OUT_F32, int U, int MS, bool S_LDS>
+hipError_t launch_v(const GemmArgs& a, const MidPlan& p) {
+  const int64_t chunk = (int64_t)65535 * 16 * MS;
+  const int64_t es = OUT_F32 ? 4 : 2;
+  for (int64_t m = 0; m < a.M; m += chunk) {
+    const int64_t rows = a.M - m < chunk ? a.M - m : chunk;
+    const dim3 grid((unsigned)((a.N + kMidCols - 1) / kMidCols), (unsigned)((rows + 16 * MS - 1) / (16 * MS)));
+    Epilogue epi = a.epi;
+    if (epi.res) epi.res = static_cast<const uint8_t*>(epi.res) + m * a.N * es;
+    hipLaunchKernelGGL((mid_kernel<FMT, OUT_F32, U, MS, S_LDS>), grid, dim3(64 * p.waves), p.lds, a.stream,
+                       a.A + m * a.K, a.packed, a.scales, a.zeros, static_cast<uint8_t*>(a.C) + m * a.N * es,
+                       (int)rows, (int)a.N, (int)a.K, epi);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int FMT, bool OUT_F32, int U, int MS>
+hipError_t launch_s(const GemmArgs& a, const MidPlan& p) {
+  return p.s_lds ? launch_v<FMT, OUT_F32, U, MS, true>(a, p) : launch_v<FMT, OUT_F32, U, MS, false>(a, p);
+}
+
+template <int FMT, bool OUT_F32, int U>
+hipError_t launch_m(const GemmArgs& a, const MidPlan& p) {
+  if (p.MS == 2) return launch_s<FMT, OUT_F32, U, 2>(a, p);
+  if (p.MS == 3) return launch_s<FMT, OUT_F32, U, 3>(a, p);
+  return launch_s<FMT, OUT_F32, U, 4>(a, p);
+}
+
+template <int FMT, bool OUT_F32>
+hipError_t launch_fmt(const GemmArgs& a) {
+  const MidPlan p = mid_plan(FMT, a.M, a.K);
+  return p.U == 2 ? launch_m<FMT, OUT_F32, 2>(a, p) : launch_m<FMT, OUT_F32, 4>(a, p);
+}
+
+}  // namespace
+
+hipError_t launch_mid(const GemmArgs& a) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  switch (a.fmt * 2 + (a.out_f32 ? 1 : 0)) {
+    case 0: return launch_fmt<kInt4, false>(a);
+    case 1: return launch_fmt<kInt4, true>(a);
+    case 2: return launch_fmt<kNvfp4, false>(a);
+    case 3: return launch_fmt<kNvfp4, true>(a);
+    case 4: return launch_fmt<kMxfp4, false>(a);
+    default: return launch_fmt<kMxfp4, true>(a);
+  }
+}
+
+}  // namespace w4a16

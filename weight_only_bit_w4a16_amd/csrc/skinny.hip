@@ -16,12 +16,12 @@
 //   * partial sums of the W waves are added through LDS at the end (split-K
 //     inside the workgroup: no workspace, no atomics, deterministic).
 // Decode per format:
-//   * int4: codes become exact bf16 values -- the codes themselves through the
-//     scaled fp8 converter when A sits in LDS (A is stored in the decoder's
-//     k order), else 128 + code by byte assembly; a second MFMA per step with
-//     the constant -zero (or -(128 + zero)) fills a second accumulator; their
-//     sum is sum_k a_k (code_k - zero), which the group scale multiplies once
-//     per k-block (k-block = int4 group);
+//   * int4: the codes become exact bf16 values through the scaled fp8
+//     converter -- in even / odd k order when A sits in LDS (A is stored in
+//     that order), else in natural k order; a second MFMA per step with the
+//     constant -zero fills a second accumulator; their sum is
+//     sum_k a_k (code_k - zero), which the group scale multiplies once per
+//     k-block (k-block = int4 group);
 //   * NVFP4: e2m1 -> fp32, times |e4m3 scale| (exact), -> bf16 (exact);
 //   * MXFP4: hardware e2m1 conversion scaled by 2^(E-127) (exact).
 #include <stdlib.h>
@@ -287,18 +287,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
         }
       }
       if constexpr (FMT == kInt4) {
-        // the +code (or +(128 + code)) and -zero (or -(128 + zero)) products
-        // go to separate accumulators that follow the same rounding
-        // sequence, so a k-block whose codes all equal the zero point cancels
-        // to exactly 0.  With A in LDS (already in the decoder's k order) the
-        // codes convert exactly without an offset; otherwise the offset-128
-        // encoding keeps A in its natural order.
-        const u32x4_t nz = A_LDS ? int4_neg_zero(zraw[u]) : int4_neg_offset_zero(zraw[u]);
+        // the +code and -zero products go to separate accumulators that
+        // follow the same rounding sequence, so a k-block whose codes all
+        // equal the zero point cancels to exactly 0.  With A in LDS (already
+        // in the even / odd k order of the shorter decode) the codes convert
+        // in that order; otherwise in natural k order, like A.
+        const u32x4_t nz = int4_neg_zero(zraw[u]);
         f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
         f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x4_t b = A_LDS ? int4x8_to_bf16_exact(q[u][j]) : int4x8_to_bf16_offset128(q[u][j]);
+          const u32x4_t b = A_LDS ? int4x8_to_bf16_exact(q[u][j]) : int4x8_to_bf16_natural(q[u][j]);
           dp = mfma16x16x32(a[u][j], b, dp);
           dn = mfma16x16x32(a[u][j], nz, dn);
         }
