@@ -68,16 +68,20 @@ def test_version_and_strerror():
 def test_path_choice():
     assert w4.gemm_path(w4.INT4_G128, 1, 8192, 3072) == "skinny"
     assert w4.gemm_path(w4.NVFP4, 16, 3072, 8192) == "skinny"
-    # 17 <= M <= 384 with a small tiled grid: the mid kernel when it has >= 160
-    # workgroups of 32 columns x 64 rows, else the skinny kernel
+    # a small tiled grid: the mid kernel (workgroups of 32 columns x 64 rows)
+    # while it has >= 160 workgroups in at most 2 rounds of 256 (3 for int4),
+    # the skinny kernel below 160 workgroups, else the tiled kernel
     assert w4.gemm_path(w4.MXFP4, 17, 64, 64) == "skinny"
     assert w4.gemm_path(w4.INT4_G128, 64, 1024, 3072) == "skinny"
     assert w4.gemm_path(w4.NVFP4, 64, 3072, 8192) == "skinny"        # 96 workgroups
     assert w4.gemm_path(w4.NVFP4, 65, 3072, 8192) == "mid"           # 192
     assert w4.gemm_path(w4.INT4_G128, 17, 5120, 3072) == "mid"       # 160
-    assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "mid"
-    assert w4.gemm_path(w4.INT4_G128, 384, 8192, 3072) == "mid"
-    assert w4.gemm_path(w4.INT4_G128, 385, 8192, 3072) == "tiled"
+    assert w4.gemm_path(w4.MXFP4, 128, 8192, 3072) == "mid"          # 2 rounds
+    assert w4.gemm_path(w4.MXFP4, 129, 8192, 3072) == "tiled"        # 3 rounds
+    assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "mid"      # 3 rounds
+    assert w4.gemm_path(w4.INT4_G128, 193, 8192, 3072) == "tiled"
+    assert w4.gemm_path(w4.INT4_G128, 384, 1024, 3072) == "mid"      # 192 workgroups
+    assert w4.gemm_path(w4.INT4_G128, 400, 512, 3072) == "tiled"
     # a large tiled grid (>= 256 tiles): the mid kernel up to 48 rows
     assert w4.gemm_path(w4.INT4_G128, 48, 65536, 3072) == "mid"
     assert w4.gemm_path(w4.INT4_G128, 49, 65536, 3072) == "tiled"

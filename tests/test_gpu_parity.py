@@ -230,6 +230,22 @@ def test_gemm_ragged(fmt, M, N, K, path):
         check_gate(C, Cref, S, odt == torch.bfloat16, f"ragged {fmt} {M}x{N}x{K} {path} {odt}")
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [(w4.NVFP4, 2050, 6150, 96), (w4.INT4_G128, 1999, 6200, 256),
+                                       (w4.MXFP4, 4100, 3000, 160)])
+def test_gemm_large_tiles_ragged_sampled(fmt, M, N, K):
+    """The tiled kernel's 256 x 256 tiles (chosen from 192 of them up) with
+    every dimension ragged; 4096 sampled outputs plus the four corners."""
+    assert w4.gemm_path(fmt, M, N, K) == "tiled"
+    case = inputs.make_case(fmt, M, N, K, seed=M + N + K)
+    C = run_gemm(case, torch.bfloat16, "auto")
+    rng = np.random.default_rng(M)
+    mi = np.concatenate([rng.integers(0, M, 4096), [0, 0, M - 1, M - 1]])
+    ni = np.concatenate([rng.integers(0, N, 4096), [0, N - 1, 0, N - 1]])
+    Cref, S = oracle.gemm_at(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K, mi, ni)
+    check_gate(C[mi, ni], Cref, S, True, f"large tiles {fmt} {M}x{N}x{K}")
+    assert np.all(np.isfinite(C))
+
+
 @pytest.mark.parametrize("path", ["skinny", "mid", "tiled"])
 def test_gemm_degenerate(path):
     # every int4 code equal to its zero point -> exactly 0

@@ -33,25 +33,29 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
 
 // The skinny kernel reads and decodes the weights once per 16-row slice of
 // A; the mid kernel once per tile of up to 64 rows, but each of its
-// workgroups (32 columns) reads all of A through its CU's L1, which caps a
-// workgroup at ~15 us for 64 rows x K = 3072 however few run; the tiled
-// kernel runs the whole of K inside each 256 x 256 tile and leaves CUs idle
-// when its tiles number fewer than the CUs.  Measured (us, K = 3072 unless
-// noted): N = 8192, M = 64: skinny 30, mid 17, tiled 97; M = 384: 162 / 88 /
-// 104; N = 1024, M = 64: 4.8 / 15 / 96; N = 3072, K = 8192, M = 64: 23 / 36 /
-// 250, M = 128: 42 / 38 / 253; N = 128256, M = 32: 242 / 144 / 219, M = 64:
-// 445 / 242 / 225.  So: the mid kernel when it has >= 160 workgroups (and
-// at most 384 rows while the tiled grid is small; at most 48 rows when it is
-// not), else the skinny kernel below 385 rows.  N: the widest matrix.
+// workgroups (32 columns) reads all of A through its CU, which sets a
+// workgroup's time (~15 us at 64 rows, K = 3072) however many run; the tiled
+// kernel (256 x 256 tiles, or 128 x 128 when the large ones would leave CUs
+// idle) runs the whole of K inside each tile, and with few tiles its time is
+// one tile's k-loop (~33 us MXFP4, ~53 us int4 at K = 3072).  So, measured
+// (us at N = 8192, K = 3072: M = 64 skinny 29 / mid 17 / tiled 30 (MXFP4);
+// M = 192 int4 83 / 46 / 53, MXFP4 70 / 46 / 33; M = 384 int4 162 / 88 / 56):
+// the mid kernel while it runs in at most 2 rounds of 256 workgroups (3 for
+// int4, whose tiled decode is dearer) and has >= 160 of them; the skinny
+// kernel when it would have fewer (narrow matrices: N = 1024, M = 64: 4.8 /
+// 15 / 51); with 256 or more large tiles the tiled kernel, except at M <= 48
+// (LM head 128256 x 3072, M = 32: 242 / 144 / 219).  N: the widest matrix.
 int choose_path(int format, int64_t M, int64_t N) {
   const int forced = format & W4A16_PATH_MASK;
   if (forced) return forced;
   if (M <= 16) return W4A16_PATH_SKINNY;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t mid_wgs = ((N + 31) / 32) * ((M + 63) / 64);
   if (tiles >= 256) return M <= 48 ? W4A16_PATH_MID : W4A16_PATH_TILED;
-  if (M > 384) return W4A16_PATH_TILED;
-  return mid_wgs >= 160 ? W4A16_PATH_MID : W4A16_PATH_SKINNY;
+  const int64_t mid_wgs = ((N + 31) / 32) * ((M + 63) / 64);
+  if (mid_wgs < 160) return M <= 384 ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
+  const int64_t rounds = (mid_wgs + 255) / 256;
+  const int max_rounds = (format & W4A16_FORMAT_MASK) == W4A16_INT4_G128 ? 3 : 2;
+  return rounds <= max_rounds ? W4A16_PATH_MID : W4A16_PATH_TILED;
 }
 
 hipError_t launch_path(int path, const w4a16::GemmArgs& a) {

@@ -487,10 +487,15 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   }
 }
 
-// the tile configuration: 256 x 256, waves 2 (M) x 4 (N), wave tile 128 x 64
+// The tile configurations.  256 x 256, waves 2 (M) x 4 (N), wave tile 128 x 64
 // (64 x 128 wave tiles halve the A-fragment reads but double the decode, and
-// 128 x 128 wave tiles leave one wave per SIMD: both measured slower)
+// 128 x 128 wave tiles leave one wave per SIMD: both measured slower).  With
+// fewer than 192 such tiles most CUs would idle: then 128 x 128 tiles of 4
+// waves (64 x 64 wave tiles), whose time is set by the latency of each
+// wave's k-loop rather than by the MFMA work (deeper copy pipelines measured
+// slower; 128 x 64 and 64 x 128 tiles no faster).
 using Cfg = TileCfg<2, 4, 8, 4>;
+using CfgSmall = TileCfg<2, 2, 4, 4>;
 
 template <int FMT, bool OUT_F32, class CFG>
 hipError_t launch_cfg(const GemmArgs& a) {
@@ -503,6 +508,8 @@ hipError_t launch_cfg(const GemmArgs& a) {
 
 template <int FMT, bool OUT_F32>
 hipError_t launch_fmt(const GemmArgs& a) {
+  const int64_t big_tiles = ((a.N + Cfg::BN - 1) / Cfg::BN) * ((a.M + Cfg::BM - 1) / Cfg::BM);
+  if (big_tiles < 192) return launch_cfg<FMT, OUT_F32, CfgSmall>(a);
   return launch_cfg<FMT, OUT_F32, Cfg>(a);
 }
 
