@@ -196,12 +196,6 @@ __device__ __forceinline__ u32x4_t fp4x8_to_bf16_fscale(uint32_t q, float scale)
   return r;
 }
 
-// byte i of x as an exact fp32 (one v_cvt_f32_ubyte<i>)
-template <int I>
-__device__ __forceinline__ float ubyte_f32(uint32_t x) {
-  return (float)((x >> (8 * I)) & 0xFFu);
-}
-
 // ---- int4 decoders -------------------------------------------------------------
 
 // 8 int4 codes (one dword, code k in nibble k) to their exact bf16 values in
@@ -262,19 +256,21 @@ __device__ __forceinline__ u32x4_t int4_neg_zero(uint32_t z) {
 // 8 int4 codes to bf16 weights (code - zero) * scale, each rounded once to
 // nearest even.  The subtraction comes first, as the format defines it (so a
 // zero weight takes the sign of the scale); both steps are exact in fp32 (at
-// most 12 significant bits), so the only rounding is the final bf16 one.
+// most 17 significant bits), so the only rounding is the final bf16 one.  The
+// codes reach fp32 through the scaled fp8 converter (each masked byte read as
+// the e4m3 value code * 2^-9, scaled by 2^9: exact, two per instruction).
 __device__ __forceinline__ u32x4_t int4x8_to_bf16_weights(uint32_t q, float s, float zf) {
   const uint32_t lo = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
   const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+  const f32x2_t e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, false);  // k0, k2
+  const f32x2_t e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, true);   // k4, k6
+  const f32x2_t o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, false);  // k1, k3
+  const f32x2_t o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, true);   // k5, k7
   u32x4_t r;
-  r[0] = pack_bf16x2((ubyte_f32<0>(lo) - zf) * s,
-                     (ubyte_f32<0>(hi) - zf) * s);
-  r[1] = pack_bf16x2((ubyte_f32<1>(lo) - zf) * s,
-                     (ubyte_f32<1>(hi) - zf) * s);
-  r[2] = pack_bf16x2((ubyte_f32<2>(lo) - zf) * s,
-                     (ubyte_f32<2>(hi) - zf) * s);
-  r[3] = pack_bf16x2((ubyte_f32<3>(lo) - zf) * s,
-                     (ubyte_f32<3>(hi) - zf) * s);
+  r[0] = pack_bf16x2((e0[0] - zf) * s, (o0[0] - zf) * s);
+  r[1] = pack_bf16x2((e0[1] - zf) * s, (o0[1] - zf) * s);
+  r[2] = pack_bf16x2((e1[0] - zf) * s, (o1[0] - zf) * s);
+  r[3] = pack_bf16x2((e1[1] - zf) * s, (o1[1] - zf) * s);
   return r;
 }
 
