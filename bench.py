@@ -44,13 +44,15 @@ WORKLOADS = {
     "mxfp4_m4096": (2, 4096, 8192, 3072, "bf16"),
 }
 CHAIN = "decode_chain_3b_int4_m1"
-GROUP = {0: 128, 1: 16, 2: 32}
+GROUP = {0: 128, 1: 16, 2: 32, 3: 32, 4: 64}   # int4 g128, NVFP4, MXFP4, int4 g32, int4 g64
+INT4_FORMATS = (0, 3, 4)
 
 
 def algorithmic_bytes(fmt, M, N, K, out):
     """Bytes the method must move once: packed + scales (+ zeros) + A + C."""
     G = GROUP[fmt]
-    weight = N * K // 2 + N * (K // G) * (2 if fmt == 0 else 1) + (N * (K // G) if fmt == 0 else 0)
+    int4 = fmt in INT4_FORMATS
+    weight = N * K // 2 + N * (K // G) * (2 if int4 else 1) + (N * (K // G) if int4 else 0)
     io = M * K * 2 + M * N * (4 if out == "f32" else 2)
     return weight, weight + io
 
@@ -150,7 +152,7 @@ def main():
     def to_dev(case):
         A = torch.from_numpy(case.A.view(np.int16)).to(dev).view(torch.bfloat16)
         p = torch.from_numpy(case.packed).to(dev)
-        if case.fmt == 0:
+        if case.fmt in INT4_FORMATS:
             s = torch.from_numpy(case.scales.view(np.int16)).to(dev).view(torch.bfloat16)
             z = torch.from_numpy(case.zeros).to(dev)
         else:

@@ -15,6 +15,9 @@
  *     "The weight format" -- scale bf16 and zero uint8 per 128 contiguous
  *     input elements, value = (code - zero) * scale; the contract's nibble
  *     paragraph -- LOW nibble of byte (n, i) is input 2i, HIGH nibble 2i+1.
+ *     The group is a configuration value there (`group`, 128 in its
+ *     fixture); W4A16_INT4_G32 / _G64 are the same format with groups of 32
+ *     and 64.
  *   - NVFP4: "Matmul2dFp4" (Mojo), methods run / run_smem_decode -- packed
  *     (N, K/2) uint8, scales (N, K/16) float8_e4m3fn, value =
  *     e2m1(code) * |scale|.
@@ -27,15 +30,15 @@
  * never allocates, frees or keeps them.  All arrays are row-major and dense:
  *   A       bf16  (M, K)                    16-byte aligned
  *   packed  uint8 (N, K/2)                  16-byte aligned
- *   scales  int4: bf16 (N, K/128)           2-byte aligned
+ *   scales  int4: bf16 (N, K/G), G = 128 / 32 / 64   2-byte aligned
  *           NVFP4: e4m3 bytes (N, K/16)     2-byte aligned
  *           MXFP4: e8m0 bytes (N, K/32)
- *   zeros   int4: uint8 (N, K/128); must be NULL for NVFP4 / MXFP4
+ *   zeros   int4: uint8 (N, K/G); must be NULL for NVFP4 / MXFP4
  *   C       bf16 or fp32 (M, N)             aligned to its element size
  *   W       bf16 (N, K)                     16-byte aligned (dequant output)
  * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing and
  * checks no pointer);
- * 0 < K <= 2^22, K % 32 == 0, and K % 128 == 0 for int4; M, N < 2^31.
+ * 0 < K <= 2^22, K % 32 == 0, and K % G == 0 for int4 (G its group); M, N < 2^31.
  * Zero points: the GEMM and the dequantisation take any zero byte 0..255
  * (the format stores 0..15).
  *
@@ -62,6 +65,8 @@ extern "C" {
 #define W4A16_INT4_G128 0   /* asymmetric int4, bf16 scale + u8 zero per 128 */
 #define W4A16_NVFP4 1       /* e2m1 codes, e4m3 scale per 16                  */
 #define W4A16_MXFP4 2       /* e2m1 codes, e8m0 scale per 32                  */
+#define W4A16_INT4_G32 3    /* the int4 format with groups of 32 inputs       */
+#define W4A16_INT4_G64 4    /* the int4 format with groups of 64 inputs       */
 #define W4A16_FORMAT_MASK 0xFF
 
 #define W4A16_OUT_BF16 0x000 /* C is bf16, rounded to nearest even (default) */

@@ -15,8 +15,10 @@ arrays to it.  Sources, per function, are cited in the C file:
 * "example_dequant_gemm_bf16_fp4_hopper.py" -- fp4 sign/exponent/mantissa
   split and ``C = A @ B^T`` with B packed (N, K/2).
 
-Formats: ``INT4_G128 = 0``, ``NVFP4 = 1``, ``MXFP4 = 2``.  Scales are passed as
-their raw storage: uint16 bf16 bits (int4) or uint8 bytes (e4m3 / e8m0).
+Formats: ``INT4_G128 = 0``, ``NVFP4 = 1``, ``MXFP4 = 2``, and the same int4 with
+groups of 32 / 64 inputs, ``INT4_G32 = 3``, ``INT4_G64 = 4`` (the group is a
+configuration value of the int4 page, 128 in its fixture).  Scales are passed
+as their raw storage: uint16 bf16 bits (int4) or uint8 bytes (e4m3 / e8m0).
 """
 from __future__ import annotations
 
@@ -26,8 +28,9 @@ import subprocess
 
 import numpy as np
 
-INT4_G128, NVFP4, MXFP4 = 0, 1, 2
-GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32}
+INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64 = 0, 1, 2, 3, 4
+GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64}
+INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "w4a16_oracle.c")
@@ -91,7 +94,7 @@ def _c(a, dtype):
 
 
 def _scales(fmt, scales):
-    return _c(scales, np.uint16 if fmt == INT4_G128 else np.uint8)
+    return _c(scales, np.uint16 if fmt in INT4_FORMATS else np.uint8)
 
 
 # ---- element decoders ------------------------------------------------------

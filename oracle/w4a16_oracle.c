@@ -42,6 +42,9 @@
  *   - the NVFP4 scale enters by magnitude, as [MJ] writes |scale|.
  *   - the int4 zero byte is used as the integer it holds (0..15 for valid
  *     data), with no masking.
+ *   - the int4 group is a parameter of the format ([KB]'s configuration
+ *     carries it as `group`, 128 in its fixture): formats 3 and 4 are the
+ *     same asymmetric int4 with groups of 32 and 64 contiguous inputs.
  *   - NaN inputs produce a NaN weight; the rounded bf16 NaN is 0x7FC0 (sign
  *     kept).
  */
@@ -54,6 +57,13 @@
 #define ORC_INT4_G128 0
 #define ORC_NVFP4 1
 #define ORC_MXFP4 2
+#define ORC_INT4_G32 3
+#define ORC_INT4_G64 4
+#define ORC_NFORMATS 5
+
+static int is_int4(int fmt) {
+  return fmt == ORC_INT4_G128 || fmt == ORC_INT4_G32 || fmt == ORC_INT4_G64;
+}
 
 /* ---- element decoders ---------------------------------------------------- */
 
@@ -133,7 +143,13 @@ uint16_t orc_round_bf16(double x) {
 /* ---- weights --------------------------------------------------------------- */
 
 static int64_t group_of(int fmt) {
-  return fmt == ORC_INT4_G128 ? 128 : fmt == ORC_NVFP4 ? 16 : 32;
+  switch (fmt) {
+    case ORC_INT4_G128: return 128;
+    case ORC_NVFP4: return 16;
+    case ORC_MXFP4: return 32;
+    case ORC_INT4_G32: return 32;
+    default: return 64; /* ORC_INT4_G64 */
+  }
 }
 
 /* The 4-bit code of element (n, k): byte (n, k/2), low nibble for even k,
@@ -151,7 +167,7 @@ double orc_weight(int fmt, const uint8_t* packed, const void* scales,
   int64_t G = group_of(fmt);
   int64_t g = k / G, groups = K / G;
   unsigned code = code_at(packed, K, n, k);
-  if (fmt == ORC_INT4_G128) {
+  if (is_int4(fmt)) {
     double s = orc_bf16_value(((const uint16_t*)scales)[n * groups + g]);
     int z = zeros[n * groups + g];
     return (double)((int)code - z) * s; /* subtraction first, then scale */
@@ -168,7 +184,7 @@ double orc_weight(int fmt, const uint8_t* packed, const void* scales,
 int orc_dequant(int fmt, const uint8_t* packed, const void* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, double* w_exact,
                 uint16_t* w_bf16) {
-  if (fmt < 0 || fmt > 2 || N < 0 || K <= 0 || K % group_of(fmt) != 0) return -1;
+  if (fmt < 0 || fmt >= ORC_NFORMATS || N < 0 || K <= 0 || K % group_of(fmt) != 0) return -1;
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) {
       double w = orc_weight(fmt, packed, scales, zeros, N, K, n, k);
@@ -203,7 +219,7 @@ static void dot_row(const uint16_t* A, int64_t K, int64_t m, const double* wrow,
 int orc_gemm(int fmt, const uint16_t* A, const uint8_t* packed,
              const void* scales, const uint8_t* zeros, int64_t M, int64_t N,
              int64_t K, int weights_bf16, double* C, double* S) {
-  if (fmt < 0 || fmt > 2 || M < 0 || N < 0 || K <= 0 || K % group_of(fmt) != 0)
+  if (fmt < 0 || fmt >= ORC_NFORMATS || M < 0 || N < 0 || K <= 0 || K % group_of(fmt) != 0)
     return -1;
   int err = 0;
 #pragma omp parallel
@@ -234,7 +250,7 @@ int orc_gemm_at(int fmt, const uint16_t* A, const uint8_t* packed,
                 const void* scales, const uint8_t* zeros, int64_t M, int64_t N,
                 int64_t K, int64_t count, const int64_t* m_idx,
                 const int64_t* n_idx, double* C, double* S) {
-  if (fmt < 0 || fmt > 2 || K <= 0 || K % group_of(fmt) != 0) return -1;
+  if (fmt < 0 || fmt >= ORC_NFORMATS || K <= 0 || K % group_of(fmt) != 0) return -1;
   for (int64_t i = 0; i < count; ++i)
     if (m_idx[i] < 0 || m_idx[i] >= M || n_idx[i] < 0 || n_idx[i] >= N) return -1;
   int err = 0;

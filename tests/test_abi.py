@@ -40,6 +40,7 @@ def test_python_constants_match_header():
     assert d["W4A16_INT4_G128"] == w4.INT4_G128
     assert d["W4A16_NVFP4"] == w4.NVFP4
     assert d["W4A16_MXFP4"] == w4.MXFP4
+    assert d["W4A16_INT4_G32"] == w4.INT4_G32 and d["W4A16_INT4_G64"] == w4.INT4_G64
     assert d["W4A16_OUT_F32"] == w4.OUT_F32
     assert d["W4A16_PATH_SKINNY"] == w4.PATH_SKINNY
     assert d["W4A16_PATH_TILED"] == w4.PATH_TILED
@@ -102,7 +103,9 @@ def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
 
 
 @pytest.mark.parametrize("fmt,M,N,K,expect", [
-    (3, 16, 64, 128, w4.ERR_FORMAT),                          # unknown format
+    (5, 16, 64, 128, w4.ERR_FORMAT),                          # unknown format
+    (w4.INT4_G64, 16, 64, 96, w4.ERR_SHAPE),                  # K % 64
+    (w4.INT4_G32, 16, 64, 48, w4.ERR_SHAPE),                  # K % 32
     (w4.INT4_G128 | 0x4000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
     (w4.INT4_G128 | 0x8000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
     (w4.INT4_G128, -1, 64, 128, w4.ERR_SHAPE),
@@ -114,7 +117,7 @@ def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
     (w4.MXFP4, 2 ** 31, 64, 64, w4.ERR_SHAPE),
 ])
 def test_gemm_rejects_format_and_shape(fmt, M, N, K, expect):
-    Z = PZ if (fmt & 0xFF) == w4.INT4_G128 else None
+    Z = PZ if (fmt & 0xFF) in w4.INT4_FORMATS else None
     assert _gemm(fmt, Z=Z, M=M, N=N, K=K) == expect
 
 
@@ -124,6 +127,9 @@ def test_gemm_rejects_null_and_alignment():
     assert _gemm(w4.INT4_G128, S=None) == w4.ERR_NULL
     assert _gemm(w4.INT4_G128, C=None) == w4.ERR_NULL
     assert _gemm(w4.INT4_G128, Z=None) == w4.ERR_NULL           # int4 needs zeros
+    assert _gemm(w4.INT4_G32, Z=None) == w4.ERR_NULL
+    assert _gemm(w4.INT4_G64, Z=None) == w4.ERR_NULL
+    assert _gemm(w4.INT4_G64, S=ctypes.c_void_p(0x100001)) == w4.ERR_ALIGN
     assert _gemm(w4.NVFP4, Z=PZ) == w4.ERR_NULL                  # fp4 takes none
     odd = ctypes.c_void_p(0x100008)
     assert _gemm(w4.INT4_G128, A=odd) == w4.ERR_ALIGN
@@ -207,7 +213,7 @@ def _grouped(fmt, count=3, N=(64, 32, 48), M=1, K=128, A=PA, packed=True, scales
     n = max(count, 1)
     mk = lambda base: (ctypes.c_void_p * n)(*[0x100000 * (base + 8 * i) for i in range(n)])
     P, S, Cs = mk(2), mk(3), mk(5)
-    Z = mk(4) if (zeros == "auto" and fmt == w4.INT4_G128) or zeros is True else None
+    Z = mk(4) if (zeros == "auto" and (fmt & 0xFF) in w4.INT4_FORMATS) or zeros is True else None
     if bad:
         arr, i, val = bad
         {"P": P, "S": S, "C": Cs, "Z": Z}[arr][i] = val
@@ -218,8 +224,10 @@ def _grouped(fmt, count=3, N=(64, 32, 48), M=1, K=128, A=PA, packed=True, scales
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(fmt=3), w4.ERR_FORMAT),
+    (dict(fmt=5), w4.ERR_FORMAT),
     (dict(fmt=w4.INT4_G128, count=0), w4.ERR_SHAPE),
+    (dict(fmt=w4.INT4_G64, K=96), w4.ERR_SHAPE),               # K % 64
+    (dict(fmt=w4.INT4_G32, zeros=False), w4.ERR_NULL),
     (dict(fmt=w4.INT4_G128, count=9), w4.ERR_SHAPE),
     (dict(fmt=w4.INT4_G128, K=96), w4.ERR_SHAPE),              # int4 needs K % 128
     (dict(fmt=w4.NVFP4, K=48), w4.ERR_SHAPE),                  # K % 32

@@ -2,9 +2,9 @@
 
 ``C = A . dequant(packed, scales, zeros)^T`` with bf16 activations A (M, K),
 4-bit weights packed (N, K/2) uint8 (low nibble = even k) and fp32
-accumulation.  Formats: ``INT4_G128`` (bf16 scale + uint8 zero per 128 k),
-``NVFP4`` (e2m1 codes, e4m3 scale per 16 k), ``MXFP4`` (e2m1 codes, e8m0
-scale per 32 k).
+accumulation.  Formats: ``INT4_G128`` (bf16 scale + uint8 zero per 128 k;
+``INT4_G32`` / ``INT4_G64``: the same per 32 / 64 k), ``NVFP4`` (e2m1 codes,
+e4m3 scale per 16 k), ``MXFP4`` (e2m1 codes, e8m0 scale per 32 k).
 
 This module only marshals arguments to the C ABI declared in
 ``include/w4a16.h``: it checks that tensor shapes, dtypes and devices agree
@@ -20,9 +20,11 @@ import os
 
 import torch
 
-INT4_G128, NVFP4, MXFP4 = 0, 1, 2
-GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32}
-FORMAT_NAMES = {INT4_G128: "int4_g128", NVFP4: "nvfp4", MXFP4: "mxfp4"}
+INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64 = 0, 1, 2, 3, 4
+GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64}
+FORMAT_NAMES = {INT4_G128: "int4_g128", NVFP4: "nvfp4", MXFP4: "mxfp4",
+                INT4_G32: "int4_g32", INT4_G64: "int4_g64"}
+INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64)
 OUT_BF16, OUT_F32 = 0x000, 0x100
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_MID = 0x0000, 0x1000, 0x2000, 0x3000
 PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "mid": PATH_MID, "tiled": PATH_TILED}
@@ -130,8 +132,8 @@ def _check_weights(fmt, packed, scales, zeros, N, K, device):
     if K % 32 or K % G:
         raise ValueError(f"K={K} must be a multiple of 32 and of the group size {G}")
     _check(packed, "packed", (N, K // 2), 1, device)
-    _check(scales, "scales", (N, K // G), 2 if fmt == INT4_G128 else 1, device)
-    if fmt == INT4_G128:
+    _check(scales, "scales", (N, K // G), 2 if fmt in INT4_FORMATS else 1, device)
+    if fmt in INT4_FORMATS:
         if zeros is None:
             raise ValueError("int4 weights need zeros")
         _check(zeros, "zeros", (N, K // G), 1, device)
@@ -220,7 +222,7 @@ def _grouped_args(fmt, A, weights, outs, out_dtype):
         P[i], S[i], Cs[i], Ns[i] = packed.data_ptr(), scales.data_ptr(), out.data_ptr(), N
         Z[i] = zeros.data_ptr() if zeros is not None else None
     flags = OUT_F32 if dt == torch.float32 else OUT_BF16
-    zarr = Z if fmt == INT4_G128 else None
+    zarr = Z if fmt in INT4_FORMATS else None
     return flags, outs, (P, S, zarr, Cs, Ns), (M, K)
 
 

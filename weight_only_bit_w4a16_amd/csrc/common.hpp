@@ -26,7 +26,13 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-enum Format : int { kInt4 = 0, kNvfp4 = 1, kMxfp4 = 2 };
+// kInt4: int4 with groups of 128 (one group per 128-code k-block);
+// kInt4G32 / kInt4G64: the same with groups of 32 / 64 codes.
+enum Format : int { kInt4 = 0, kNvfp4 = 1, kMxfp4 = 2, kInt4G32 = 3, kInt4G64 = 4 };
+constexpr int kFormats = 5;
+
+// int4 formats: (code - zero) * scale with a bf16 scale and u8 zero per group
+constexpr bool is_int4(int fmt) { return fmt == kInt4 || fmt == kInt4G32 || fmt == kInt4G64; }
 
 template <int FMT>
 struct FormatTraits;
@@ -41,6 +47,14 @@ struct FormatTraits<kNvfp4> {
 template <>
 struct FormatTraits<kMxfp4> {
   static constexpr int kGroup = 32;
+};
+template <>
+struct FormatTraits<kInt4G32> {
+  static constexpr int kGroup = 32;
+};
+template <>
+struct FormatTraits<kInt4G64> {
+  static constexpr int kGroup = 64;
 };
 
 // ---- bit helpers ------------------------------------------------------------

@@ -4,7 +4,8 @@
 // one row, inside one group for every format) into 64 bytes of bf16.
 //
 // Element rules (page titles): int4 -- "megakernel_int4_weight_decode.py",
-// "The weight format": (code - zero) * scale, the subtraction first; NVFP4 --
+// "The weight format": (code - zero) * scale, the subtraction first, per
+// group of 128 (its configuration's `group`; 32 and 64 also served); NVFP4 --
 // "Matmul2dFp4", run: e2m1 times |e4m3 scale| per 16; MXFP4 -- e2m1 times
 // 2^(E-127) per 32.  Each weight is exact in fp32 and rounded once to bf16.
 #include "common.hpp"
@@ -30,8 +31,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     const int64_t c = i - n * chunks_per_row;
     const u32x4_t q = *reinterpret_cast<const u32x4_t*>(packed + n * (K / 2) + c * 16);
     u32x4_t out[4];
-    if constexpr (FMT == kInt4) {
-      const int64_t g = (c * 32) / 128;
+    if constexpr (is_int4(FMT)) {
+      const int64_t g = (c * 32) / G;
       const float s = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(scales)[n * groups + g]);
       const float zf = (float)zeros[n * groups + g];
 #pragma unroll
@@ -78,6 +79,14 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, co
       break;
     case kNvfp4:
       hipLaunchKernelGGL(dequant_kernel<kNvfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                         packed, scales, zeros, W, N, K);
+      break;
+    case kInt4G32:
+      hipLaunchKernelGGL(dequant_kernel<kInt4G32>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                         packed, scales, zeros, W, N, K);
+      break;
+    case kInt4G64:
+      hipLaunchKernelGGL(dequant_kernel<kInt4G64>, dim3((unsigned)blocks), dim3(threads), 0, stream,
                          packed, scales, zeros, W, N, K);
       break;
     default:

@@ -35,7 +35,7 @@ constexpr int kMidCols = 32;   // output columns (weight rows) per workgroup
 constexpr int kMidSStage = 4;  // staged scale / zero dwords per thread, at most
 
 template <int FMT>
-constexpr int mid_sb() { return FMT == kInt4 ? 2 : 1; }  // scale bytes
+constexpr int mid_sb() { return is_int4(FMT) ? 2 : 1; }  // scale bytes
 
 // scale (zero) window capacity in bytes: 32 rows plus the <= 3-byte lead of
 // the dword-aligned start and the <= 3-byte tail of its last dword
@@ -61,6 +61,8 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
   const int KB = (KC + 3) >> 2;   // k-blocks, the last one possibly partial
   constexpr int G = FormatTraits<FMT>::kGroup;
   constexpr int SB = mid_sb<FMT>();
+  // int4: the group of 32-code chunk c is c >> GS (the k-block for G = 128)
+  constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
   const int groups = K / G;
   const uint32_t rowb = (uint32_t)(K >> 1);
   const int rows = min(kMidCols, N - n0);
@@ -69,11 +71,11 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
   const int kw = __builtin_amdgcn_readfirstlane(wave) * U;
 
   const uint32_t s_cap = S_LDS ? mid_cap((uint32_t)(kMidCols * groups * SB)) : 0u;
-  const uint32_t z_cap = S_LDS && FMT == kInt4 ? mid_cap((uint32_t)(kMidCols * groups)) : 0u;
+  const uint32_t z_cap = S_LDS && is_int4(FMT) ? mid_cap((uint32_t)(kMidCols * groups)) : 0u;
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + s_cap + z_cap);  // [waves][MS * 2][64]
 
   const uint8_t* s_base = reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB;
-  const uint8_t* z_base = FMT == kInt4 ? zeros + (int64_t)n0 * groups : nullptr;
+  const uint8_t* z_base = is_int4(FMT) ? zeros + (int64_t)n0 * groups : nullptr;
   // S_LDS: the windows' dwords, read from the 4-byte aligned address at or
   // below each block (at most 3 bytes past its end, in the same dword)
   uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
       const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
       sst[i] = wave_slot0 + i * blockDim.x < s_words ? buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB) : 0u;
     }
-    if constexpr (FMT == kInt4) {
+    if constexpr (is_int4(FMT)) {
       const rsrc_t zs = window(z_base, (uint32_t)(rows * groups), z_delta, z_words);
 #pragma unroll
       for (int i = 0; i < kMidSStage; ++i) {
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     }
   } else {
     sr = make_rsrc(s_base, (uint32_t)(rows * groups * SB));
-    if constexpr (FMT == kInt4) zr = make_rsrc(z_base, (uint32_t)(rows * groups));
+    if constexpr (is_int4(FMT)) zr = make_rsrc(z_base, (uint32_t)(rows * groups));
   }
 
   // weight rows past N, A rows past M and chunks past K read as 0
@@ -129,8 +131,8 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
         const uint32_t r = (uint32_t)(16 * h + nl);
         q[u][h] = buf_load_b128(wr, ok ? r * rowb + (uint32_t)c * 16u : kBufferOOB);
         if constexpr (!S_LDS) {
-          if constexpr (FMT == kInt4) {
-            const uint32_t gi = r * (uint32_t)groups + (uint32_t)kb;
+          if constexpr (is_int4(FMT)) {
+            const uint32_t gi = r * (uint32_t)groups + (uint32_t)(FMT == kInt4 ? kb : c >> GS);
             sraw[u][h] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
             zraw[u][h] = buf_load_b8(zr, ok ? gi : kBufferOOB);
           } else if constexpr (FMT == kNvfp4) {
@@ -175,6 +177,21 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
           nz[h] = int4_neg_zero(z);
 #pragma unroll
           for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_natural(q[u][h][j]);
+        } else if constexpr (is_int4(FMT)) {
+          // groups shorter than a k-block: the chunk's group, applied in the
+          // decode, (code - zero) * scale rounded once to bf16
+          const int gi = r * groups + (cc >> GS);
+          uint32_t sbits, z;
+          if constexpr (S_LDS) {
+            sbits = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
+            z = zb[gi];
+          } else {
+            sbits = sraw[u][h];
+            z = zraw[u][h];
+          }
+          const float s = bf16_bits_to_f32(sbits), zf = (float)z;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_weights(q[u][h][j], s, zf);
         } else if constexpr (FMT == kNvfp4) {
           const uint32_t s2 = S_LDS ? *reinterpret_cast<const uint16_t*>(sb + r * groups + 2 * cc) : sraw[u][h];
           const float s0 = e4m3_magnitude(s2 & 0xFFu), s1 = e4m3_magnitude(s2 >> 8);
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     for (int i = 0; i < kMidSStage; ++i) {
       const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
       if (w < s_words) reinterpret_cast<uint32_t*>(lds)[w] = sst[i];
-      if constexpr (FMT == kInt4) {
+      if constexpr (is_int4(FMT)) {
         if (w < z_words) reinterpret_cast<uint32_t*>(lds + s_cap)[w] = zst[i];
       }
     }
@@ -305,11 +322,12 @@ MidPlan mid_plan(int fmt, int64_t M, int64_t K) {
   p.MS = (int)((slices + row_tiles - 1) / row_tiles);
   if (p.MS < 2) p.MS = 2;
   // scale windows in LDS when every dword has a staging register
-  const int64_t groups = K / (fmt == 0 ? 128 : fmt == 1 ? 16 : 32);
-  const int64_t sb = fmt == 0 ? 2 : 1;
+  const bool int4 = is_int4(fmt);
+  const int64_t groups = K / (fmt == kInt4 ? 128 : fmt == kNvfp4 ? 16 : fmt == kInt4G64 ? 64 : 32);
+  const int64_t sb = int4 ? 2 : 1;
   const int64_t slots = (int64_t)kMidSStage * 64 * p.waves;
   const int64_t s_cap = mid_cap((uint32_t)(kMidCols * groups * sb));
-  const int64_t z_cap = fmt == 0 ? mid_cap((uint32_t)(kMidCols * groups)) : 0;
+  const int64_t z_cap = int4 ? mid_cap((uint32_t)(kMidCols * groups)) : 0;
   const int64_t red = (int64_t)p.waves * p.MS * 2 * 1024;
   p.s_lds = s_cap / 4 <= slots && z_cap / 4 <= slots && s_cap + z_cap + red <= 160 * 1024;
   p.lds = (unsigned)((p.s_lds ? s_cap + z_cap : 0) + red);
@@ -364,7 +382,11 @@ hipError_t launch_mid(const GemmArgs& a) {
     case 2: return launch_fmt<kNvfp4, false>(a);
     case 3: return launch_fmt<kNvfp4, true>(a);
     case 4: return launch_fmt<kMxfp4, false>(a);
-    default: return launch_fmt<kMxfp4, true>(a);
+    case 5: return launch_fmt<kMxfp4, true>(a);
+    case 6: return launch_fmt<kInt4G32, false>(a);
+    case 7: return launch_fmt<kInt4G32, true>(a);
+    case 8: return launch_fmt<kInt4G64, false>(a);
+    default: return launch_fmt<kInt4G64, true>(a);
   }
 }
 

@@ -94,7 +94,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const int chunks = K >> 5;           // 32-code chunks per row
   const int KB = (chunks + 3) >> 2;    // 128-code k-blocks (last may be partial)
   constexpr int G = FormatTraits<FMT>::kGroup;
-  constexpr int SB = (FMT == kInt4) ? 2 : 1;  // bytes per scale
+  constexpr int SB = is_int4(FMT) ? 2 : 1;  // bytes per scale
+  // int4: the group of 32-code chunk c is c >> GS (the k-block for G = 128)
+  constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
   const int groups = K / G;
 
   // Buffer descriptors over exactly this workgroup's 16 weight rows and 16 A
@@ -107,8 +109,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
   const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB,
                               (uint32_t)(rows * groups * SB));
-  const rsrc_t zr = make_rsrc(FMT == kInt4 ? zeros + (int64_t)n0 * groups : nullptr,
-                              FMT == kInt4 ? (uint32_t)(rows * groups) : 0u);
+  const rsrc_t zr = make_rsrc(is_int4(FMT) ? zeros + (int64_t)n0 * groups : nullptr,
+                              is_int4(FMT) ? (uint32_t)(rows * groups) : 0u);
 
   // Scale staging: rows n0 .. n0+rows-1 of the scales (and zeros) are one
   // contiguous block; it is read as dwords from the 4-byte aligned address at
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const int am = M < 16 ? M : 16;
   const uint32_t s_off = A_LDS ? (((uint32_t)(am + 1) * (uint32_t)K * 2u + 15u) & ~15u) : 0u;
   const uint32_t z_off = s_off + (((16u * (uint32_t)groups * SB + 6u) + 15u) & ~15u);
-  const uint32_t z_cap = FMT == kInt4 ? ((16u * (uint32_t)groups + 6u + 15u) & ~15u) : 0u;
+  const uint32_t z_cap = is_int4(FMT) ? ((16u * (uint32_t)groups + 6u + 15u) & ~15u) : 0u;
   // per-wave A regions (A_DMA) after the scale and zero windows
   const uint32_t a_dma_off = S_LDS ? z_off + z_cap : s_off;
   const uint32_t a_wave = lds_address(a_lds) + a_dma_off +
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
       const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
       sst[i] = wave_slot0 + i * blockDim.x < s_words ? buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB) : 0u;
     }
-    if constexpr (FMT == kInt4) {
+    if constexpr (is_int4(FMT)) {
       const rsrc_t zs = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), z_delta, z_words);
 #pragma unroll
       for (int i = 0; i < kZStage; ++i) {
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
         const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
         if (w < s_words) reinterpret_cast<uint32_t*>(a_lds + s_off)[w] = sst[i];
       }
-      if constexpr (FMT == kInt4) {
+      if constexpr (is_int4(FMT)) {
 #pragma unroll
         for (int i = 0; i < kZStage; ++i) {
           const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
@@ -199,8 +201,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
       const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
-      if constexpr (FMT == kInt4) {
-        const uint32_t gi = (uint32_t)(nl * groups + kb);
+      if constexpr (is_int4(FMT)) {
+        const uint32_t gi = (uint32_t)(nl * groups + (FMT == kInt4 ? kb : c >> GS));
         sraw[u] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
         zraw[u] = buf_load_b8(zr, ok ? gi : kBufferOOB);
       } else if constexpr (FMT == kNvfp4) {
@@ -276,8 +278,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
         const int c = kb * 4 + g;
         const bool ok = FULL || c < chunks;
         const uint8_t* sb = a_lds + s_off + s_delta;
-        if constexpr (FMT == kInt4) {
-          const int gi = nl * groups + (ok ? kb : 0);
+        if constexpr (is_int4(FMT)) {
+          const int gi = nl * groups + (ok ? (FMT == kInt4 ? kb : c >> GS) : 0);
           sraw[u] = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
           zraw[u] = (a_lds + z_off + z_delta)[gi];
         } else if constexpr (FMT == kNvfp4) {
@@ -306,6 +308,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
         acc[1] = __builtin_fmaf(s, dp[1] + dn[1], acc[1]);
         acc[2] = __builtin_fmaf(s, dp[2] + dn[2], acc[2]);
         acc[3] = __builtin_fmaf(s, dp[3] + dn[3], acc[3]);
+      } else if constexpr (is_int4(FMT)) {
+        // groups shorter than a k-block: the lane's chunk has one group,
+        // whose (code - zero) * scale is applied in the decode (one bf16
+        // rounding per weight, a weight equal to its zero point exactly 0)
+        const float s = bf16_bits_to_f32(sraw[u]);
+        const float zf = (float)zraw[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[u][j], int4x8_to_bf16_weights(q[u][j], s, zf), acc);
       } else if constexpr (FMT == kNvfp4) {
         const float s0 = e4m3_magnitude(sraw[u] & 0xFFu);
         const float s1 = e4m3_magnitude(sraw[u] >> 8);
@@ -733,10 +743,10 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   const bool a_lds = a_bytes <= (int64_t)kAStage * 16 * 64 * waves && a_bytes <= 64 * 1024;
   // LDS: A rows + a zero row (16-byte aligned), then the scale and zero windows
   const unsigned lds_a = a_lds ? (unsigned)(((arows + 1) * a.K * 2 + 15) & ~15) : 0u;
-  constexpr int SB = FMT == kInt4 ? 2 : 1;
+  constexpr int SB = is_int4(FMT) ? 2 : 1;
   const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
   const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
-  const int64_t z_cap = FMT == kInt4 ? (16 * groups + 6 + 15) & ~15 : 0;
+  const int64_t z_cap = is_int4(FMT) ? (16 * groups + 6 + 15) & ~15 : 0;
   const int64_t lds_s = s_cap + z_cap;
   // staged when every dword of the windows has a staging register
   const int64_t threads = 64 * waves;
@@ -819,6 +829,9 @@ hipError_t launch_stream_k(const GroupedArgs& a, const SkinnyGroup& grp, int til
 // (nothing launched) otherwise.
 template <int FMT, bool OUT_F32>
 bool try_stream(const GroupedArgs& a, int64_t min_tiles, hipError_t& err) {
+  if constexpr (FMT == kInt4G32 || FMT == kInt4G64) {
+    return false;  // the streaming variant decodes int4 with groups of 128 only
+  } else {
   if (a.count != 1 || a.K % 128 != 0 || a.M > 16) return false;
   const int KB = (int)(a.K / 128);
   // the one-tile kernel's split of K (a column's bits never depend on N or
@@ -856,6 +869,7 @@ bool try_stream(const GroupedArgs& a, int64_t min_tiles, hipError_t& err) {
     err = NS == 1 ? launch_stream_k<FMT, OUT_F32, 1, 1>(a, grp, (int)tiles, waves, lds)
                   : launch_stream_k<FMT, OUT_F32, 1, 2>(a, grp, (int)tiles, waves, lds);
   return true;
+  }
 }
 
 // Work split: each wave takes U consecutive k-blocks per pass (U 16-byte
@@ -899,7 +913,11 @@ hipError_t launch_skinny_grouped(const GroupedArgs& a) {
     case 2: return launch_fmt<kNvfp4, false>(a);
     case 3: return launch_fmt<kNvfp4, true>(a);
     case 4: return launch_fmt<kMxfp4, false>(a);
-    default: return launch_fmt<kMxfp4, true>(a);
+    case 5: return launch_fmt<kMxfp4, true>(a);
+    case 6: return launch_fmt<kInt4G32, false>(a);
+    case 7: return launch_fmt<kInt4G32, true>(a);
+    case 8: return launch_fmt<kInt4G64, false>(a);
+    default: return launch_fmt<kInt4G64, true>(a);
   }
 }
 

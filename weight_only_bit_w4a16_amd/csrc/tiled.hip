@@ -50,8 +50,9 @@ constexpr int kStages = 2;
 // row (E consecutive lanes, one global run per row), covering kKTiles k-tiles.
 //   MXFP4: 1-byte e8m0 per 32 codes, E = 16 -> 8 k-tiles.
 //   NVFP4: 2-byte element = the e4m3 bytes of two 16-code blocks, E = 8 -> 4 k-tiles.
-//   int4:  2-byte bf16 scale (array 0) and 1-byte zero (array 1) per 128 codes,
-//          E = 8 -> 16 k-tiles.
+//   int4:  2-byte bf16 scale (array 0) and 1-byte zero (array 1) per group:
+//          groups of 128, E = 8 -> 16 k-tiles; of 64, E = 8 -> 8 k-tiles; of
+//          32, E = 16 -> 8 k-tiles.
 // Elements past K, and rows past N, are zero-filled by the copy.
 template <int FMT>
 struct ScaleTile;
@@ -66,6 +67,14 @@ struct ScaleTile<kNvfp4> {
 template <>
 struct ScaleTile<kInt4> {
   static constexpr int kElems = 8, kKTiles = 16, kArrays = 2;
+};
+template <>
+struct ScaleTile<kInt4G64> {
+  static constexpr int kElems = 8, kKTiles = 8, kArrays = 2;
+};
+template <>
+struct ScaleTile<kInt4G32> {
+  static constexpr int kElems = 16, kKTiles = 8, kArrays = 2;
 };
 // slot swizzle of row r: 16 rows reading one element hit 16 distinct banks
 template <int E>
@@ -169,11 +178,11 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   const int brows = min(BN, N - n_base);
   const rsrc_t ar = make_rsrc(A + (int64_t)m_base * K, (uint32_t)min(BM, M - m_base) * arow_b);
   const rsrc_t br = make_rsrc(packed + (int64_t)n_base * brow_b, (uint32_t)brows * brow_b);
-  constexpr int SB = FMT == kInt4 ? 2 : 1;
+  constexpr int SB = is_int4(FMT) ? 2 : 1;
   const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n_base * groups * SB,
                               (uint32_t)(brows * groups * SB));
-  const rsrc_t zr = make_rsrc(FMT == kInt4 ? zeros + (int64_t)n_base * groups : nullptr,
-                              FMT == kInt4 ? (uint32_t)(brows * groups) : 0u);
+  const rsrc_t zr = make_rsrc(is_int4(FMT) ? zeros + (int64_t)n_base * groups : nullptr,
+                              is_int4(FMT) ? (uint32_t)(brows * groups) : 0u);
   const uint32_t lds0 = lds_address(smem);
   // Resolve the output pointer's scalar load here: a scalar load still in
   // flight in the k-loop would turn every partial LDS wait there into a full one.
@@ -275,7 +284,8 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     const uint8_t* Bs = smem + L::kBOff + cur * kBBytes + (wn * TN * 16) * 32;
     // scale element of lane group g in this k-tile, and its slot
     const int jt = j % ST::kKTiles;
-    const int se = FMT == kInt4 ? (jt >> 1) : 2 * jt + (g >> 1);
+    // (lane group g holds codes 16g .. 16g+15 of the k-tile's 64)
+    const int se = FMT == kInt4 ? (jt >> 1) : FMT == kInt4G64 ? jt : 2 * jt + (g >> 1);
     const uint8_t* Ss = smem + L::kSOff + ((j / ST::kKTiles) & 1) * L::kSBytes +
                         ((wn * TN * 16 + l16) * E + (se ^ fs)) * 4;
 
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     for (int t = 0; t < TN; ++t) {
       bq[t] = *reinterpret_cast<const u32x2_t*>(Bs + b_rd + t * 16 * 32);
       sw[t] = *reinterpret_cast<const uint32_t*>(Ss + t * 16 * E * 4);
-      if constexpr (FMT == kInt4)
+      if constexpr (is_int4(FMT))
         zw[t] = *reinterpret_cast<const uint32_t*>(Ss + t * 16 * E * 4 + L::kSArrayBytes);
     }
 #pragma unroll
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     float bs[TN], bz[TN];
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      if constexpr (FMT == kInt4) {
+      if constexpr (is_int4(FMT)) {
         bs[t] = bf16_bits_to_f32(sw[t]);
         bz[t] = (float)zw[t];
       } else if constexpr (FMT == kNvfp4) {
@@ -312,7 +322,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
       }
     }
     auto decode = [&](int s, int t) -> u32x4_t {
-      if constexpr (FMT == kInt4) {
+      if constexpr (is_int4(FMT)) {
         return int4x8_to_bf16_weights(bq[t][s], bs[t], bz[t]);
       } else if constexpr (FMT == kNvfp4) {
         return fp4x8_to_bf16_fscale(bq[t][s], bs[t]);
@@ -522,7 +532,11 @@ hipError_t launch_tiled(const GemmArgs& a) {
     case 2: return launch_fmt<kNvfp4, false>(a);
     case 3: return launch_fmt<kNvfp4, true>(a);
     case 4: return launch_fmt<kMxfp4, false>(a);
-    default: return launch_fmt<kMxfp4, true>(a);
+    case 5: return launch_fmt<kMxfp4, true>(a);
+    case 6: return launch_fmt<kInt4G32, false>(a);
+    case 7: return launch_fmt<kInt4G32, true>(a);
+    case 8: return launch_fmt<kInt4G64, false>(a);
+    default: return launch_fmt<kInt4G64, true>(a);
   }
 }
 
