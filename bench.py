@@ -95,10 +95,10 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode_gemv_int4_m1", choices=list(WORKLOADS) + [CHAIN])
-    ap.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
+    ap.add_argument("--path", default="auto", choices=["auto", "skinny", "mid", "tiled"])
     ap.add_argument("--shape", default=None,
-                    help="custom single-GEMM workload 'format,M,N,K' (format 0 int4, 1 nvfp4, "
-                         "2 mxfp4; bf16 out) instead of --workload")
+                    help="custom single-GEMM workload 'format,M,N,K' (format 0 int4 g128, 1 nvfp4, "
+                         "2 mxfp4, 3 int4 g32, 4 int4 g64; bf16 out) instead of --workload")
     ap.add_argument("--epilogue", default=None, choices=["none", "relu", "silu", "gelu_tanh"],
                     help="single-GEMM workloads: fuse a bf16 bias, a residual (beta = 1) and this "
                          "activation into the GEMM (w4a16_gemm_ex); their bytes count as traffic")
