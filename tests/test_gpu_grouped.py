@@ -20,7 +20,7 @@ DEV = torch.device("cuda", 0)
 
 def _dev_weights(case):
     p = torch.from_numpy(case.packed).to(DEV)
-    if case.fmt == w4.INT4_G128:
+    if case.fmt in w4.INT4_FORMATS:
         s = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
         z = torch.from_numpy(case.zeros).to(DEV)
     else:

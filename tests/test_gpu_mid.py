@@ -32,7 +32,7 @@ def _dev(case, s_off=0, z_off=0):
     buf = torch.zeros(sb.size + s_off + 16, dtype=torch.uint8, device=DEV)
     buf[s_off:s_off + sb.size] = torch.from_numpy(sb.copy()).to(DEV)
     s = buf[s_off:s_off + sb.size]
-    if case.fmt == w4.INT4_G128:
+    if case.fmt in w4.INT4_FORMATS:
         s = s.view(torch.bfloat16).view(case.scales.shape)
         zb = torch.zeros(case.zeros.size + z_off + 16, dtype=torch.uint8, device=DEV)
         zb[z_off:z_off + case.zeros.size] = torch.from_numpy(case.zeros.reshape(-1).copy()).to(DEV)

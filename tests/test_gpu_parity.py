@@ -24,7 +24,7 @@ DEV = torch.device("cuda", 0)
 def to_dev(case):
     A = torch.from_numpy(case.A.view(np.int16)).to(DEV).view(torch.bfloat16)
     packed = torch.from_numpy(case.packed).to(DEV)
-    if case.fmt == w4.INT4_G128:
+    if case.fmt in w4.INT4_FORMATS:
         scales = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
         zeros = torch.from_numpy(case.zeros).to(DEV)
     else:
@@ -306,17 +306,20 @@ def test_deterministic_and_stream(fmt, M, N, K):
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
 
 
-@pytest.mark.parametrize("fmt,M,N,K", [(w4.INT4_G128, 1, 4096, 3072), (w4.NVFP4, 16, 1024, 512),
-                                       (w4.NVFP4, 64, 1024, 512), (w4.MXFP4, 300, 512, 256)])
-def test_hip_graph_capture_replay(fmt, M, N, K):
+@pytest.mark.parametrize("fmt,M,N,K,path", [(w4.INT4_G128, 1, 4096, 3072, "auto"),
+                                            (w4.NVFP4, 16, 1024, 512, "auto"),
+                                            (w4.NVFP4, 64, 1024, 512, "mid"),
+                                            (w4.MXFP4, 300, 512, 256, "tiled"),
+                                            (w4.INT4_G64, 40, 300, 512, "skinny")])
+def test_hip_graph_capture_replay(fmt, M, N, K, path):
     """The C ABI call is capturable: replays of a captured graph, with eager
     work and synchronisations between them, match the eager result."""
     case = inputs.make_case(fmt, M, N, K, seed=21)
     A, p, s, z = to_dev(case)
-    eager = w4.gemm(fmt, A, p, s, z)
+    eager = w4.gemm(fmt, A, p, s, z, path=path)
     torch.cuda.synchronize()
     out = torch.empty_like(eager)
-    call = w4.PreparedGemm(fmt, A, p, s, z, out)
+    call = w4.PreparedGemm(fmt, A, p, s, z, out, path=path)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         call()
@@ -327,3 +330,62 @@ def test_hip_graph_capture_replay(fmt, M, N, K):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+
+
+# ---- exact single-atom and chain-graph checks ----------------------------------------
+
+@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.NVFP4, w4.MXFP4, w4.INT4_G32, w4.INT4_G64])
+@pytest.mark.parametrize("path", ["skinny", "mid", "tiled"])
+def test_integer_data_is_exact(fmt, path):
+    """One MFMA atom's worth of rows and columns (16 x 16) over one or a few
+    k-blocks, with small-integer activations and unit scales: every product
+    and partial sum is an integer below 2^24, so any correct kernel returns the
+    oracle's value bit for bit -- a transposed operand, a wrong k-slot order
+    or a misplaced nibble cannot hide inside the tolerance."""
+    M, N, K = 16, 16, 256
+    case = inputs.make_case(fmt, M, N, K, seed=40 + fmt)
+    rng = np.random.default_rng(41 + fmt)
+    a = rng.integers(-3, 4, size=(M, K)).astype(np.float32)
+    case.A[:] = np.array([oracle.round_bf16(v) for v in a.ravel()], np.uint16).reshape(M, K)
+    if fmt in w4.INT4_FORMATS:
+        case.scales[:] = oracle.round_bf16(1.0)
+    elif fmt == w4.NVFP4:
+        case.scales[:] = 0x38   # e4m3 1.0
+    else:
+        case.scales[:] = 127    # e8m0 1.0
+    C = run_gemm(case, torch.float32, path)
+    Cref, _ = oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
+    assert np.all(np.abs(Cref) < 2 ** 20) and np.all(Cref == np.round(Cref * 2) / 2)
+    assert np.array_equal(C, Cref), np.argwhere(C != Cref)[:5]
+
+
+def test_decode_chain_graph_replay():
+    """Two decoder layers of the chain (8 launches: grouped q/k/v, o, grouped
+    gate/up, down) captured in one graph; every replay equals eager calls."""
+    shapes = inputs.decoder_chain_shapes(2)
+    groups = inputs.decoder_chain_groups(2)[:-1]  # without the LM head
+    dev_w, dev_a = [], []
+    for i, (name, n, k) in enumerate(shapes[:-1]):
+        case = inputs.make_case(w4.INT4_G128, 1, n, k, inputs.chain_seed(0, i))
+        A, p, s, z = to_dev(case)
+        dev_w.append((p, s, z))
+        dev_a.append(A)
+    outs = [[torch.empty((1, shapes[i][1]), dtype=torch.bfloat16, device=DEV) for i in g] for g in groups]
+    calls = [w4.PreparedGroupedGemm(w4.INT4_G128, dev_a[g[0]], [dev_w[i] for i in g], o)
+             for g, o in zip(groups, outs)]
+    eager = [[w4.gemm(w4.INT4_G128, dev_a[g[0]], *dev_w[i]) for i in g] for g in groups]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c()
+    for rep in range(3):
+        for o in outs:
+            for t in o:
+                t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            for t, ref in zip(o, e):
+                assert torch.equal(t.view(torch.int16), ref.view(torch.int16)), rep
