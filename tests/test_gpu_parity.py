@@ -217,6 +217,9 @@ RAGGED = [
     # here with part counts that do not divide the k-blocks evenly
     (w4.MXFP4, 1, 200, 288), (w4.NVFP4, 2, 100, 480), (w4.INT4_G128, 3, 50, 1280),
     (w4.INT4_G128, 1, 1024, 3072), (w4.NVFP4, 1, 72, 8192),
+    # long fp4 scale windows: per-lane scale loads at one row, the LDS-staged
+    # window from two rows on
+    (w4.NVFP4, 4, 72, 8192), (w4.MXFP4, 1, 40, 8192), (w4.MXFP4, 3, 40, 8192),
 ]
 
 

@@ -748,10 +748,15 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
   const int64_t z_cap = is_int4(FMT) ? (16 * groups + 6 + 15) & ~15 : 0;
   const int64_t lds_s = s_cap + z_cap;
-  // staged when every dword of the windows has a staging register
+  // staged when every dword of the windows has a staging register (the zero
+  // window exists for int4 only).  Exception, measured: a single fp4 row with
+  // a window of 4 KB or more is one memory round trip per workgroup, and
+  // per-lane scale loads that travel with the weights beat the staged copy
+  // there (e.g. 3072 x 8192 NVFP4: 7.4 against 8.0 us).
   const int64_t threads = 64 * waves;
-  const bool s_lds = (16 * groups * SB + 6) / 4 <= kSStage * threads &&
-                     (16 * groups + 6) / 4 <= kZStage * threads && lds_s <= 32 * 1024;
+  const bool lane_scales = !is_int4(FMT) && a.M == 1 && 16 * groups * SB >= 4096;
+  const bool s_lds = !lane_scales && (16 * groups * SB + 6) / 4 <= kSStage * threads &&
+                     (!is_int4(FMT) || (16 * groups + 6) / 4 <= kZStage * threads) && lds_s <= 32 * 1024;
   const bool full = a.K % 128 == 0;
   const dim3 block(64 * waves);
   static const bool no_dma = [] {
