@@ -21,13 +21,15 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
 ACTS = ["none", "relu", "silu", "gelu_tanh"]
 
-# (fmt, M, N, K, path): skinny, mid, tiled, and a launch the streaming
-# variant takes
+# (fmt, M, N, K, path): skinny, mid, tiled, a launch the streaming variant
+# takes and one the ring variant takes
 SHAPES = {
     "skinny": (w4.INT4_G128, 3, 200, 384, "skinny"),
     "mid": (w4.MXFP4, 40, 136, 320, "mid"),
     "tiled": (w4.NVFP4, 40, 136, 256, "tiled"),
     "stream": (w4.INT4_G128, 1, 16384, 256, "auto"),
+    # 12 x 8192 A rows: the skinny kernel's ring variant (A through LDS copies)
+    "ring": (w4.MXFP4, 12, 80, 8192, "skinny"),
 }
 
 

@@ -124,6 +124,18 @@ __device__ __forceinline__ void lds_dma_b128(rsrc_t r, uint32_t lds_addr, uint32
       : "s"(lds_addr), "v"(voff), "s"(r)
       : "memory");
 }
+__device__ __forceinline__ void lds_dma_b32(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
 __device__ __forceinline__ void lds_dma_b16(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
   uint32_t saved;
   asm volatile(

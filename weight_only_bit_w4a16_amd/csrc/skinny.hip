@@ -57,6 +57,126 @@ struct SkinnyGroup {
   int rows;  // weight rows (output columns) per workgroup, 1 .. 16
 };
 
+// One k-block of 128 codes into acc: a[j] is the lane's A fragment of MFMA
+// step j (32 codes), q[j] its 8 codes of that step, sraw / zraw the raw scale
+// (and zero) bytes of the lane's chunk.
+//   int4 g128: the +code and -zero products go to separate accumulators that
+//     follow the same rounding sequence, so a k-block whose codes all equal
+//     the zero point cancels to exactly 0.  EVEN_ODD: A sits in LDS in the
+//     even / odd k order of the shorter decode, and the codes convert in that
+//     order; otherwise in natural k order, like A.
+//   int4 g32 / g64: groups shorter than a k-block; the lane's chunk has one
+//     group, whose (code - zero) * scale is applied in the decode (one bf16
+//     rounding per weight, a weight equal to its zero point exactly 0).
+//   NVFP4: chunk = two blocks of 16, one e4m3 scale each (low byte first).
+//   MXFP4: chunk = one block of 32, one e8m0 scale.
+template <int FMT, bool EVEN_ODD>
+__device__ __forceinline__ f32x4_t kblock_mac(const u32x4_t (&a)[4], const u32x4_t& q, uint32_t sraw,
+                                              uint32_t zraw, f32x4_t acc) {
+  if constexpr (FMT == kInt4) {
+    const u32x4_t nz = int4_neg_zero(zraw);
+    f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t b = EVEN_ODD ? int4x8_to_bf16_exact(q[j]) : int4x8_to_bf16_natural(q[j]);
+      dp = mfma16x16x32(a[j], b, dp);
+      dn = mfma16x16x32(a[j], nz, dn);
+    }
+    const float s = bf16_bits_to_f32(sraw);
+    acc[0] = __builtin_fmaf(s, dp[0] + dn[0], acc[0]);
+    acc[1] = __builtin_fmaf(s, dp[1] + dn[1], acc[1]);
+    acc[2] = __builtin_fmaf(s, dp[2] + dn[2], acc[2]);
+    acc[3] = __builtin_fmaf(s, dp[3] + dn[3], acc[3]);
+  } else if constexpr (is_int4(FMT)) {
+    const float s = bf16_bits_to_f32(sraw);
+    const float zf = (float)zraw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[j], int4x8_to_bf16_weights(q[j], s, zf), acc);
+  } else if constexpr (FMT == kNvfp4) {
+    const float s0 = e4m3_magnitude(sraw & 0xFFu);
+    const float s1 = e4m3_magnitude(sraw >> 8);
+    acc = mfma16x16x32(a[0], fp4x8_to_bf16_fscale(q[0], s0), acc);
+    acc = mfma16x16x32(a[1], fp4x8_to_bf16_fscale(q[1], s0), acc);
+    acc = mfma16x16x32(a[2], fp4x8_to_bf16_fscale(q[2], s1), acc);
+    acc = mfma16x16x32(a[3], fp4x8_to_bf16_fscale(q[3], s1), acc);
+  } else {
+    const float es = e8m0_as_exponent_scale(sraw);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[j], fp4x8_to_bf16_escale(q[j], es), acc);
+  }
+  return acc;
+}
+
+// The split-K sum over the waves' partials red[w * 64 + lane] (w = 0 ..
+// waves-1, in order) and the store of this workgroup's outputs, plain or
+// through the fused epilogue; run by wave 0.  Lane (nl, g) holds rows
+// m0 + 4g .. m0 + 4g + 3 of column n = n0 + nl; rows / arows bound the
+// workgroup's columns / A rows.
+template <bool OUT_F32>
+__device__ __forceinline__ void skinny_store(const f32x4_t* red, int waves, int lane, int nl, int g,
+                                             int rows, int arows, int m0, int n, int M, int N, void* C,
+                                             const Epilogue& epi) {
+  // the plain store and the fused epilogue are separate paths (one uniform
+  // branch; the plain path carries no epilogue code)
+  if (!epi.on) {
+    f32x4_t sum = red[lane];
+    for (int w = 1; w < waves; ++w) {
+      const f32x4_t v = red[w * 64 + lane];
+      sum[0] += v[0];
+      sum[1] += v[1];
+      sum[2] += v[2];
+      sum[3] += v[3];
+    }
+    if (nl >= rows) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 4 * g + i;
+      if (m < M) {
+        if constexpr (OUT_F32) {
+          reinterpret_cast<float*>(C)[(int64_t)m * N + n] = sum[i];
+        } else {
+          reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n] = (__bf16)sum[i];
+        }
+      }
+    }
+    return;
+  }
+  // epilogue operands first, all in one round trip (the residual may alias
+  // C, so the compiler could not hoist them over the stores itself)
+  float epi_b = 0.f, epi_r[4] = {0.f, 0.f, 0.f, 0.f};
+  if (nl < rows) {
+    if (epi.bias) epi_b = bf16_bits_to_f32(epi.bias[n]);
+    if (epi.res) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i < arows) epi_r[i] = residual_at<OUT_F32>(epi.res, (int64_t)(m0 + 4 * g + i) * N + n);
+    }
+  }
+  f32x4_t sum = red[lane];
+  for (int w = 1; w < waves; ++w) {
+    const f32x4_t v = red[w * 64 + lane];
+    sum[0] += v[0];
+    sum[1] += v[1];
+    sum[2] += v[2];
+    sum[3] += v[3];
+  }
+  if (nl >= rows) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 4 * g + i;
+    if (m < M) {
+      const int64_t mn = (int64_t)m * N + n;
+      const float v = epilogue_value(epi, sum[i], epi_b, epi_r[i]);
+      if constexpr (OUT_F32) {
+        reinterpret_cast<float*>(C)[mn] = v;
+      } else {
+        reinterpret_cast<__bf16*>(C)[mn] = (__bf16)v;
+      }
+    }
+  }
+}
+
 // FULL: K % 128 == 0, so every chunk of a k-block below KB exists and the
 // validity of a k-block is the same for the whole wave.
 // S_LDS: the workgroup's scale (and zero) bytes are copied to LDS once, in
@@ -288,46 +408,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
           sraw[u] = sb[nl * groups + (ok ? c : 0)];
         }
       }
-      if constexpr (FMT == kInt4) {
-        // the +code and -zero products go to separate accumulators that
-        // follow the same rounding sequence, so a k-block whose codes all
-        // equal the zero point cancels to exactly 0.  With A in LDS (already
-        // in the even / odd k order of the shorter decode) the codes convert
-        // in that order; otherwise in natural k order, like A.
-        const u32x4_t nz = int4_neg_zero(zraw[u]);
-        f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4_t b = A_LDS ? int4x8_to_bf16_exact(q[u][j]) : int4x8_to_bf16_natural(q[u][j]);
-          dp = mfma16x16x32(a[u][j], b, dp);
-          dn = mfma16x16x32(a[u][j], nz, dn);
-        }
-        const float s = bf16_bits_to_f32(sraw[u]);
-        acc[0] = __builtin_fmaf(s, dp[0] + dn[0], acc[0]);
-        acc[1] = __builtin_fmaf(s, dp[1] + dn[1], acc[1]);
-        acc[2] = __builtin_fmaf(s, dp[2] + dn[2], acc[2]);
-        acc[3] = __builtin_fmaf(s, dp[3] + dn[3], acc[3]);
-      } else if constexpr (is_int4(FMT)) {
-        // groups shorter than a k-block: the lane's chunk has one group,
-        // whose (code - zero) * scale is applied in the decode (one bf16
-        // rounding per weight, a weight equal to its zero point exactly 0)
-        const float s = bf16_bits_to_f32(sraw[u]);
-        const float zf = (float)zraw[u];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[u][j], int4x8_to_bf16_weights(q[u][j], s, zf), acc);
-      } else if constexpr (FMT == kNvfp4) {
-        const float s0 = e4m3_magnitude(sraw[u] & 0xFFu);
-        const float s1 = e4m3_magnitude(sraw[u] >> 8);
-        acc = mfma16x16x32(a[u][0], fp4x8_to_bf16_fscale(q[u][0], s0), acc);
-        acc = mfma16x16x32(a[u][1], fp4x8_to_bf16_fscale(q[u][1], s0), acc);
-        acc = mfma16x16x32(a[u][2], fp4x8_to_bf16_fscale(q[u][2], s1), acc);
-        acc = mfma16x16x32(a[u][3], fp4x8_to_bf16_fscale(q[u][3], s1), acc);
-      } else {
-        const float es = e8m0_as_exponent_scale(sraw[u]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[u][j], fp4x8_to_bf16_escale(q[u][j], es), acc);
-      }
+      acc = kblock_mac<FMT, A_LDS>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc);
     }
   };
 
@@ -364,64 +445,184 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   red[wave][lane] = acc;
   lds_barrier();
   if (wave != 0) return;
-  // the plain store and the fused epilogue are separate paths (one uniform
-  // branch; the plain path carries no epilogue code)
-  if (!epi.on) {
-    f32x4_t sum = red[0][lane];
-    for (int w = 1; w < waves; ++w) {
-      const f32x4_t v = red[w][lane];
-      sum[0] += v[0];
-      sum[1] += v[1];
-      sum[2] += v[2];
-      sum[3] += v[3];
-    }
-    if (nl >= rows) return;
+  skinny_store<OUT_F32>(&red[0][0], waves, lane, nl, g, rows, arows, m0, n, M, N, C, epi);
+}
+
+// ---- ring variant: every per-k-block operand through LDS copies ----------
+//
+// For A slices too large for the one-time LDS copy (e.g. 16 rows x 8192).
+// K is split over kRingVirt = 8 virtual waves: virtual wave v sums k-blocks
+// v, v + 8, v + 16, ... in that order, and the 8 partial sums are added in
+// order v = 0 .. 7, whatever the number of real waves W = 8 / R: real wave w
+// computes k-blocks w, w + W, w + 2W, ... and its j-th goes to accumulator
+// j % R (virtual wave w + W (j % R)).  So every W gives the same bits, and a
+// grouped launch (more workgroups, possibly another W) equals the single
+// ones.  The A rows (16 x 256
+// bytes) and the weight rows (16 x 64 bytes) of each k-block arrive by
+// asynchronous global -> LDS copies in one of the wave's D ring slots, issued
+// D k-blocks ahead, so the copies of the next D - 1 k-blocks are in flight
+// while one is computed.  The scale (and zero) window arrives the same way,
+// once.  No operand goes through a load the compiler can see, so every wait is
+// an explicit count of the copies issued after the one needed (vmcnt retires
+// in issue order) and never includes later copies.
+// LDS: scale window, zero window (int4), W * D slots of kRingSlot bytes, then
+// kRingVirt * 64 f32x4 partial sums.
+constexpr uint32_t kRingSlot = 5120;  // A 16 x 256 bytes, then weights 16 x 64 bytes
+constexpr int kRingVirt = 8;          // virtual waves of the K split
+
+// wait until at most `later` k-blocks' copies (5 each) are still in flight
+template <int D>
+__device__ __forceinline__ void ring_wait(int later) {
+  static_assert(D >= 2 && D <= 4, "ring depth");
+  if (D > 3 && later >= 3) {
+    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+  } else if (D > 2 && later >= 2) {
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  } else if (later >= 1) {
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// bytes of a copied window of `bytes` (plus <= 3 before and after it for
+// dword alignment), whole 256-byte copy instructions
+__host__ __device__ constexpr uint32_t ring_window_cap(uint32_t bytes) {
+  return (bytes + 6u + 255u) / 256u * 256u;
+}
+
+template <int FMT, bool OUT_F32, int D, int R, bool FULL, bool GROUPED>
+__global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint16_t* __restrict__ A,
+                                                                     SkinnyGroup grp, int M, int K,
+                                                                     Epilogue epi) {
+  const SkinnyMember& mem = grp.m[GROUPED ? (int)blockIdx.z : 0];
+  const uint8_t* packed = mem.packed;
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(mem.scales);
+  const uint8_t* zeros = mem.zeros;
+  void* C = mem.C;
+  const int N = mem.N;
+  const int n0 = (int)blockIdx.x * grp.rows;
+  if (GROUPED && n0 >= N) return;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int waves = kRingVirt / R;  // the launch has exactly these
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int m0 = blockIdx.y * 16;
+  const int n = n0 + nl;
+  const int chunks = K >> 5;
+  const int KB = (chunks + 3) >> 2;
+  constexpr int G = FormatTraits<FMT>::kGroup;
+  constexpr int SB = is_int4(FMT) ? 2 : 1;
+  constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
+  const int groups = K / G;
+  const int rows = min(grp.rows, N - n0);
+  const int arows = min(16, M - m0);
+
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
+
+  const uint32_t s_cap = ring_window_cap(16u * (uint32_t)groups * SB);
+  const uint32_t z_cap = is_int4(FMT) ? ring_window_cap(16u * (uint32_t)groups) : 0u;
+  const uint32_t base = lds_address(lds);
+  const uint32_t my_ring = s_cap + z_cap + (uint32_t)wave * (uint32_t)(D * kRingSlot);
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + s_cap + z_cap + (uint32_t)waves * (D * kRingSlot));
+
+  // window copies: dwords from the 4-byte aligned address at or below the
+  // block's start (delta bytes before it); instruction t of the window moves
+  // dwords 64t .. 64t+63, and the waves take turns
+  auto window = [&](const uint8_t* start, uint32_t bytes, uint32_t lds_off) {
+    const uintptr_t al = reinterpret_cast<uintptr_t>(start) & ~(uintptr_t)3;
+    const uint32_t delta = (uint32_t)(reinterpret_cast<uintptr_t>(start) - al);
+    const uint32_t words = (delta + bytes + 3u) / 4u;  // may read <= 3 bytes past the block (same page)
+    const rsrc_t r = make_rsrc(reinterpret_cast<const void*>(al), words * 4u);
+    const int instrs = (int)((words + 63u) / 64u);
+    for (int t = wave; t < instrs; t += waves)
+      lds_dma_b32(r, base + lds_off + (uint32_t)t * 256u, ((uint32_t)t * 64u + (uint32_t)lane) * 4u);
+    return delta;
+  };
+  const uint32_t s_delta = window(scales + (int64_t)n0 * groups * SB, (uint32_t)(rows * groups * SB), 0u);
+  uint32_t z_delta = 0;
+  if constexpr (is_int4(FMT)) z_delta = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), s_cap);
+
+  // this wave's k-blocks: kb = i * waves + wave, i = 0 .. nk-1
+  const int nk = wave < KB ? (KB - 1 - wave) / waves + 1 : 0;
+  // k-block i -> slot i % D.  A: instruction r4 moves rows 4 r4 .. 4 r4 + 3,
+  // lane -> row 4 r4 + l/16 and LDS chunk l%16, which holds 16-byte chunk
+  // (l%16) ^ row of the row's 256 bytes (the fragment reads of 16 rows then
+  // hit distinct banks).  Weights: lane -> row l/4, 16-byte chunk l%4.
+  auto issue = [&](int i) {
+    const int kb = i * waves + wave;
+    const uint32_t slot = base + my_ring + (uint32_t)(i % D) * kRingSlot;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 4 * g + i;
-      if (m < M) {
-        if constexpr (OUT_F32) {
-          reinterpret_cast<float*>(C)[(int64_t)m * N + n] = sum[i];
-        } else {
-          reinterpret_cast<__bf16*>(C)[(int64_t)m * N + n] = (__bf16)sum[i];
-        }
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int r = 4 * r4 + (lane >> 4);
+      const int ch = (lane & 15) ^ r;
+      const bool ok = FULL || kb * 128 + 8 * ch < K;
+      lds_dma_b128(ar, slot + (uint32_t)r4 * 1024u,
+                   ok ? ((uint32_t)r * (uint32_t)K + (uint32_t)kb * 128u + 8u * (uint32_t)ch) * 2u : kBufferOOB);
     }
-    return;
-  }
-  // epilogue operands first, all in one round trip (the residual may alias
-  // C, so the compiler could not hoist them over the stores itself)
-  float epi_b = 0.f, epi_r[4] = {0.f, 0.f, 0.f, 0.f};
-  if (nl < rows) {
-    if (epi.bias) epi_b = bf16_bits_to_f32(epi.bias[n]);
-    if (epi.res) {
+    const int wrow = lane >> 2, wch = lane & 3;
+    const bool okw = FULL || kb * 4 + wch < chunks;
+    lds_dma_b128(wr, slot + 4096u,
+                 okw ? (uint32_t)wrow * rowb + (uint32_t)kb * 64u + (uint32_t)wch * 16u : kBufferOOB);
+  };
+  const int first = nk < D ? nk : D;
+  for (int i = 0; i < first; ++i) issue(i);
+  // the window (issued first) and k-block 0 have landed in this wave's part;
+  // after the barrier every wave's part has
+  ring_wait<D>(first - 1);
+  lds_barrier();
+
+  f32x4_t acc[R];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * g + i < arows) epi_r[i] = residual_at<OUT_F32>(epi.res, (int64_t)(m0 + 4 * g + i) * N + n);
-    }
-  }
-  f32x4_t sum = red[0][lane];
-  for (int w = 1; w < waves; ++w) {
-    const f32x4_t v = red[w][lane];
-    sum[0] += v[0];
-    sum[1] += v[1];
-    sum[2] += v[2];
-    sum[3] += v[3];
-  }
-  if (nl >= rows) return;
+  for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* sb = lds + s_delta;
+  const uint8_t* zb = lds + s_cap + z_delta;
+  for (int i0 = 0; i0 < nk; i0 += R) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 4 * g + i;
-    if (m < M) {
-      const int64_t mn = (int64_t)m * N + n;
-      const float v = epilogue_value(epi, sum[i], epi_b, epi_r[i]);
-      if constexpr (OUT_F32) {
-        reinterpret_cast<float*>(C)[mn] = v;
-      } else {
-        reinterpret_cast<__bf16*>(C)[mn] = (__bf16)v;
-      }
+   for (int r = 0; r < R; ++r) {
+    const int i = i0 + r;
+    if (i >= nk) break;  // wave-uniform
+    if (i > 0) ring_wait<D>(min(D - 1, nk - 1 - i));
+    const int kb = i * waves + wave;
+    const uint8_t* slot = lds + my_ring + (uint32_t)(i % D) * kRingSlot;
+    u32x4_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[j] = *reinterpret_cast<const u32x4_t*>(slot + nl * 256 + (((4 * g + j) ^ nl) * 16));
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(slot + 4096 + (nl * 4 + g) * 16);
+    // this lane's scale (and zero) bytes; past K the weights and A are zero,
+    // so any finite scale will do
+    const int c = kb * 4 + g;
+    const bool ok = FULL || c < chunks;
+    uint32_t sraw, zraw = 0u;
+    if constexpr (is_int4(FMT)) {
+      const int gi = nl * groups + (ok ? (FMT == kInt4 ? kb : c >> GS) : 0);
+      sraw = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
+      zraw = zb[gi];
+    } else if constexpr (FMT == kNvfp4) {
+      sraw = *reinterpret_cast<const uint16_t*>(sb + nl * groups + 2 * (ok ? c : 0));
+    } else {
+      sraw = sb[nl * groups + (ok ? c : 0)];
     }
+    acc[r] = kblock_mac<FMT, false>(a, q, sraw, zraw, acc[r]);
+    if (i + D < nk) {
+      // the slot's reads have completed before its next copy is issued
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(i + D);
+    }
+   }
   }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) red[(wave + waves * r) * 64 + lane] = acc[r];
+  lds_barrier();
+  if (wave != 0) return;
+  skinny_store<OUT_F32>(red, kRingVirt, lane, nl, g, rows, arows, m0, n, M, N, C, epi);
 }
 
 // ---- streaming variant: one workgroup walks many column tiles -------------
@@ -694,35 +895,38 @@ hipError_t launch_s(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim
   return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, false>(a, grp, grid, block, lds_a + lds_dma);
 }
 
-template <int FMT, bool OUT_F32, int U>
-hipError_t launch_u(const GroupedArgs& a, int waves) {
-  static const int rows_env = [] {  // W4A16_SKINNY_ROWS=1..16 fixes the rows (tuning)
+// Rows per workgroup: 16 unless fewer make the workgroup count fill whole
+// rounds of 256 (one per CU) better -- e.g. N = 3072 gives 192 workgroups of
+// 16 rows but 256 of 12.  Lanes of the missing rows read zeros.  A workgroup
+// keeps >= 12 KB of weights (fewer rows would only add per-workgroup
+// overhead).  W4A16_SKINNY_ROWS=1..16 fixes the rows (tuning).
+int skinny_rows(const GroupedArgs& a) {
+  static const int rows_env = [] {
     const char* e = getenv("W4A16_SKINNY_ROWS");
     const int r = e ? atoi(e) : 0;
     return r >= 1 && r <= 16 ? r : 0;
   }();
-  // Rows per workgroup: 16 unless fewer make the workgroup count fill whole
-  // rounds of 256 (one per CU) better -- e.g. N = 3072 gives 192 workgroups
-  // of 16 rows but 256 of 12.  Lanes of the missing rows read zeros.
-  // A workgroup keeps >= 12 KB of weights (fewer rows would only add
-  // per-workgroup overhead).
+  if (rows_env) return rows_env;
   int rows = 16;
-  if (!rows_env) {
-    const int64_t r_min = (12288 + a.K / 2 - 1) / (a.K / 2);
-    double best = -1.0;
-    for (int r = 16; r >= (r_min > 4 ? (int)(r_min < 16 ? r_min : 16) : 4); --r) {
-      int64_t wgs = 0;
-      for (int i = 0; i < a.count; ++i) wgs += (a.N[i] + r - 1) / r;
-      wgs *= (a.M + 15) / 16;
-      const double fill = (double)wgs / (double)(256 * ((wgs + 255) / 256));
-      if (fill > best + 0.02) {
-        best = fill;
-        rows = r;
-      }
+  const int64_t r_min = (12288 + a.K / 2 - 1) / (a.K / 2);
+  double best = -1.0;
+  for (int r = 16; r >= (r_min > 4 ? (int)(r_min < 16 ? r_min : 16) : 4); --r) {
+    int64_t wgs = 0;
+    for (int i = 0; i < a.count; ++i) wgs += (a.N[i] + r - 1) / r;
+    wgs *= (a.M + 15) / 16;
+    const double fill = (double)wgs / (double)(256 * ((wgs + 255) / 256));
+    if (fill > best + 0.02) {
+      best = fill;
+      rows = r;
     }
-  } else {
-    rows = rows_env;
   }
+  return rows;
+}
+
+// The launch's members and its grid: x = column tiles of `rows` (of the
+// widest member), y = 16-row slices of A, z = members; a member with fewer
+// tiles than the widest has workgroups that exit at once.
+SkinnyGroup skinny_group(const GroupedArgs& a, int rows, dim3& grid) {
   SkinnyGroup grp = {};
   int64_t max_n = 0;
   for (int i = 0; i < a.count; ++i) {
@@ -734,9 +938,70 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
     max_n = a.N[i] > max_n ? a.N[i] : max_n;
   }
   grp.rows = rows;
-  // members along z; a member with fewer tiles than the widest has
-  // workgroups that exit at once
-  dim3 grid((unsigned)((max_n + rows - 1) / rows), (unsigned)((a.M + 15) / 16), (unsigned)a.count);
+  grid = dim3((unsigned)((max_n + rows - 1) / rows), (unsigned)((a.M + 15) / 16), (unsigned)a.count);
+  return grp;
+}
+
+template <int FMT, bool OUT_F32, int D, int R, bool FULL>
+hipError_t launch_ring_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, unsigned lds) {
+  const dim3 block(64 * (kRingVirt / R));
+  if (a.count > 1)
+    hipLaunchKernelGGL((skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, true>), grid, block, lds, a.stream,
+                       a.A, grp, (int)a.M, (int)a.K, a.epi);
+  else
+    hipLaunchKernelGGL((skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, false>), grid, block, lds, a.stream,
+                       a.A, grp, (int)a.M, (int)a.K, a.epi);
+  return hipGetLastError();
+}
+template <int FMT, bool OUT_F32, int D, int R>
+hipError_t launch_ring_f(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, unsigned lds) {
+  return a.K % 128 == 0 ? launch_ring_k<FMT, OUT_F32, D, R, true>(a, grp, grid, lds)
+                        : launch_ring_k<FMT, OUT_F32, D, R, false>(a, grp, grid, lds);
+}
+
+// The ring variant for A slices past the one-time LDS copy.  A grid of one
+// round (<= 256 workgroups, one per CU): 8 waves with 3 slots each (120 KB of
+// copies in flight per workgroup).  More rounds: 4 waves with 2 slots (40 KB
+// plus the windows), so that several workgroups share a CU and the next
+// round's copies overlap the current one's arithmetic (measured, e.g.
+// 8 x 32000 x 4096 int4: 36.6 us with the per-pass kernel, 26.6 with 8 x 3
+// slots, 23.7 with 4 x 2).  2 slots when the scale windows leave no room for
+// 3; false when even that does not fit the 160 KB of LDS.  Tuning:
+// W4A16_SKINNY_RING=0 never, =8 / =4 force 8 x 3 / 4 x 2 (8 x 2 when the
+// windows leave no room for 3 slots).
+template <int FMT, bool OUT_F32>
+bool try_ring(const GroupedArgs& a, hipError_t& err) {
+  static const int env = [] {
+    const char* e = getenv("W4A16_SKINNY_RING");
+    return e ? atoi(e) : 1;
+  }();
+  if (env == 0) return false;
+  constexpr int SB = is_int4(FMT) ? 2 : 1;
+  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t win = ring_window_cap((uint32_t)(16 * groups * SB)) +
+                      (is_int4(FMT) ? ring_window_cap((uint32_t)(16 * groups)) : 0);
+  dim3 grid;
+  const SkinnyGroup grp = skinny_group(a, skinny_rows(a), grid);
+  const bool one_round = env == 8 || (env != 4 && (int64_t)grid.x * grid.y * grid.z <= 256);
+  auto lds_of = [&](int w, int d) { return win + (int64_t)w * d * kRingSlot + (int64_t)kRingVirt * 1024; };
+  constexpr int64_t kLds = 160 * 1024;
+  if (!one_round && lds_of(4, 2) <= kLds) {
+    err = launch_ring_f<FMT, OUT_F32, 2, 2>(a, grp, grid, (unsigned)lds_of(4, 2));
+  } else if (lds_of(8, 3) <= kLds) {
+    err = launch_ring_f<FMT, OUT_F32, 3, 1>(a, grp, grid, (unsigned)lds_of(8, 3));
+  } else if (lds_of(8, 2) <= kLds) {
+    err = launch_ring_f<FMT, OUT_F32, 2, 1>(a, grp, grid, (unsigned)lds_of(8, 2));
+  } else {
+    return false;
+  }
+  return true;
+}
+
+template <int FMT, bool OUT_F32, int U>
+hipError_t launch_u(const GroupedArgs& a, int waves) {
+  const int rows = skinny_rows(a);
+  dim3 grid;
+  const SkinnyGroup grp = skinny_group(a, rows, grid);
   // stage A in LDS when the workgroup's A slice fits its staging registers
   const int64_t arows = a.M < 16 ? a.M : 16;
   const int64_t a_bytes = arows * a.K * 2;
@@ -903,6 +1168,10 @@ hipError_t launch_fmt(const GroupedArgs& a) {
   // U k-blocks (4 KB each): keep those within 128 KB
   const int64_t arows = a.M < 16 ? a.M : 16;
   const bool a_big = arows * a.K * 2 > (int64_t)kAStage * 16 * 64 * waves || arows * a.K * 2 > 64 * 1024;
+  if (a_big) {
+    hipError_t err = hipSuccess;
+    if (try_ring<FMT, OUT_F32>(a, err)) return err;
+  }
   if (!skinny_u_env() && a_big && waves * U > 32) U = 32 / waves > 0 ? 32 / waves : 1;
   if (U == 1) return launch_u<FMT, OUT_F32, 1>(a, waves);
   if (U == 2) return launch_u<FMT, OUT_F32, 2>(a, waves);
