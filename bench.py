@@ -44,15 +44,17 @@ WORKLOADS = {
     "mxfp4_m4096": (2, 4096, 8192, 3072, "bf16"),
 }
 CHAIN = "decode_chain_3b_int4_m1"
-GROUP = {0: 128, 1: 16, 2: 32, 3: 32, 4: 64}   # int4 g128, NVFP4, MXFP4, int4 g32, int4 g64
-INT4_FORMATS = (0, 3, 4)
+# int4 g128, NVFP4, MXFP4, int4 g32, int4 g64, symmetric int4 (g128, no zeros)
+GROUP = {0: 128, 1: 16, 2: 32, 3: 32, 4: 64, 5: 128}
+INT4_FORMATS = (0, 3, 4, 5)  # bf16 scales
+ZERO_FORMATS = (0, 3, 4)     # with a zero array
 
 
 def algorithmic_bytes(fmt, M, N, K, out):
     """Bytes the method must move once: packed + scales (+ zeros) + A + C."""
     G = GROUP[fmt]
     int4 = fmt in INT4_FORMATS
-    weight = N * K // 2 + N * (K // G) * (2 if int4 else 1) + (N * (K // G) if int4 else 0)
+    weight = N * K // 2 + N * (K // G) * (2 if int4 else 1) + (N * (K // G) if fmt in ZERO_FORMATS else 0)
     io = M * K * 2 + M * N * (4 if out == "f32" else 2)
     return weight, weight + io
 
@@ -98,7 +100,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "skinny", "mid", "tiled"])
     ap.add_argument("--shape", default=None,
                     help="custom single-GEMM workload 'format,M,N,K' (format 0 int4 g128, 1 nvfp4, "
-                         "2 mxfp4, 3 int4 g32, 4 int4 g64; bf16 out) instead of --workload")
+                         "2 mxfp4, 3 int4 g32, 4 int4 g64, 5 symmetric int4; bf16 out) instead of --workload")
     ap.add_argument("--epilogue", default=None, choices=["none", "relu", "silu", "gelu_tanh"],
                     help="single-GEMM workloads: fuse a bf16 bias, a residual (beta = 1) and this "
                          "activation into the GEMM (w4a16_gemm_ex); their bytes count as traffic")
@@ -154,7 +156,7 @@ def main():
         p = torch.from_numpy(case.packed).to(dev)
         if case.fmt in INT4_FORMATS:
             s = torch.from_numpy(case.scales.view(np.int16)).to(dev).view(torch.bfloat16)
-            z = torch.from_numpy(case.zeros).to(dev)
+            z = torch.from_numpy(case.zeros).to(dev) if case.zeros is not None else None
         else:
             s = torch.from_numpy(case.scales).to(dev)
             z = None

@@ -17,7 +17,11 @@
  *     paragraph -- LOW nibble of byte (n, i) is input 2i, HIGH nibble 2i+1.
  *     The group is a configuration value there (`group`, 128 in its
  *     fixture); W4A16_INT4_G32 / _G64 are the same format with groups of 32
- *     and 64.
+ *     and 64.  W4A16_INT4_SYM is its symmetric form: no zero array, every
+ *     group's zero point is the midpoint 8 of the codes 0..15, value =
+ *     (code - 8) * scale, groups of 128 (the page measures only what ignoring
+ *     the zero point of ITS asymmetric weights costs, in its tolerance table;
+ *     the symmetric encoding itself is the usual reading, not the page's).
  *   - NVFP4: "Matmul2dFp4" (Mojo), methods run / run_smem_decode -- packed
  *     (N, K/2) uint8, scales (N, K/16) float8_e4m3fn, value =
  *     e2m1(code) * |scale|.
@@ -30,10 +34,11 @@
  * never allocates, frees or keeps them.  All arrays are row-major and dense:
  *   A       bf16  (M, K)                    16-byte aligned
  *   packed  uint8 (N, K/2)                  16-byte aligned
- *   scales  int4: bf16 (N, K/G), G = 128 / 32 / 64   2-byte aligned
+ *   scales  int4: bf16 (N, K/G), G = 128 / 32 / 64 (128 for INT4_SYM)   2-byte aligned
  *           NVFP4: e4m3 bytes (N, K/16)     2-byte aligned
  *           MXFP4: e8m0 bytes (N, K/32)
- *   zeros   int4: uint8 (N, K/G); must be NULL for NVFP4 / MXFP4
+ *   zeros   int4 G128 / G32 / G64: uint8 (N, K/G); must be NULL for
+ *           INT4_SYM, NVFP4 and MXFP4
  *   C       bf16 or fp32 (M, N)             aligned to its element size
  *   W       bf16 (N, K)                     16-byte aligned (dequant output)
  * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing and
@@ -67,6 +72,7 @@ extern "C" {
 #define W4A16_MXFP4 2       /* e2m1 codes, e8m0 scale per 32                  */
 #define W4A16_INT4_G32 3    /* the int4 format with groups of 32 inputs       */
 #define W4A16_INT4_G64 4    /* the int4 format with groups of 64 inputs       */
+#define W4A16_INT4_SYM 5    /* symmetric int4: bf16 scale per 128, zero 8     */
 #define W4A16_FORMAT_MASK 0xFF
 
 #define W4A16_OUT_BF16 0x000 /* C is bf16, rounded to nearest even (default) */
@@ -95,7 +101,8 @@ extern "C" {
                                  multiple of the group, M or N >= 2^31, or
                                  K > 2^22                                   */
 #define W4A16_ERR_NULL (-3)   /* a required pointer is NULL, or zeros is
-                                 non-NULL for an fp4 format                 */
+                                 non-NULL for a format without zeros
+                                 (INT4_SYM, NVFP4, MXFP4)                   */
 #define W4A16_ERR_ALIGN (-4)  /* a pointer violates its alignment           */
 #define W4A16_ERR_HIP (-5)    /* the HIP runtime rejected a launch          */
 #define W4A16_ERR_EPILOGUE (-6) /* unknown activation, nonzero reserved field,
@@ -156,7 +163,7 @@ int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* sca
  *     C[i] = A . dequant(packed[i], scales[i], zeros[i])^T,  C[i] (M, N[i]).
  * `packed`, `scales`, `C` and `N` are HOST arrays of `count` entries (device
  * pointers / sizes), read during the call only; `zeros` is such an array for
- * int4 and must be NULL for NVFP4 / MXFP4.  Each member follows the layout,
+ * the int4 formats with zeros and must be NULL for INT4_SYM, NVFP4 and MXFP4.  Each member follows the layout,
  * alignment and accuracy rules of w4a16_gemm.  1 <= count <= W4A16_MAX_GROUP
  * (else W4A16_ERR_SHAPE); members with N[i] == 0 are skipped and their
  * pointers not checked.  The skinny path computes all members in ONE launch;

@@ -17,8 +17,10 @@ arrays to it.  Sources, per function, are cited in the C file:
 
 Formats: ``INT4_G128 = 0``, ``NVFP4 = 1``, ``MXFP4 = 2``, and the same int4 with
 groups of 32 / 64 inputs, ``INT4_G32 = 3``, ``INT4_G64 = 4`` (the group is a
-configuration value of the int4 page, 128 in its fixture).  Scales are passed
-as their raw storage: uint16 bf16 bits (int4) or uint8 bytes (e4m3 / e8m0).
+configuration value of the int4 page, 128 in its fixture), and symmetric int4
+``INT4_SYM = 5`` (groups of 128, no zero array, zero point 8).  Scales are
+passed as their raw storage: uint16 bf16 bits (int4) or uint8 bytes (e4m3 /
+e8m0).
 """
 from __future__ import annotations
 
@@ -28,9 +30,10 @@ import subprocess
 
 import numpy as np
 
-INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64 = 0, 1, 2, 3, 4
-GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64}
-INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64)
+INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64, INT4_SYM = 0, 1, 2, 3, 4, 5
+GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64, INT4_SYM: 128}
+INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64, INT4_SYM)  # bf16 scales
+ZERO_FORMATS = (INT4_G128, INT4_G32, INT4_G64)  # with a zero array
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "w4a16_oracle.c")

@@ -45,6 +45,11 @@
  *   - the int4 group is a parameter of the format ([KB]'s configuration
  *     carries it as `group`, 128 in its fixture): formats 3 and 4 are the
  *     same asymmetric int4 with groups of 32 and 64 contiguous inputs.
+ *   - format 5, symmetric int4: [KB] names only the cost of ignoring its
+ *     weights' zero point; the symmetric encoding read here is the usual one
+ *     for unsigned 4-bit codes -- no zero array, the zero point of every
+ *     group is the code midpoint 8, value = (code - 8) * scale, bf16 scale
+ *     per 128 contiguous inputs.
  *   - NaN inputs produce a NaN weight; the rounded bf16 NaN is 0x7FC0 (sign
  *     kept).
  */
@@ -59,10 +64,12 @@
 #define ORC_MXFP4 2
 #define ORC_INT4_G32 3
 #define ORC_INT4_G64 4
-#define ORC_NFORMATS 5
+#define ORC_INT4_SYM 5
+#define ORC_NFORMATS 6
 
 static int is_int4(int fmt) {
-  return fmt == ORC_INT4_G128 || fmt == ORC_INT4_G32 || fmt == ORC_INT4_G64;
+  return fmt == ORC_INT4_G128 || fmt == ORC_INT4_G32 || fmt == ORC_INT4_G64 ||
+         fmt == ORC_INT4_SYM;
 }
 
 /* ---- element decoders ---------------------------------------------------- */
@@ -148,6 +155,7 @@ static int64_t group_of(int fmt) {
     case ORC_NVFP4: return 16;
     case ORC_MXFP4: return 32;
     case ORC_INT4_G32: return 32;
+    case ORC_INT4_SYM: return 128;
     default: return 64; /* ORC_INT4_G64 */
   }
 }
@@ -169,7 +177,7 @@ double orc_weight(int fmt, const uint8_t* packed, const void* scales,
   unsigned code = code_at(packed, K, n, k);
   if (is_int4(fmt)) {
     double s = orc_bf16_value(((const uint16_t*)scales)[n * groups + g]);
-    int z = zeros[n * groups + g];
+    int z = (fmt == ORC_INT4_SYM) ? 8 : zeros[n * groups + g];
     return (double)((int)code - z) * s; /* subtraction first, then scale */
   }
   double v = orc_e2m1_value(code);

@@ -41,6 +41,7 @@ def test_python_constants_match_header():
     assert d["W4A16_NVFP4"] == w4.NVFP4
     assert d["W4A16_MXFP4"] == w4.MXFP4
     assert d["W4A16_INT4_G32"] == w4.INT4_G32 and d["W4A16_INT4_G64"] == w4.INT4_G64
+    assert d["W4A16_INT4_SYM"] == w4.INT4_SYM
     assert d["W4A16_OUT_F32"] == w4.OUT_F32
     assert d["W4A16_PATH_SKINNY"] == w4.PATH_SKINNY
     assert d["W4A16_PATH_TILED"] == w4.PATH_TILED
@@ -59,7 +60,7 @@ def test_epilogue_struct_layout():
 
 
 def test_version_and_strerror():
-    assert w4.version() == 103
+    assert w4.version() == 104
     for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP,
                  w4.ERR_EPILOGUE):
         assert w4.strerror(code) != "unknown status"
@@ -81,6 +82,8 @@ def test_path_choice():
     assert w4.gemm_path(w4.MXFP4, 129, 8192, 3072) == "tiled"        # 3 rounds
     assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "mid"      # 3 rounds
     assert w4.gemm_path(w4.INT4_G128, 193, 8192, 3072) == "tiled"
+    assert w4.gemm_path(w4.INT4_SYM, 192, 8192, 3072) == "mid"       # int4: 3 rounds
+    assert w4.gemm_path(w4.INT4_SYM, 193, 8192, 3072) == "tiled"
     assert w4.gemm_path(w4.INT4_G128, 384, 1024, 3072) == "mid"      # 192 workgroups
     assert w4.gemm_path(w4.INT4_G128, 400, 512, 3072) == "tiled"
     # a large tiled grid (>= 256 tiles): the mid kernel up to 48 rows
@@ -103,7 +106,8 @@ def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
 
 
 @pytest.mark.parametrize("fmt,M,N,K,expect", [
-    (5, 16, 64, 128, w4.ERR_FORMAT),                          # unknown format
+    (6, 16, 64, 128, w4.ERR_FORMAT),                          # unknown format
+    (w4.INT4_SYM, 16, 64, 96, w4.ERR_SHAPE),                  # symmetric int4: K % 128
     (w4.INT4_G64, 16, 64, 96, w4.ERR_SHAPE),                  # K % 64
     (w4.INT4_G32, 16, 64, 48, w4.ERR_SHAPE),                  # K % 32
     (w4.INT4_G128 | 0x4000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
@@ -117,7 +121,7 @@ def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
     (w4.MXFP4, 2 ** 31, 64, 64, w4.ERR_SHAPE),
 ])
 def test_gemm_rejects_format_and_shape(fmt, M, N, K, expect):
-    Z = PZ if (fmt & 0xFF) in w4.INT4_FORMATS else None
+    Z = PZ if (fmt & 0xFF) in w4.ZERO_FORMATS else None
     assert _gemm(fmt, Z=Z, M=M, N=N, K=K) == expect
 
 
@@ -131,6 +135,8 @@ def test_gemm_rejects_null_and_alignment():
     assert _gemm(w4.INT4_G64, Z=None) == w4.ERR_NULL
     assert _gemm(w4.INT4_G64, S=ctypes.c_void_p(0x100001)) == w4.ERR_ALIGN
     assert _gemm(w4.NVFP4, Z=PZ) == w4.ERR_NULL                  # fp4 takes none
+    assert _gemm(w4.INT4_SYM, Z=PZ) == w4.ERR_NULL               # symmetric int4 takes none
+    assert _gemm(w4.INT4_SYM, Z=None, S=ctypes.c_void_p(0x100001)) == w4.ERR_ALIGN
     odd = ctypes.c_void_p(0x100008)
     assert _gemm(w4.INT4_G128, A=odd) == w4.ERR_ALIGN
     assert _gemm(w4.INT4_G128, B=odd) == w4.ERR_ALIGN
@@ -192,6 +198,9 @@ def test_dequant_rejects_bad_arguments():
     assert lib.w4a16_dequant(w4.INT4_G128, PB, PS, PZ, PC, 4, 64, None) == w4.ERR_SHAPE
     assert lib.w4a16_dequant(w4.INT4_G128, PB, PS, None, PC, 4, 128, None) == w4.ERR_NULL
     assert lib.w4a16_dequant(w4.MXFP4, PB, PS, PZ, PC, 4, 64, None) == w4.ERR_NULL
+    assert lib.w4a16_dequant(w4.INT4_SYM, PB, PS, PZ, PC, 4, 128, None) == w4.ERR_NULL
+    assert lib.w4a16_dequant(w4.INT4_SYM, PB, PS, None, PC, 4, 64, None) == w4.ERR_SHAPE
+    assert lib.w4a16_dequant(6, PB, PS, None, PC, 4, 128, None) == w4.ERR_FORMAT
     assert lib.w4a16_dequant(w4.MXFP4, PB, PS, None, ctypes.c_void_p(0x100008), 4, 64,
                              None) == w4.ERR_ALIGN
 
@@ -213,7 +222,7 @@ def _grouped(fmt, count=3, N=(64, 32, 48), M=1, K=128, A=PA, packed=True, scales
     n = max(count, 1)
     mk = lambda base: (ctypes.c_void_p * n)(*[0x100000 * (base + 8 * i) for i in range(n)])
     P, S, Cs = mk(2), mk(3), mk(5)
-    Z = mk(4) if (zeros == "auto" and (fmt & 0xFF) in w4.INT4_FORMATS) or zeros is True else None
+    Z = mk(4) if (zeros == "auto" and (fmt & 0xFF) in w4.ZERO_FORMATS) or zeros is True else None
     if bad:
         arr, i, val = bad
         {"P": P, "S": S, "C": Cs, "Z": Z}[arr][i] = val
@@ -224,7 +233,9 @@ def _grouped(fmt, count=3, N=(64, 32, 48), M=1, K=128, A=PA, packed=True, scales
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(fmt=5), w4.ERR_FORMAT),
+    (dict(fmt=6), w4.ERR_FORMAT),
+    (dict(fmt=w4.INT4_SYM, zeros=True), w4.ERR_NULL),          # symmetric int4 takes no zeros
+    (dict(fmt=w4.INT4_SYM, K=192), w4.ERR_SHAPE),              # K % 128
     (dict(fmt=w4.INT4_G128, count=0), w4.ERR_SHAPE),
     (dict(fmt=w4.INT4_G64, K=96), w4.ERR_SHAPE),               # K % 64
     (dict(fmt=w4.INT4_G32, zeros=False), w4.ERR_NULL),

@@ -20,11 +20,12 @@ import os
 
 import torch
 
-INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64 = 0, 1, 2, 3, 4
-GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64}
+INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64, INT4_SYM = 0, 1, 2, 3, 4, 5
+GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64, INT4_SYM: 128}
 FORMAT_NAMES = {INT4_G128: "int4_g128", NVFP4: "nvfp4", MXFP4: "mxfp4",
-                INT4_G32: "int4_g32", INT4_G64: "int4_g64"}
-INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64)
+                INT4_G32: "int4_g32", INT4_G64: "int4_g64", INT4_SYM: "int4_sym"}
+INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64, INT4_SYM)  # bf16 scales
+ZERO_FORMATS = (INT4_G128, INT4_G32, INT4_G64)  # with a zero array (symmetric int4: zero point 8)
 OUT_BF16, OUT_F32 = 0x000, 0x100
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_MID = 0x0000, 0x1000, 0x2000, 0x3000
 PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "mid": PATH_MID, "tiled": PATH_TILED}
@@ -133,12 +134,12 @@ def _check_weights(fmt, packed, scales, zeros, N, K, device):
         raise ValueError(f"K={K} must be a multiple of 32 and of the group size {G}")
     _check(packed, "packed", (N, K // 2), 1, device)
     _check(scales, "scales", (N, K // G), 2 if fmt in INT4_FORMATS else 1, device)
-    if fmt in INT4_FORMATS:
+    if fmt in ZERO_FORMATS:
         if zeros is None:
-            raise ValueError("int4 weights need zeros")
+            raise ValueError("asymmetric int4 weights need zeros")
         _check(zeros, "zeros", (N, K // G), 1, device)
     elif zeros is not None:
-        raise ValueError("fp4 weights take no zeros")
+        raise ValueError(f"{FORMAT_NAMES[fmt]} weights take no zeros")
 
 
 def _epilogue(bias, residual, alpha, beta, activation, out, M, N, device):
@@ -222,7 +223,7 @@ def _grouped_args(fmt, A, weights, outs, out_dtype):
         P[i], S[i], Cs[i], Ns[i] = packed.data_ptr(), scales.data_ptr(), out.data_ptr(), N
         Z[i] = zeros.data_ptr() if zeros is not None else None
     flags = OUT_F32 if dt == torch.float32 else OUT_BF16
-    zarr = Z if fmt in INT4_FORMATS else None
+    zarr = Z if fmt in ZERO_FORMATS else None
     return flags, outs, (P, S, zarr, Cs, Ns), (M, K)
 
 

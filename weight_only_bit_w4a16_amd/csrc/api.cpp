@@ -12,12 +12,18 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows with 32-bit
 constexpr int64_t kMaxK = (int64_t)1 << 22;    // a 256-row tile of A fits a 32-bit byte offset
 
 bool is_int4(int fmt) {
+  return fmt == W4A16_INT4_G128 || fmt == W4A16_INT4_G32 || fmt == W4A16_INT4_G64 || fmt == W4A16_INT4_SYM;
+}
+// formats whose weights come with a zero array (required non-NULL; NULL
+// required for every other format)
+bool has_zeros(int fmt) {
   return fmt == W4A16_INT4_G128 || fmt == W4A16_INT4_G32 || fmt == W4A16_INT4_G64;
 }
 
 int group_of(int fmt) {
   switch (fmt) {
     case W4A16_INT4_G128: return 128;
+    case W4A16_INT4_SYM: return 128;
     case W4A16_NVFP4: return 16;
     case W4A16_INT4_G64: return 64;
     default: return 32;  // MXFP4, INT4_G32
@@ -30,7 +36,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_flags) {
   const int fmt = format & W4A16_FORMAT_MASK;
   const int flags = format & ~W4A16_FORMAT_MASK;
-  if (fmt > W4A16_INT4_G64) return W4A16_ERR_FORMAT;
+  if (fmt > W4A16_INT4_SYM) return W4A16_ERR_FORMAT;
   if (allow_flags) {
     if (flags & ~(W4A16_OUT_F32 | W4A16_PATH_MASK)) return W4A16_ERR_FORMAT;
   } else if (flags) {
@@ -79,7 +85,7 @@ hipError_t launch_path(int path, const w4a16::GemmArgs& a) {
 
 extern "C" {
 
-int w4a16_version(void) { return 103; }
+int w4a16_version(void) { return 104; }
 
 const char* w4a16_strerror(int status) {
   switch (status) {
@@ -88,7 +94,7 @@ const char* w4a16_strerror(int status) {
     case W4A16_ERR_SHAPE:
       return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^22, K % 32 == 0 and K a multiple "
              "of the format's group size (and 1 <= count <= W4A16_MAX_GROUP for a group)";
-    case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for an fp4 format";
+    case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for a format without zeros";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
     case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case W4A16_ERR_EPILOGUE:
@@ -121,7 +127,7 @@ int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* sca
   const bool out_f32 = (format & W4A16_OUT_F32) != 0;
   if (M == 0 || N == 0) return W4A16_OK;  // nothing is read or written
   if (!A || !packed || !scales || !C) return W4A16_ERR_NULL;
-  if (is_int4(fmt) ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
+  if (has_zeros(fmt) ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
   if (!aligned(A, 16) || !aligned(packed, 16)) return W4A16_ERR_ALIGN;
   if (fmt != W4A16_MXFP4 && !aligned(scales, 2)) return W4A16_ERR_ALIGN;
   const uintptr_t es = out_f32 ? 4 : 2;
@@ -175,11 +181,11 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
   for (int i = 0; i < count; ++i) active += N[i] > 0;
   if (M == 0 || active == 0) return W4A16_OK;  // nothing is read or written
   if (!A || !packed || !scales || !C) return W4A16_ERR_NULL;
-  if (is_int4(fmt) ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
+  if (has_zeros(fmt) ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
   if (!aligned(A, 16)) return W4A16_ERR_ALIGN;
   for (int i = 0; i < count; ++i) {
     if (N[i] == 0) continue;
-    if (!packed[i] || !scales[i] || !C[i] || (is_int4(fmt) && !zeros[i]))
+    if (!packed[i] || !scales[i] || !C[i] || (has_zeros(fmt) && !zeros[i]))
       return W4A16_ERR_NULL;
     if (!aligned(packed[i], 16)) return W4A16_ERR_ALIGN;
     if (fmt != W4A16_MXFP4 && !aligned(scales[i], 2)) return W4A16_ERR_ALIGN;
@@ -198,7 +204,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
       if (N[i] == 0) continue;
       g.packed[g.count] = static_cast<const uint8_t*>(packed[i]);
       g.scales[g.count] = scales[i];
-      g.zeros[g.count] = is_int4(fmt) ? static_cast<const uint8_t*>(zeros[i]) : nullptr;
+      g.zeros[g.count] = has_zeros(fmt) ? static_cast<const uint8_t*>(zeros[i]) : nullptr;
       g.C[g.count] = C[i];
       g.N[g.count] = N[i];
       ++g.count;
@@ -218,7 +224,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     a.A = static_cast<const uint16_t*>(A);
     a.packed = static_cast<const uint8_t*>(packed[i]);
     a.scales = scales[i];
-    a.zeros = is_int4(fmt) ? static_cast<const uint8_t*>(zeros[i]) : nullptr;
+    a.zeros = has_zeros(fmt) ? static_cast<const uint8_t*>(zeros[i]) : nullptr;
     a.C = C[i];
     a.M = M;
     a.N = N[i];
@@ -236,7 +242,7 @@ int w4a16_dequant(int format, const void* packed, const void* scales, const void
   const int fmt = format & W4A16_FORMAT_MASK;
   if (N == 0) return W4A16_OK;  // nothing is read or written
   if (!packed || !scales || !W) return W4A16_ERR_NULL;
-  if (is_int4(fmt) ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
+  if (has_zeros(fmt) ? !zeros : zeros != nullptr) return W4A16_ERR_NULL;
   if (!aligned(packed, 16) || !aligned(W, 16)) return W4A16_ERR_ALIGN;
   if (fmt != W4A16_MXFP4 && !aligned(scales, 2)) return W4A16_ERR_ALIGN;
   const hipError_t e = w4a16::launch_dequant(fmt, static_cast<const uint8_t*>(packed), scales,

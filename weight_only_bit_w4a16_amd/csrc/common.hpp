@@ -27,12 +27,21 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // kInt4: int4 with groups of 128 (one group per 128-code k-block);
-// kInt4G32 / kInt4G64: the same with groups of 32 / 64 codes.
-enum Format : int { kInt4 = 0, kNvfp4 = 1, kMxfp4 = 2, kInt4G32 = 3, kInt4G64 = 4 };
-constexpr int kFormats = 5;
+// kInt4G32 / kInt4G64: the same with groups of 32 / 64 codes;
+// kInt4Sym: groups of 128 with the fixed zero point 8 (no zero array).
+enum Format : int { kInt4 = 0, kNvfp4 = 1, kMxfp4 = 2, kInt4G32 = 3, kInt4G64 = 4, kInt4Sym = 5 };
+constexpr int kFormats = 6;
 
-// int4 formats: (code - zero) * scale with a bf16 scale and u8 zero per group
-constexpr bool is_int4(int fmt) { return fmt == kInt4 || fmt == kInt4G32 || fmt == kInt4G64; }
+// int4 formats: (code - zero) * scale with a bf16 scale per group; the zero
+// is a u8 per group, or 8 for the symmetric format
+constexpr bool is_int4(int fmt) {
+  return fmt == kInt4 || fmt == kInt4G32 || fmt == kInt4G64 || fmt == kInt4Sym;
+}
+// int4 formats that come with a zero array
+constexpr bool has_zeros(int fmt) { return fmt == kInt4 || fmt == kInt4G32 || fmt == kInt4G64; }
+// int4 formats whose group is the 128-code k-block
+constexpr bool is_int4_g128(int fmt) { return fmt == kInt4 || fmt == kInt4Sym; }
+constexpr uint32_t kSymZero = 8;  // the symmetric format's zero point
 
 template <int FMT>
 struct FormatTraits;
@@ -55,6 +64,10 @@ struct FormatTraits<kInt4G32> {
 template <>
 struct FormatTraits<kInt4G64> {
   static constexpr int kGroup = 64;
+};
+template <>
+struct FormatTraits<kInt4Sym> {
+  static constexpr int kGroup = 128;
 };
 
 // ---- bit helpers ------------------------------------------------------------

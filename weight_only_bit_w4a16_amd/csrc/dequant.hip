@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     if constexpr (is_int4(FMT)) {
       const int64_t g = (c * 32) / G;
       const float s = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(scales)[n * groups + g]);
-      const float zf = (float)zeros[n * groups + g];
+      const float zf = has_zeros(FMT) ? (float)zeros[n * groups + g] : (float)kSymZero;
 #pragma unroll
       for (int d = 0; d < 4; ++d) out[d] = int4x8_to_bf16_weights(q[d], s, zf);
     } else if constexpr (FMT == kNvfp4) {
@@ -87,6 +87,10 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, co
       break;
     case kInt4G64:
       hipLaunchKernelGGL(dequant_kernel<kInt4G64>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                         packed, scales, zeros, W, N, K);
+      break;
+    case kInt4Sym:
+      hipLaunchKernelGGL(dequant_kernel<kInt4Sym>, dim3((unsigned)blocks), dim3(threads), 0, stream,
                          packed, scales, zeros, W, N, K);
       break;
     default:

@@ -71,11 +71,11 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
   const int kw = __builtin_amdgcn_readfirstlane(wave) * U;
 
   const uint32_t s_cap = S_LDS ? mid_cap((uint32_t)(kMidCols * groups * SB)) : 0u;
-  const uint32_t z_cap = S_LDS && is_int4(FMT) ? mid_cap((uint32_t)(kMidCols * groups)) : 0u;
+  const uint32_t z_cap = S_LDS && has_zeros(FMT) ? mid_cap((uint32_t)(kMidCols * groups)) : 0u;
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + s_cap + z_cap);  // [waves][MS * 2][64]
 
   const uint8_t* s_base = reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB;
-  const uint8_t* z_base = is_int4(FMT) ? zeros + (int64_t)n0 * groups : nullptr;
+  const uint8_t* z_base = has_zeros(FMT) ? zeros + (int64_t)n0 * groups : nullptr;
   // S_LDS: the windows' dwords, read from the 4-byte aligned address at or
   // below each block (at most 3 bytes past its end, in the same dword)
   uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
       const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
       sst[i] = wave_slot0 + i * blockDim.x < s_words ? buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB) : 0u;
     }
-    if constexpr (is_int4(FMT)) {
+    if constexpr (has_zeros(FMT)) {
       const rsrc_t zs = window(z_base, (uint32_t)(rows * groups), z_delta, z_words);
 #pragma unroll
       for (int i = 0; i < kMidSStage; ++i) {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     }
   } else {
     sr = make_rsrc(s_base, (uint32_t)(rows * groups * SB));
-    if constexpr (is_int4(FMT)) zr = make_rsrc(z_base, (uint32_t)(rows * groups));
+    if constexpr (has_zeros(FMT)) zr = make_rsrc(z_base, (uint32_t)(rows * groups));
   }
 
   // weight rows past N, A rows past M and chunks past K read as 0
@@ -132,9 +132,9 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
         q[u][h] = buf_load_b128(wr, ok ? r * rowb + (uint32_t)c * 16u : kBufferOOB);
         if constexpr (!S_LDS) {
           if constexpr (is_int4(FMT)) {
-            const uint32_t gi = r * (uint32_t)groups + (uint32_t)(FMT == kInt4 ? kb : c >> GS);
+            const uint32_t gi = r * (uint32_t)groups + (uint32_t)(is_int4_g128(FMT) ? kb : c >> GS);
             sraw[u][h] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
-            zraw[u][h] = buf_load_b8(zr, ok ? gi : kBufferOOB);
+            zraw[u][h] = has_zeros(FMT) ? buf_load_b8(zr, ok ? gi : kBufferOOB) : kSymZero;
           } else if constexpr (FMT == kNvfp4) {
             sraw[u][h] = buf_load_b16(sr, ok ? r * (uint32_t)groups + 2u * (uint32_t)c : kBufferOOB);
           } else {
@@ -163,12 +163,12 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = 16 * h + nl;
-        if constexpr (FMT == kInt4) {
+        if constexpr (is_int4_g128(FMT)) {
           const int gi = r * groups + kb;
           uint32_t sbits, z;
           if constexpr (S_LDS) {
             sbits = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
-            z = zb[gi];
+            z = has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero;
           } else {
             sbits = sraw[u][h];
             z = zraw[u][h];
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
         for (int j = 0; j < 4; ++j) a[j] = buf_load_b128(ar, ok ? off + 16u * j : kBufferOOB);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          if constexpr (FMT == kInt4) {
+          if constexpr (is_int4_g128(FMT)) {
             f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
             f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     for (int i = 0; i < kMidSStage; ++i) {
       const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
       if (w < s_words) reinterpret_cast<uint32_t*>(lds)[w] = sst[i];
-      if constexpr (is_int4(FMT)) {
+      if constexpr (has_zeros(FMT)) {
         if (w < z_words) reinterpret_cast<uint32_t*>(lds + s_cap)[w] = zst[i];
       }
     }
@@ -323,11 +323,11 @@ MidPlan mid_plan(int fmt, int64_t M, int64_t K) {
   if (p.MS < 2) p.MS = 2;
   // scale windows in LDS when every dword has a staging register
   const bool int4 = is_int4(fmt);
-  const int64_t groups = K / (fmt == kInt4 ? 128 : fmt == kNvfp4 ? 16 : fmt == kInt4G64 ? 64 : 32);
+  const int64_t groups = K / (is_int4_g128(fmt) ? 128 : fmt == kNvfp4 ? 16 : fmt == kInt4G64 ? 64 : 32);
   const int64_t sb = int4 ? 2 : 1;
   const int64_t slots = (int64_t)kMidSStage * 64 * p.waves;
   const int64_t s_cap = mid_cap((uint32_t)(kMidCols * groups * sb));
-  const int64_t z_cap = int4 ? mid_cap((uint32_t)(kMidCols * groups)) : 0;
+  const int64_t z_cap = has_zeros(fmt) ? mid_cap((uint32_t)(kMidCols * groups)) : 0;
   const int64_t red = (int64_t)p.waves * p.MS * 2 * 1024;
   p.s_lds = s_cap / 4 <= slots && z_cap / 4 <= slots && s_cap + z_cap + red <= 160 * 1024;
   p.lds = (unsigned)((p.s_lds ? s_cap + z_cap : 0) + red);
@@ -386,7 +386,9 @@ hipError_t launch_mid(const GemmArgs& a) {
     case 6: return launch_fmt<kInt4G32, false>(a);
     case 7: return launch_fmt<kInt4G32, true>(a);
     case 8: return launch_fmt<kInt4G64, false>(a);
-    default: return launch_fmt<kInt4G64, true>(a);
+    case 9: return launch_fmt<kInt4G64, true>(a);
+    case 10: return launch_fmt<kInt4Sym, false>(a);
+    default: return launch_fmt<kInt4Sym, true>(a);
   }
 }
 

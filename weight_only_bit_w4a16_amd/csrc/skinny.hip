@@ -60,7 +60,7 @@ struct SkinnyGroup {
 // One k-block of 128 codes into acc: a[j] is the lane's A fragment of MFMA
 // step j (32 codes), q[j] its 8 codes of that step, sraw / zraw the raw scale
 // (and zero) bytes of the lane's chunk.
-//   int4 g128: the +code and -zero products go to separate accumulators that
+//   int4 g128 (and symmetric): the +code and -zero products go to separate accumulators that
 //     follow the same rounding sequence, so a k-block whose codes all equal
 //     the zero point cancels to exactly 0.  EVEN_ODD: A sits in LDS in the
 //     even / odd k order of the shorter decode, and the codes convert in that
@@ -73,7 +73,7 @@ struct SkinnyGroup {
 template <int FMT, bool EVEN_ODD>
 __device__ __forceinline__ f32x4_t kblock_mac(const u32x4_t (&a)[4], const u32x4_t& q, uint32_t sraw,
                                               uint32_t zraw, f32x4_t acc) {
-  if constexpr (FMT == kInt4) {
+  if constexpr (is_int4_g128(FMT)) {
     const u32x4_t nz = int4_neg_zero(zraw);
     f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
     f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
   const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB,
                               (uint32_t)(rows * groups * SB));
-  const rsrc_t zr = make_rsrc(is_int4(FMT) ? zeros + (int64_t)n0 * groups : nullptr,
-                              is_int4(FMT) ? (uint32_t)(rows * groups) : 0u);
+  const rsrc_t zr = make_rsrc(has_zeros(FMT) ? zeros + (int64_t)n0 * groups : nullptr,
+                              has_zeros(FMT) ? (uint32_t)(rows * groups) : 0u);
 
   // Scale staging: rows n0 .. n0+rows-1 of the scales (and zeros) are one
   // contiguous block; it is read as dwords from the 4-byte aligned address at
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   const int am = M < 16 ? M : 16;
   const uint32_t s_off = A_LDS ? (((uint32_t)(am + 1) * (uint32_t)K * 2u + 15u) & ~15u) : 0u;
   const uint32_t z_off = s_off + (((16u * (uint32_t)groups * SB + 6u) + 15u) & ~15u);
-  const uint32_t z_cap = is_int4(FMT) ? ((16u * (uint32_t)groups + 6u + 15u) & ~15u) : 0u;
+  const uint32_t z_cap = has_zeros(FMT) ? ((16u * (uint32_t)groups + 6u + 15u) & ~15u) : 0u;
   // per-wave A regions (A_DMA) after the scale and zero windows
   const uint32_t a_dma_off = S_LDS ? z_off + z_cap : s_off;
   const uint32_t a_wave = lds_address(a_lds) + a_dma_off +
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
       const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
       sst[i] = wave_slot0 + i * blockDim.x < s_words ? buf_load_b32(ss, w < s_words ? w * 4u : kBufferOOB) : 0u;
     }
-    if constexpr (is_int4(FMT)) {
+    if constexpr (has_zeros(FMT)) {
       const rsrc_t zs = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), z_delta, z_words);
 #pragma unroll
       for (int i = 0; i < kZStage; ++i) {
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
         const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
         if (w < s_words) reinterpret_cast<uint32_t*>(a_lds + s_off)[w] = sst[i];
       }
-      if constexpr (is_int4(FMT)) {
+      if constexpr (has_zeros(FMT)) {
 #pragma unroll
         for (int i = 0; i < kZStage; ++i) {
           const uint32_t w = (uint32_t)(tid + i * (int)blockDim.x);
@@ -322,9 +322,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
       if constexpr (is_int4(FMT)) {
-        const uint32_t gi = (uint32_t)(nl * groups + (FMT == kInt4 ? kb : c >> GS));
+        const uint32_t gi = (uint32_t)(nl * groups + (is_int4_g128(FMT) ? kb : c >> GS));
         sraw[u] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
-        zraw[u] = buf_load_b8(zr, ok ? gi : kBufferOOB);
+        zraw[u] = has_zeros(FMT) ? buf_load_b8(zr, ok ? gi : kBufferOOB) : kSymZero;
       } else if constexpr (FMT == kNvfp4) {
         // the chunk's two e4m3 scales (blocks 2c and 2c+1), one 16-bit load
         sraw[u] = buf_load_b16(sr, ok ? (uint32_t)(nl * groups + 2 * c) : kBufferOOB);
@@ -399,9 +399,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
         const bool ok = FULL || c < chunks;
         const uint8_t* sb = a_lds + s_off + s_delta;
         if constexpr (is_int4(FMT)) {
-          const int gi = nl * groups + (ok ? (FMT == kInt4 ? kb : c >> GS) : 0);
+          const int gi = nl * groups + (ok ? (is_int4_g128(FMT) ? kb : c >> GS) : 0);
           sraw[u] = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
-          zraw[u] = (a_lds + z_off + z_delta)[gi];
+          zraw[u] = has_zeros(FMT) ? (uint32_t)(a_lds + z_off + z_delta)[gi] : kSymZero;
         } else if constexpr (FMT == kNvfp4) {
           sraw[u] = *reinterpret_cast<const uint16_t*>(sb + nl * groups + 2 * (ok ? c : 0));
         } else {
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
     for (int i = 0; i < kAStage; ++i) {
       const int ch = tid + i * (int)blockDim.x;
       // int4 codes decode in the k order (0,2,4,6,1,3,5,7) per 8: A follows it
-      const u32x4_t v = FMT == kInt4 ? bf16x8_even_odd(astage[i]) : astage[i];
+      const u32x4_t v = is_int4_g128(FMT) ? bf16x8_even_odd(astage[i]) : astage[i];
       if (ch < a16) reinterpret_cast<u32x4_t*>(a_lds)[ch] = v;
     }
     for (int ch = a16 + tid; ch < a16 + K / 8; ch += blockDim.x)
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
 
   const uint32_t s_cap = ring_window_cap(16u * (uint32_t)groups * SB);
-  const uint32_t z_cap = is_int4(FMT) ? ring_window_cap(16u * (uint32_t)groups) : 0u;
+  const uint32_t z_cap = has_zeros(FMT) ? ring_window_cap(16u * (uint32_t)groups) : 0u;
   const uint32_t base = lds_address(lds);
   const uint32_t my_ring = s_cap + z_cap + (uint32_t)wave * (uint32_t)(D * kRingSlot);
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + s_cap + z_cap + (uint32_t)waves * (D * kRingSlot));
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
   };
   const uint32_t s_delta = window(scales + (int64_t)n0 * groups * SB, (uint32_t)(rows * groups * SB), 0u);
   uint32_t z_delta = 0;
-  if constexpr (is_int4(FMT)) z_delta = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), s_cap);
+  if constexpr (has_zeros(FMT)) z_delta = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), s_cap);
 
   // this wave's k-blocks: kb = i * waves + wave, i = 0 .. nk-1
   const int nk = wave < KB ? (KB - 1 - wave) / waves + 1 : 0;
@@ -601,9 +601,9 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
     const bool ok = FULL || c < chunks;
     uint32_t sraw, zraw = 0u;
     if constexpr (is_int4(FMT)) {
-      const int gi = nl * groups + (ok ? (FMT == kInt4 ? kb : c >> GS) : 0);
+      const int gi = nl * groups + (ok ? (is_int4_g128(FMT) ? kb : c >> GS) : 0);
       sraw = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
-      zraw = zb[gi];
+      zraw = has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero;
     } else if constexpr (FMT == kNvfp4) {
       sraw = *reinterpret_cast<const uint16_t*>(sb + nl * groups + 2 * (ok ? c : 0));
     } else {
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
   const int g = lane >> 4;   // 32-code chunk within the k-block
   const int KB = K >> 7;
   constexpr int G = FormatTraits<FMT>::kGroup;
-  constexpr int SB = (FMT == kInt4) ? 2 : 1;
+  constexpr int SB = is_int4_g128(FMT) ? 2 : 1;
   const int groups = K / G;
   const uint32_t rowb = (uint32_t)(K >> 1);
   const uint32_t wave_slot0 = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64u;
@@ -762,13 +762,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
       u32x4_t a[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[j] = src[j];
-      if constexpr (FMT == kInt4) {
+      if constexpr (is_int4_g128(FMT)) {
         // codes exact (A is stored in the decoder's k order); the zero point
         // goes through a second accumulator with the same rounding sequence,
         // so a k-block whose codes all equal it cancels to exactly 0
         const int gi = nl * groups + kb;
         const float s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
-        const u32x4_t nz = int4_neg_zero(zb[gi]);
+        const u32x4_t nz = int4_neg_zero(has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero);
         f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
         f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -843,7 +843,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
   for (int i = 0; i < kAStage; ++i) {
     const int ch = tid + i * (int)blockDim.x;
     // int4 codes decode in the k order (0,2,4,6,1,3,5,7) per 8: A follows it
-    const u32x4_t v = FMT == kInt4 ? bf16x8_even_odd(astage[i]) : astage[i];
+    const u32x4_t v = is_int4_g128(FMT) ? bf16x8_even_odd(astage[i]) : astage[i];
     if (ch < a16) reinterpret_cast<u32x4_t*>(lds)[ch] = v;
   }
   for (int ch = a16 + tid; ch < a16 + K / 8; ch += blockDim.x)
@@ -979,7 +979,7 @@ bool try_ring(const GroupedArgs& a, hipError_t& err) {
   constexpr int SB = is_int4(FMT) ? 2 : 1;
   const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
   const int64_t win = ring_window_cap((uint32_t)(16 * groups * SB)) +
-                      (is_int4(FMT) ? ring_window_cap((uint32_t)(16 * groups)) : 0);
+                      (has_zeros(FMT) ? ring_window_cap((uint32_t)(16 * groups)) : 0);
   dim3 grid;
   const SkinnyGroup grp = skinny_group(a, skinny_rows(a), grid);
   const bool one_round = env == 8 || (env != 4 && (int64_t)grid.x * grid.y * grid.z <= 256);
@@ -1011,7 +1011,7 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   constexpr int SB = is_int4(FMT) ? 2 : 1;
   const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
   const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
-  const int64_t z_cap = is_int4(FMT) ? (16 * groups + 6 + 15) & ~15 : 0;
+  const int64_t z_cap = has_zeros(FMT) ? (16 * groups + 6 + 15) & ~15 : 0;
   const int64_t lds_s = s_cap + z_cap;
   // staged when every dword of the windows has a staging register (the zero
   // window exists for int4 only).  Exception, measured: a single fp4 row with
@@ -1021,7 +1021,7 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   const int64_t threads = 64 * waves;
   const bool lane_scales = !is_int4(FMT) && a.M == 1 && 16 * groups * SB >= 4096;
   const bool s_lds = !lane_scales && (16 * groups * SB + 6) / 4 <= kSStage * threads &&
-                     (!is_int4(FMT) || (16 * groups + 6) / 4 <= kZStage * threads) && lds_s <= 32 * 1024;
+                     (!has_zeros(FMT) || (16 * groups + 6) / 4 <= kZStage * threads) && lds_s <= 32 * 1024;
   const bool full = a.K % 128 == 0;
   const dim3 block(64 * waves);
   static const bool no_dma = [] {
@@ -1112,7 +1112,7 @@ bool try_stream(const GroupedArgs& a, int64_t min_tiles, hipError_t& err) {
   const int64_t threads = 64 * waves;
   const int64_t a16 = a.M * a.K / 8;
   if (a16 > kAStage * threads || a.M * a.K * 2 > 64 * 1024) return false;
-  constexpr int SB = FMT == kInt4 ? 2 : 1;
+  constexpr int SB = is_int4_g128(FMT) ? 2 : 1;
   const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
   const int64_t s_words = (16 * groups * SB + 6) / 4, z_words = (16 * groups + 6) / 4;
   const int NS = s_words <= threads ? 1 : (s_words <= 2 * threads ? 2 : 0);
@@ -1191,7 +1191,9 @@ hipError_t launch_skinny_grouped(const GroupedArgs& a) {
     case 6: return launch_fmt<kInt4G32, false>(a);
     case 7: return launch_fmt<kInt4G32, true>(a);
     case 8: return launch_fmt<kInt4G64, false>(a);
-    default: return launch_fmt<kInt4G64, true>(a);
+    case 9: return launch_fmt<kInt4G64, true>(a);
+    case 10: return launch_fmt<kInt4Sym, false>(a);
+    default: return launch_fmt<kInt4Sym, true>(a);
   }
 }
 

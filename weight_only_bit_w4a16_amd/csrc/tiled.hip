@@ -69,6 +69,10 @@ struct ScaleTile<kInt4> {
   static constexpr int kElems = 8, kKTiles = 16, kArrays = 2;
 };
 template <>
+struct ScaleTile<kInt4Sym> {  // scales only (the zero point is 8)
+  static constexpr int kElems = 8, kKTiles = 16, kArrays = 1;
+};
+template <>
 struct ScaleTile<kInt4G64> {
   static constexpr int kElems = 8, kKTiles = 8, kArrays = 2;
 };
@@ -181,8 +185,8 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   constexpr int SB = is_int4(FMT) ? 2 : 1;
   const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n_base * groups * SB,
                               (uint32_t)(brows * groups * SB));
-  const rsrc_t zr = make_rsrc(is_int4(FMT) ? zeros + (int64_t)n_base * groups : nullptr,
-                              is_int4(FMT) ? (uint32_t)(brows * groups) : 0u);
+  const rsrc_t zr = make_rsrc(has_zeros(FMT) ? zeros + (int64_t)n_base * groups : nullptr,
+                              has_zeros(FMT) ? (uint32_t)(brows * groups) : 0u);
   const uint32_t lds0 = lds_address(smem);
   // Resolve the output pointer's scalar load here: a scalar load still in
   // flight in the k-loop would turn every partial LDS wait there into a full one.
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
       } else if constexpr (FMT == kNvfp4) {
         lds_dma_b16(sr, dst, 2 * e < groups ? (uint32_t)(row * groups + 2 * e) : kBufferOOB);
       } else {
-        if (arr == 0)
+        if (!has_zeros(FMT) || arr == 0)
           lds_dma_b16(sr, dst, e < groups ? (uint32_t)(row * groups + e) * 2u : kBufferOOB);
         else
           lds_dma_b8(zr, dst, e < groups ? (uint32_t)(row * groups + e) : kBufferOOB);
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     // scale element of lane group g in this k-tile, and its slot
     const int jt = j % ST::kKTiles;
     // (lane group g holds codes 16g .. 16g+15 of the k-tile's 64)
-    const int se = FMT == kInt4 ? (jt >> 1) : FMT == kInt4G64 ? jt : 2 * jt + (g >> 1);
+    const int se = is_int4_g128(FMT) ? (jt >> 1) : FMT == kInt4G64 ? jt : 2 * jt + (g >> 1);
     const uint8_t* Ss = smem + L::kSOff + ((j / ST::kKTiles) & 1) * L::kSBytes +
                         ((wn * TN * 16 + l16) * E + (se ^ fs)) * 4;
 
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     for (int t = 0; t < TN; ++t) {
       bq[t] = *reinterpret_cast<const u32x2_t*>(Bs + b_rd + t * 16 * 32);
       sw[t] = *reinterpret_cast<const uint32_t*>(Ss + t * 16 * E * 4);
-      if constexpr (is_int4(FMT))
+      if constexpr (has_zeros(FMT))
         zw[t] = *reinterpret_cast<const uint32_t*>(Ss + t * 16 * E * 4 + L::kSArrayBytes);
     }
 #pragma unroll
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     for (int t = 0; t < TN; ++t) {
       if constexpr (is_int4(FMT)) {
         bs[t] = bf16_bits_to_f32(sw[t]);
-        bz[t] = (float)zw[t];
+        bz[t] = has_zeros(FMT) ? (float)zw[t] : (float)kSymZero;
       } else if constexpr (FMT == kNvfp4) {
         bs[t] = e4m3_magnitude((sw[t] >> (8 * (g & 1))) & 0xFFu);
       } else {
@@ -536,7 +540,9 @@ hipError_t launch_tiled(const GemmArgs& a) {
     case 6: return launch_fmt<kInt4G32, false>(a);
     case 7: return launch_fmt<kInt4G32, true>(a);
     case 8: return launch_fmt<kInt4G64, false>(a);
-    default: return launch_fmt<kInt4G64, true>(a);
+    case 9: return launch_fmt<kInt4G64, true>(a);
+    case 10: return launch_fmt<kInt4Sym, false>(a);
+    default: return launch_fmt<kInt4Sym, true>(a);
   }
 }
 

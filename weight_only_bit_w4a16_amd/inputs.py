@@ -26,11 +26,12 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64 = 0, 1, 2, 3, 4
+INT4_G128, NVFP4, MXFP4, INT4_G32, INT4_G64, INT4_SYM = 0, 1, 2, 3, 4, 5
 FORMAT_NAMES = {INT4_G128: "int4_g128", NVFP4: "nvfp4", MXFP4: "mxfp4",
-                INT4_G32: "int4_g32", INT4_G64: "int4_g64"}
-GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64}
-INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64)
+                INT4_G32: "int4_g32", INT4_G64: "int4_g64", INT4_SYM: "int4_sym"}
+GROUP = {INT4_G128: 128, NVFP4: 16, MXFP4: 32, INT4_G32: 32, INT4_G64: 64, INT4_SYM: 128}
+INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64, INT4_SYM)  # bf16 scales
+ZERO_FORMATS = (INT4_G128, INT4_G32, INT4_G64)  # with a zero array
 
 
 @dataclass
@@ -42,7 +43,7 @@ class Case:
     A: np.ndarray        # uint16 bf16 bits (M, K)
     packed: np.ndarray   # uint8 (N, K/2)
     scales: np.ndarray   # uint16 bf16 bits (int4) or uint8 bytes (fp4), (N, K/G)
-    zeros: np.ndarray | None  # uint8 (N, K/G) for int4, else None
+    zeros: np.ndarray | None  # uint8 (N, K/G) for asymmetric int4, else None
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -67,8 +68,10 @@ def make_weights(rng: np.random.Generator, fmt: int, N: int, K: int):
         raise ValueError(f"K={K} must be a multiple of the group size {G}")
     packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     zeros = None
-    if fmt in INT4_FORMATS:
+    if fmt in ZERO_FORMATS:
         zeros = rng.integers(0, 16, size=(N, K // G), dtype=np.uint8)
+        scales = bf16_bits(rng.uniform(0.005, 0.02, size=(N, K // G)))
+    elif fmt == INT4_SYM:
         scales = bf16_bits(rng.uniform(0.005, 0.02, size=(N, K // G)))
     elif fmt == NVFP4:
         scales = e4m3_bytes(rng.uniform(2.0 ** -4, 4.0, size=(N, K // G)))
