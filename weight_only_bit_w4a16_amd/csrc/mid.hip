@@ -23,6 +23,8 @@
 //   * scales (and zeros) of the workgroup's 32 rows are one contiguous block:
 //     copied once to LDS with coalesced dword loads when it fits the staging
 //     registers (S_LDS), else each lane loads its own with its weights.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,6 +42,55 @@ constexpr int mid_sb() { return is_int4(FMT) ? 2 : 1; }  // scale bytes
 // scale (zero) window capacity in bytes: 32 rows plus the <= 3-byte lead of
 // the dword-aligned start and the <= 3-byte tail of its last dword
 __host__ __device__ constexpr uint32_t mid_cap(uint32_t bytes) { return (bytes + 6u + 15u) & ~15u; }
+
+// The split-K sum and the stores of one workgroup: output block p = (row
+// slice s, column slice h) is the sum of red[(w * P + p) * 64 + lane] over the
+// waves w in order, stored (through the fused epilogue when on) by wave
+// p % waves.  Lane (nl, g) holds rows 16s + 4g .. 16s + 4g + 3 of column
+// 16h + nl; rows bounds the workgroup's columns.
+template <bool OUT_F32, int MS>
+__device__ __forceinline__ void mid_store(const f32x4_t* red, int wave, int waves, int lane, int nl, int g,
+                                          int n0, int m0, int rows, int M, int N, void* C,
+                                          const Epilogue& epi) {
+  constexpr int P = MS * 2;
+  for (int p = wave; p < P; p += waves) {
+    const int s = p >> 1, h = p & 1;
+    const int n = n0 + 16 * h + nl;
+    const bool col_ok = 16 * h + nl < rows;
+    // epilogue operands first, in one round trip (the residual may alias C)
+    float eb = 0.f, er[4] = {0.f, 0.f, 0.f, 0.f};
+    if (epi.on && col_ok) {
+      if (epi.bias) eb = bf16_bits_to_f32(epi.bias[n]);
+      if (epi.res) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 16 * s + 4 * g + i;
+          if (m < M) er[i] = residual_at<OUT_F32>(epi.res, (int64_t)m * N + n);
+        }
+      }
+    }
+    f32x4_t sum = red[p * 64 + lane];
+    for (int w = 1; w < waves; ++w) {
+      const f32x4_t v = red[(w * P + p) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += v[i];
+    }
+    if (!col_ok) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 16 * s + 4 * g + i;
+      if (m < M) {
+        const int64_t mn = (int64_t)m * N + n;
+        const float v = epi.on ? epilogue_value(epi, sum[i], eb, er[i]) : sum[i];
+        if constexpr (OUT_F32) {
+          reinterpret_cast<float*>(C)[mn] = v;
+        } else {
+          reinterpret_cast<__bf16*>(C)[mn] = (__bf16)v;
+        }
+      }
+    }
+  }
+}
 
 template <int FMT, bool OUT_F32, int U, int MS, bool S_LDS>
 __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* __restrict__ A,
@@ -253,51 +304,221 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     compute(kbase);
   }
 
-  // ---- split-K sum over the waves through LDS: output block p = (row slice
-  // s, column slice h) is summed in wave order and stored by wave p % waves ----
+  // ---- split-K sum over the waves through LDS ----
   constexpr int P = MS * 2;
 #pragma unroll
   for (int s = 0; s < MS; ++s)
 #pragma unroll
     for (int h = 0; h < 2; ++h) red[(wave * P + s * 2 + h) * 64 + lane] = acc[s][h];
   lds_barrier();
-  for (int p = wave; p < P; p += waves) {
-    const int s = p >> 1, h = p & 1;
-    const int n = n0 + 16 * h + nl;
-    const bool col_ok = 16 * h + nl < rows;
-    // epilogue operands first, in one round trip (the residual may alias C)
-    float eb = 0.f, er[4] = {0.f, 0.f, 0.f, 0.f};
-    if (epi.on && col_ok) {
-      if (epi.bias) eb = bf16_bits_to_f32(epi.bias[n]);
-      if (epi.res) {
+  mid_store<OUT_F32, MS>(red, wave, waves, lane, nl, g, n0, m0, rows, M, N, C, epi);
+}
+
+// ---- ring variant -----------------------------------------------------------
+//
+// The same tile (32 columns x 16 MS rows) and decode, with every operand
+// moved by asynchronous global -> LDS copies: k-block kb's A rows (16 MS x
+// 256 bytes, chunk c of row r in slot c ^ (r & 15) so that the fragment reads
+// of 16 rows hit distinct banks) and weight rows (32 x 64 bytes) fill one of
+// the wave's D ring slots, refilled D k-blocks ahead; the scale (and zero)
+// window arrives the same way, once.  kMidRingWaves waves split K, wave w
+// taking k-blocks w, w + W, ...; no operand goes through a load the compiler
+// sees, so every wait is an explicit count of the copies issued after the
+// one needed (vmcnt retires in issue order).  The per-lane A loads of the
+// other form leave each CU reading A at about half the rate its memory
+// pipeline sustains; here copies of D - 1 k-blocks stay in flight while one
+// is computed.  The partial sums reuse the ring's LDS once every wave is done.
+constexpr int kMidRingWaves = 4;
+
+__host__ __device__ constexpr uint32_t mid_ring_slot(int ms) { return (uint32_t)ms * 4096u + 2048u; }
+__host__ __device__ constexpr uint32_t mid_ring_window(uint32_t bytes) { return (bytes + 6u + 255u) / 256u * 256u; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int FMT, bool OUT_F32, int MS, int D, bool FULL>
+__global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint16_t* __restrict__ A,
+                                                                    const uint8_t* __restrict__ packed,
+                                                                    const void* __restrict__ scales,
+                                                                    const uint8_t* __restrict__ zeros,
+                                                                    void* __restrict__ C, int M, int N, int K,
+                                                                    Epilogue epi) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int W = kMidRingWaves;
+  constexpr int CPK = 4 * MS + 2;  // copies per k-block
+  static_assert((D - 1) * CPK <= 63, "vmcnt");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = (int)blockIdx.x * kMidCols;
+  const int m0 = (int)blockIdx.y * 16 * MS;
+  const int KC = K >> 5;
+  const int KB = (KC + 3) >> 2;
+  constexpr int G = FormatTraits<FMT>::kGroup;
+  constexpr int SB = mid_sb<FMT>();
+  constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
+  const int groups = K / G;
+  const uint32_t rowb = (uint32_t)(K >> 1);
+  const int rows = min(kMidCols, N - n0);
+  const int arows = min(16 * MS, M - m0);
+
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
+  const uint32_t s_cap = mid_ring_window((uint32_t)(kMidCols * groups * SB));
+  const uint32_t z_cap = has_zeros(FMT) ? mid_ring_window((uint32_t)(kMidCols * groups)) : 0u;
+  const uint32_t base = lds_address(lds);
+  const uint32_t ring0 = s_cap + z_cap;
+  const uint32_t my_ring = ring0 + (uint32_t)wave * (uint32_t)(D * mid_ring_slot(MS));
+
+  // window copies: dwords from the 4-byte aligned address at or below the
+  // block's start (delta bytes before it), 64 per copy, the waves in turn
+  auto window = [&](const uint8_t* start, uint32_t bytes, uint32_t lds_off) {
+    const uintptr_t al = reinterpret_cast<uintptr_t>(start) & ~(uintptr_t)3;
+    const uint32_t delta = (uint32_t)(reinterpret_cast<uintptr_t>(start) - al);
+    const uint32_t words = (delta + bytes + 3u) / 4u;  // may read <= 3 bytes past the block (same page)
+    const rsrc_t r = make_rsrc(reinterpret_cast<const void*>(al), words * 4u);
+    const int instrs = (int)((words + 63u) / 64u);
+    for (int t = wave; t < instrs; t += W)
+      lds_dma_b32(r, base + lds_off + (uint32_t)t * 256u, ((uint32_t)t * 64u + (uint32_t)lane) * 4u);
+    return delta;
+  };
+  const uint32_t s_delta = window(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB,
+                                  (uint32_t)(rows * groups * SB), 0u);
+  uint32_t z_delta = 0;
+  if constexpr (has_zeros(FMT)) z_delta = window(zeros + (int64_t)n0 * groups, (uint32_t)(rows * groups), s_cap);
+
+  const int nk = wave < KB ? (KB - 1 - wave) / W + 1 : 0;
+  // k-block i -> slot i % D: A copy r4 moves rows 4 r4 .. 4 r4 + 3 (lane ->
+  // row 4 r4 + l/16, LDS chunk l%16 holding chunk (l%16) ^ (row & 15));
+  // weight copy t moves rows 16t .. 16t + 15 (lane -> row 16t + l/4, chunk l%4)
+  auto issue = [&](int i) {
+    const int kb = i * W + wave;
+    const uint32_t slot = base + my_ring + (uint32_t)(i % D) * mid_ring_slot(MS);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 16 * s + 4 * g + i;
-          if (m < M) er[i] = residual_at<OUT_F32>(epi.res, (int64_t)m * N + n);
-        }
+    for (int r4 = 0; r4 < 4 * MS; ++r4) {
+      const int r = 4 * r4 + (lane >> 4);
+      const int ch = (lane & 15) ^ (r & 15);
+      const bool ok = FULL || kb * 128 + 8 * ch < K;
+      lds_dma_b128(ar, slot + (uint32_t)r4 * 1024u,
+                   ok ? ((uint32_t)r * (uint32_t)K + (uint32_t)kb * 128u + 8u * (uint32_t)ch) * 2u : kBufferOOB);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int wrow = 16 * t + (lane >> 2), wch = lane & 3;
+      const bool okw = FULL || kb * 4 + wch < KC;
+      lds_dma_b128(wr, slot + (uint32_t)MS * 4096u + (uint32_t)t * 1024u,
+                   okw ? (uint32_t)wrow * rowb + (uint32_t)kb * 64u + (uint32_t)wch * 16u : kBufferOOB);
+    }
+  };
+  auto ring_wait = [&](int later) {
+    if (D > 2 && later >= 2) {
+      wait_vmcnt<(D > 2 ? 2 * CPK : 0)>();
+    } else if (later >= 1) {
+      wait_vmcnt<CPK>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+  const int first = nk < D ? nk : D;
+  for (int i = 0; i < first; ++i) issue(i);
+  // the windows (issued first) and k-block 0 have landed in this wave's part;
+  // after the barrier every wave's part has
+  ring_wait(first - 1);
+  lds_barrier();
+
+  f32x4_t acc[MS][2];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) acc[s][0] = acc[s][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* sb = lds + s_delta;
+  const uint8_t* zb = lds + s_cap + z_delta;
+  for (int i = 0; i < nk; ++i) {
+    if (i > 0) ring_wait(min(D - 1, nk - 1 - i));
+    const int kb = i * W + wave;
+    const int c = kb * 4 + g;
+    const bool ok = FULL || c < KC;
+    const int cc = ok ? c : 0;  // window reads stay inside it
+    const uint8_t* slot = lds + my_ring + (uint32_t)(i % D) * mid_ring_slot(MS);
+    // both column slices decoded once, to bf16 MFMA operands
+    u32x4_t b[2][4];
+    float sc[2];
+    u32x4_t nz[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * h + nl;
+      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(slot + MS * 4096 + (r * 4 + g) * 16);
+      if constexpr (is_int4_g128(FMT)) {
+        const int gi = r * groups + kb;
+        sc[h] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
+        nz[h] = int4_neg_zero(has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_natural(q[j]);
+      } else if constexpr (is_int4(FMT)) {
+        const int gi = r * groups + (cc >> GS);
+        const float sv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
+        const float zf = (float)zb[gi];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_weights(q[j], sv, zf);
+      } else if constexpr (FMT == kNvfp4) {
+        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sb + r * groups + 2 * cc);
+        const float s0 = e4m3_magnitude(s2 & 0xFFu), s1 = e4m3_magnitude(s2 >> 8);
+        b[h][0] = fp4x8_to_bf16_fscale(q[0], s0);
+        b[h][1] = fp4x8_to_bf16_fscale(q[1], s0);
+        b[h][2] = fp4x8_to_bf16_fscale(q[2], s1);
+        b[h][3] = fp4x8_to_bf16_fscale(q[3], s1);
+      } else {
+        const float es = e8m0_as_exponent_scale((uint32_t)sb[r * groups + cc]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[h][j] = fp4x8_to_bf16_escale(q[j], es);
       }
     }
-    f32x4_t sum = red[p * 64 + lane];
-    for (int w = 1; w < waves; ++w) {
-      const f32x4_t v = red[(w * P + p) * 64 + lane];
+    // every row slice of A meets both decoded column slices
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum[i] += v[i];
-    }
-    if (!col_ok) continue;
+    for (int s = 0; s < MS; ++s) {
+      u32x4_t a[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 16 * s + 4 * g + i;
-      if (m < M) {
-        const int64_t mn = (int64_t)m * N + n;
-        const float v = epi.on ? epilogue_value(epi, sum[i], eb, er[i]) : sum[i];
-        if constexpr (OUT_F32) {
-          reinterpret_cast<float*>(C)[mn] = v;
+      for (int j = 0; j < 4; ++j)
+        a[j] = *reinterpret_cast<const u32x4_t*>(slot + (16 * s + nl) * 256 + (((4 * g + j) ^ nl) * 16));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (is_int4_g128(FMT)) {
+          f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dp = mfma16x16x32(a[j], b[h][j], dp);
+            dn = mfma16x16x32(a[j], nz[h], dn);
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[s][h][t] = __builtin_fmaf(sc[h], dp[t] + dn[t], acc[s][h][t]);
         } else {
-          reinterpret_cast<__bf16*>(C)[mn] = (__bf16)v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[s][h] = mfma16x16x32(a[j], b[h][j], acc[s][h]);
         }
       }
+    }
+    if (i + D < nk) {
+      // the slot's reads have completed before its next copy is issued
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(i + D);
     }
   }
+
+  // ---- split-K sum: the partial sums take the ring's place once every wave
+  // is past its last k-block (its copies all waited for) ----
+  constexpr int P = MS * 2;
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + ring0);
+  lds_barrier();
+#pragma unroll
+  for (int s = 0; s < MS; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) red[(wave * P + s * 2 + h) * 64 + lane] = acc[s][h];
+  lds_barrier();
+  mid_store<OUT_F32, MS>(red, wave, W, lane, nl, g, n0, m0, rows, M, N, C, epi);
 }
 
 // launch shape of one call: k-blocks per wave and pass, waves, row slices
@@ -366,9 +587,63 @@ hipError_t launch_m(const GemmArgs& a, const MidPlan& p) {
   return launch_s<FMT, OUT_F32, U, 4>(a, p);
 }
 
+// the ring variant over row tiles of 16 MS rows, at most 65535 per launch
+template <int FMT, bool OUT_F32, int MS, int D>
+hipError_t launch_ring(const GemmArgs& a, unsigned lds) {
+  const int64_t chunk = (int64_t)65535 * 16 * MS;
+  const int64_t es = OUT_F32 ? 4 : 2;
+  const bool full = a.K % 128 == 0;
+  for (int64_t m = 0; m < a.M; m += chunk) {
+    const int64_t rows = a.M - m < chunk ? a.M - m : chunk;
+    const dim3 grid((unsigned)((a.N + kMidCols - 1) / kMidCols), (unsigned)((rows + 16 * MS - 1) / (16 * MS)));
+    Epilogue epi = a.epi;
+    if (epi.res) epi.res = static_cast<const uint8_t*>(epi.res) + m * a.N * es;
+    if (full)
+      hipLaunchKernelGGL((mid_ring_kernel<FMT, OUT_F32, MS, D, true>), grid, dim3(64 * kMidRingWaves), lds,
+                         a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
+                         static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi);
+    else
+      hipLaunchKernelGGL((mid_ring_kernel<FMT, OUT_F32, MS, D, false>), grid, dim3(64 * kMidRingWaves), lds,
+                         a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
+                         static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The ring variant when its LDS fits beside the scale windows (3 slots per
+// wave for 32-row tiles, else 2); W4A16_MID_RING=0 never (tuning).
+template <int FMT, bool OUT_F32>
+bool try_mid_ring(const GemmArgs& a, int MS, hipError_t& err) {
+  static const int env = [] {
+    const char* e = getenv("W4A16_MID_RING");
+    return e ? atoi(e) : 1;
+  }();
+  if (env == 0) return false;
+  constexpr int SB = mid_sb<FMT>();
+  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t win = mid_ring_window((uint32_t)(kMidCols * groups * SB)) +
+                      (has_zeros(FMT) ? mid_ring_window((uint32_t)(kMidCols * groups)) : 0);
+  auto lds_of = [&](int d) { return win + (int64_t)kMidRingWaves * d * mid_ring_slot(MS); };
+  constexpr int64_t kLds = 160 * 1024;
+  if (MS == 2 && lds_of(3) <= kLds) {
+    err = launch_ring<FMT, OUT_F32, 2, 3>(a, (unsigned)lds_of(3));
+    return true;
+  }
+  if (lds_of(2) > kLds) return false;
+  const unsigned lds = (unsigned)lds_of(2);
+  err = MS == 2 ? launch_ring<FMT, OUT_F32, 2, 2>(a, lds)
+      : MS == 3 ? launch_ring<FMT, OUT_F32, 3, 2>(a, lds)
+                : launch_ring<FMT, OUT_F32, 4, 2>(a, lds);
+  return true;
+}
+
 template <int FMT, bool OUT_F32>
 hipError_t launch_fmt(const GemmArgs& a) {
   const MidPlan p = mid_plan(FMT, a.M, a.K);
+  hipError_t err = hipSuccess;
+  if (try_mid_ring<FMT, OUT_F32>(a, p.MS, err)) return err;
   return p.U == 2 ? launch_m<FMT, OUT_F32, 2>(a, p) : launch_m<FMT, OUT_F32, 4>(a, p);
 }
 
