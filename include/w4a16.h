@@ -82,10 +82,10 @@ extern "C" {
  * decode) kernel for M <= 16.  Above that, while the LDS-tiled MFMA kernel
  * would have fewer than 256 tiles of 256 x 256: the mid kernel (tiles of 32
  * columns x up to 64 rows, split-K, each weight decoded once per tile) when it
- * has at least 160 workgroups in at most 2 rounds of 256 (3 for int4), the
+ * has at least 160 and at most 896 workgroups (3.5 rounds of 256), the
  * skinny kernel (M <= 384) when it would have fewer, else the tiled kernel
  * (128 x 128 tiles below 192 large ones); with 256 or more large tiles, the
- * mid kernel for M <= 48 and the tiled kernel above.  The others force one
+ * mid kernel for M <= 64 and the tiled kernel above.  The others force one
  * kernel at any M (the skinny kernel then walks M in slices of 16 rows, the
  * mid kernel in tiles of 32 to 64). */
 #define W4A16_PATH_AUTO 0x0000

@@ -71,24 +71,27 @@ def test_path_choice():
     assert w4.gemm_path(w4.INT4_G128, 1, 8192, 3072) == "skinny"
     assert w4.gemm_path(w4.NVFP4, 16, 3072, 8192) == "skinny"
     # a small tiled grid: the mid kernel (workgroups of 32 columns x 64 rows)
-    # while it has >= 160 workgroups in at most 2 rounds of 256 (3 for int4),
+    # while it has 160 .. 896 workgroups (3.5 rounds of 256),
     # the skinny kernel below 160 workgroups, else the tiled kernel
     assert w4.gemm_path(w4.MXFP4, 17, 64, 64) == "skinny"
     assert w4.gemm_path(w4.INT4_G128, 64, 1024, 3072) == "skinny"
     assert w4.gemm_path(w4.NVFP4, 64, 3072, 8192) == "skinny"        # 96 workgroups
     assert w4.gemm_path(w4.NVFP4, 65, 3072, 8192) == "mid"           # 192
     assert w4.gemm_path(w4.INT4_G128, 17, 5120, 3072) == "mid"       # 160
-    assert w4.gemm_path(w4.MXFP4, 128, 8192, 3072) == "mid"          # 2 rounds
-    assert w4.gemm_path(w4.MXFP4, 129, 8192, 3072) == "tiled"        # 3 rounds
-    assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "mid"      # 3 rounds
+    assert w4.gemm_path(w4.MXFP4, 192, 8192, 3072) == "mid"          # 768 workgroups
+    assert w4.gemm_path(w4.MXFP4, 193, 8192, 3072) == "tiled"        # 1024
+    assert w4.gemm_path(w4.MXFP4, 96, 14336, 4096) == "mid"          # 896
+    assert w4.gemm_path(w4.INT4_G128, 64, 28672, 4096) == "mid"      # 896 (112 large tiles)
+    assert w4.gemm_path(w4.INT4_G128, 65, 28672, 4096) == "tiled"    # 1792
+    assert w4.gemm_path(w4.INT4_G128, 192, 8192, 3072) == "mid"
     assert w4.gemm_path(w4.INT4_G128, 193, 8192, 3072) == "tiled"
-    assert w4.gemm_path(w4.INT4_SYM, 192, 8192, 3072) == "mid"       # int4: 3 rounds
+    assert w4.gemm_path(w4.INT4_SYM, 192, 8192, 3072) == "mid"
     assert w4.gemm_path(w4.INT4_SYM, 193, 8192, 3072) == "tiled"
     assert w4.gemm_path(w4.INT4_G128, 384, 1024, 3072) == "mid"      # 192 workgroups
     assert w4.gemm_path(w4.INT4_G128, 400, 512, 3072) == "tiled"
     # a large tiled grid (>= 256 tiles): the mid kernel up to 48 rows
-    assert w4.gemm_path(w4.INT4_G128, 48, 65536, 3072) == "mid"
-    assert w4.gemm_path(w4.INT4_G128, 49, 65536, 3072) == "tiled"
+    assert w4.gemm_path(w4.INT4_G128, 64, 65536, 3072) == "mid"
+    assert w4.gemm_path(w4.INT4_G128, 65, 65536, 3072) == "tiled"
     assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072) == "tiled"
     assert w4.gemm_path(w4.MXFP4, 4096, 8192, 3072, "skinny") == "skinny"
     assert w4.gemm_path(w4.INT4_G128, 1, 64, 128, "tiled") == "tiled"

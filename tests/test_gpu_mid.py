@@ -1,6 +1,8 @@
 """Parity of the mid kernel (tiles of 32 columns x 32..64 rows, split-K over
 the waves; chosen for 16 < M <= 384 on wide matrices) with the oracle,
-through the C ABI.
+through the C ABI.  Its ring variant (every operand through per-wave LDS copy
+slots) runs whenever its LDS fits beside the scale windows -- 48- and 64-row
+tiles that do not fit become 32-row tiles -- and the per-lane form beyond.
 
 Every element within the gate |C - C_ref| <= 2e-3 S + 1e-6 (+ 2^-8 |C_ref|
 for bf16 output).  Covered: the row-tile shapes (2, 3 and 4 slices of 16
@@ -84,12 +86,15 @@ def test_mid_ragged_k_and_n(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [
-    (w4.INT4_G128, 40, 72, 8192),    # scale windows in LDS, two passes over K
-    (w4.INT4_G128, 20, 40, 32768),   # int4 windows past the staging registers: per-lane loads
-    (w4.NVFP4, 40, 72, 8192),        # per-lane loads
-    (w4.MXFP4, 36, 50, 8192),        # per-lane loads
-    (w4.MXFP4, 24, 64, 6144),        # LDS, U = 4
-    (w4.NVFP4, 24, 40, 3104),        # LDS, partial last k-block
+    (w4.INT4_G128, 40, 72, 8192),    # ring, 48-row tiles
+    (w4.INT4_G128, 20, 40, 32768),   # ring, 24 KB of windows, 3 slots
+    (w4.NVFP4, 40, 72, 8192),        # ring, 16 KB window
+    (w4.NVFP4, 64, 72, 8192),        # 64-row tiles past the ring's LDS: 32-row tiles
+    (w4.MXFP4, 36, 50, 8192),
+    (w4.MXFP4, 24, 64, 6144),
+    (w4.NVFP4, 24, 40, 3104),        # partial last k-block
+    (w4.NVFP4, 20, 40, 65536),       # 128 KB window: the per-lane form
+    (w4.INT4_G32, 24, 40, 32768),    # 96 KB of scale and zero windows: the per-lane form
 ])
 def test_mid_large_k(fmt, M, N, K):
     _check(fmt, M, N, K, path="mid", odts=(torch.float32,))
@@ -101,8 +106,8 @@ def test_mid_scale_windows_off_dword_boundary(fmt):
     offs = [1, 3] if fmt == w4.MXFP4 else [2]
     for off in offs:
         _check(fmt, 40, 100, 512, path="mid", s_off=off, z_off=1, odts=(torch.float32,))
-    # and with per-lane scale loads
-    _check(fmt, 20, 40, 32768 if fmt == w4.INT4_G128 else 8192, path="mid", s_off=offs[0], z_off=3,
+    # and in the per-lane form (windows too large for the ring)
+    _check(fmt, 20, 40, 65536 if fmt == w4.NVFP4 else 131072, path="mid", s_off=offs[0], z_off=3,
            odts=(torch.float32,))
 
 

@@ -11,9 +11,6 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows with 32-bit ints
 constexpr int64_t kMaxK = (int64_t)1 << 22;    // a 256-row tile of A fits a 32-bit byte offset
 
-bool is_int4(int fmt) {
-  return fmt == W4A16_INT4_G128 || fmt == W4A16_INT4_G32 || fmt == W4A16_INT4_G64 || fmt == W4A16_INT4_SYM;
-}
 // formats whose weights come with a zero array (required non-NULL; NULL
 // required for every other format)
 bool has_zeros(int fmt) {
@@ -67,12 +64,12 @@ int choose_path(int format, int64_t M, int64_t N) {
   if (forced) return forced;
   if (M <= 16) return W4A16_PATH_SKINNY;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles >= 256) return M <= 48 ? W4A16_PATH_MID : W4A16_PATH_TILED;
+  if (tiles >= 256) return M <= 64 ? W4A16_PATH_MID : W4A16_PATH_TILED;
   const int64_t mid_wgs = ((N + 31) / 32) * ((M + 63) / 64);
   if (mid_wgs < 160) return M <= 384 ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
-  const int64_t rounds = (mid_wgs + 255) / 256;
-  const int max_rounds = is_int4(format & W4A16_FORMAT_MASK) ? 3 : 2;
-  return rounds <= max_rounds ? W4A16_PATH_MID : W4A16_PATH_TILED;
+  // up to 3.5 rounds of 256 workgroups (measured crossover against the
+  // tiled kernel, every format)
+  return mid_wgs <= 896 ? W4A16_PATH_MID : W4A16_PATH_TILED;
 }
 
 hipError_t launch_path(int path, const w4a16::GemmArgs& a) {
