@@ -26,7 +26,7 @@ def to_dev(case):
     packed = torch.from_numpy(case.packed).to(DEV)
     if case.fmt in w4.INT4_FORMATS:
         scales = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
-        zeros = torch.from_numpy(case.zeros).to(DEV)
+        zeros = torch.from_numpy(case.zeros).to(DEV) if case.zeros is not None else None
     else:
         scales = torch.from_numpy(case.scales).to(DEV)
         zeros = None
@@ -312,6 +312,7 @@ def test_deterministic_and_stream(fmt, M, N, K):
 @pytest.mark.parametrize("fmt,M,N,K,path", [(w4.INT4_G128, 1, 4096, 3072, "auto"),
                                             (w4.NVFP4, 16, 1024, 512, "auto"),
                                             (w4.NVFP4, 64, 1024, 512, "mid"),
+                                            (w4.NVFP4, 16, 1024, 8192, "auto"),   # skinny ring
                                             (w4.MXFP4, 300, 512, 256, "tiled"),
                                             (w4.INT4_G64, 40, 300, 512, "skinny")])
 def test_hip_graph_capture_replay(fmt, M, N, K, path):
@@ -337,7 +338,7 @@ def test_hip_graph_capture_replay(fmt, M, N, K, path):
 
 # ---- exact single-atom and chain-graph checks ----------------------------------------
 
-@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.NVFP4, w4.MXFP4, w4.INT4_G32, w4.INT4_G64])
+@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.NVFP4, w4.MXFP4, w4.INT4_G32, w4.INT4_G64, w4.INT4_SYM])
 @pytest.mark.parametrize("path", ["skinny", "mid", "tiled"])
 def test_integer_data_is_exact(fmt, path):
     """One MFMA atom's worth of rows and columns (16 x 16) over one or a few
