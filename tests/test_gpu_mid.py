@@ -87,8 +87,8 @@ def test_mid_ragged_k_and_n(fmt, M, N, K):
 
 @pytest.mark.parametrize("fmt,M,N,K", [
     (w4.INT4_G128, 40, 72, 8192),    # ring, 48-row tiles
-    (w4.INT4_G128, 20, 40, 32768),   # ring, 24 KB of windows, 3 slots
-    (w4.INT4_G32, 20, 40, 16384),    # ring, 48 KB of windows: 2 slots
+    (w4.INT4_G128, 20, 40, 32768),   # ring, 24 KB of windows
+    (w4.INT4_G32, 20, 40, 16384),    # ring, 48 KB of windows
     (w4.NVFP4, 40, 72, 8192),        # ring, 16 KB window
     (w4.NVFP4, 64, 72, 8192),        # 64-row tiles past the ring's LDS: 32-row tiles
     (w4.MXFP4, 36, 50, 8192),

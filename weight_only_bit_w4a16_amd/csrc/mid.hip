@@ -612,9 +612,9 @@ hipError_t launch_ring(const GemmArgs& a, unsigned lds) {
   return hipSuccess;
 }
 
-// The ring variant when its LDS fits beside the scale windows: 3 slots per
-// wave for 32-row tiles, else 2; tiles of 48 or 64 rows that do not fit
-// become 32-row tiles.  W4A16_MID_RING=0 never (tuning).
+// The ring variant when its LDS fits beside the scale windows, 2 slots per
+// wave (measured: 3 slots or 2 / 3 waves are no faster); tiles of 48 or 64
+// rows that do not fit become 32-row tiles.  W4A16_MID_RING=0 never (tuning).
 template <int FMT, bool OUT_F32>
 bool try_mid_ring(const GemmArgs& a, int MS, hipError_t& err) {
   static const int env = [] {
@@ -629,10 +629,6 @@ bool try_mid_ring(const GemmArgs& a, int MS, hipError_t& err) {
   constexpr int64_t kLds = 160 * 1024;
   if (MS > 2 && win + (int64_t)kMidRingWaves * 2 * mid_ring_slot(MS) > kLds) MS = 2;
   auto lds_of = [&](int d) { return win + (int64_t)kMidRingWaves * d * mid_ring_slot(MS); };
-  if (MS == 2 && lds_of(3) <= kLds) {
-    err = launch_ring<FMT, OUT_F32, 2, 3>(a, (unsigned)lds_of(3));
-    return true;
-  }
   if (lds_of(2) > kLds) return false;
   const unsigned lds = (unsigned)lds_of(2);
   err = MS == 2 ? launch_ring<FMT, OUT_F32, 2, 2>(a, lds)
