@@ -84,6 +84,7 @@ def test_ring_partial_and_short(fmt, M, N, K):
     (w4.NVFP4, 16, 24, 32768),     # 32 KB scale window: two slots per wave
     (w4.INT4_G32, 4, 20, 32768),   # 48 KB of scale and zero windows: two slots
     (w4.MXFP4, 16, 20, 16384),     # 8 KB window: three slots
+    (w4.NVFP4, 16, 20, 81920),     # 80 KB window: no ring fits, the per-pass copies instead
 ])
 def test_ring_large_windows(fmt, M, N, K):
     _check(fmt, M, N, K, odts=(torch.float32,))
