@@ -23,6 +23,10 @@
 //   * scales (and zeros) of the workgroup's 32 rows are one contiguous block:
 //     copied once to LDS with coalesced dword loads when it fits the staging
 //     registers (S_LDS), else each lane loads its own with its weights.
+// That is the per-lane form.  The ring variant below (used whenever its LDS
+// fits) keeps the tile and the operand layouts but moves every operand by
+// global -> LDS copies, and decodes int4 with groups of 128 as the exact
+// code - zero (one MFMA chain, the scale once per k-block).
 #include <stdlib.h>
 
 #include "common.hpp"
