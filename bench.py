@@ -54,7 +54,8 @@ def algorithmic_bytes(fmt, M, N, K, out):
     """Bytes the method must move once: packed + scales (+ zeros) + A + C."""
     G = GROUP[fmt]
     int4 = fmt in INT4_FORMATS
-    weight = N * K // 2 + N * (K // G) * (2 if int4 else 1) + (N * (K // G) if fmt in ZERO_FORMATS else 0)
+    ng = (K + G - 1) // G  # groups per row (the last may be shorter)
+    weight = N * K // 2 + N * ng * (2 if int4 else 1) + (N * ng if fmt in ZERO_FORMATS else 0)
     io = M * K * 2 + M * N * (4 if out == "f32" else 2)
     return weight, weight + io
 

@@ -34,16 +34,19 @@
  * never allocates, frees or keeps them.  All arrays are row-major and dense:
  *   A       bf16  (M, K)                    16-byte aligned
  *   packed  uint8 (N, K/2)                  16-byte aligned
- *   scales  int4: bf16 (N, K/G), G = 128 / 32 / 64 (128 for INT4_SYM)   2-byte aligned
+ *   scales  int4: bf16 (N, ceil(K/G)), G = 128 / 32 / 64 (128 for INT4_SYM)   2-byte aligned
  *           NVFP4: e4m3 bytes (N, K/16)     2-byte aligned
  *           MXFP4: e8m0 bytes (N, K/32)
- *   zeros   int4 G128 / G32 / G64: uint8 (N, K/G); must be NULL for
+ *   zeros   int4 G128 / G32 / G64: uint8 (N, ceil(K/G)); must be NULL for
  *           INT4_SYM, NVFP4 and MXFP4
  *   C       bf16 or fp32 (M, N)             aligned to its element size
  *   W       bf16 (N, K)                     16-byte aligned (dequant output)
  * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing and
  * checks no pointer);
- * 0 < K <= 2^22, K % 32 == 0, and K % G == 0 for int4 (G its group); M, N < 2^31.
+ * 0 < K <= 2^22, K % 32 == 0 (16-byte weight rows); M, N < 2^31.  Groups
+ * start at k = 0 and run along K; when K is not a multiple of the group (int4
+ * with groups of 128 or 64), the last group of each row is the shorter rest
+ * and has its own scale (and zero), hence ceil(K/G) of them per row.
  * Zero points: the GEMM and the dequantisation take any zero byte 0..255
  * (the format stores 0..15).
  *
@@ -97,9 +100,8 @@ extern "C" {
 /* ---- status codes --------------------------------------------------------- */
 #define W4A16_OK 0
 #define W4A16_ERR_FORMAT (-1) /* unknown format or flag bits                 */
-#define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 32 != 0, K not a
-                                 multiple of the group, M or N >= 2^31, or
-                                 K > 2^22                                   */
+#define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 32 != 0, M or N
+                                 >= 2^31, or K > 2^22                       */
 #define W4A16_ERR_NULL (-3)   /* a required pointer is NULL, or zeros is
                                  non-NULL for a format without zeros
                                  (INT4_SYM, NVFP4, MXFP4)                   */

@@ -131,11 +131,29 @@ def bf16_values(bits: np.ndarray) -> np.ndarray:
 
 # ---- dequant / GEMM ---------------------------------------------------------
 
+def _check_sizes(fmt, N, K, packed, scales, zeros, A=None, M=0):
+    """The C code trusts its arguments: refuse arrays too small for (M, N, K)
+    before any of it runs (groups per row = ceil(K / G), the last one may be
+    shorter)."""
+    if fmt not in GROUP or K <= 0 or K % 2 or N < 0 or M < 0:
+        raise ValueError("oracle: bad format or shape")
+    ng = (K + GROUP[fmt] - 1) // GROUP[fmt]
+    if packed is None or packed.size < N * (K // 2):
+        raise ValueError("oracle: packed smaller than (N, K/2)")
+    if scales is None or scales.size < N * ng:
+        raise ValueError("oracle: scales smaller than (N, ceil(K/G))")
+    if fmt in ZERO_FORMATS and (zeros is None or zeros.size < N * ng):
+        raise ValueError("oracle: zeros smaller than (N, ceil(K/G))")
+    if A is not None and A.size < M * K:
+        raise ValueError("oracle: A smaller than (M, K)")
+
+
 def dequant(fmt: int, packed, scales, zeros, N: int, K: int):
     """Return (w_exact float64 (N, K), w_bf16 uint16 (N, K))."""
     packed = _c(packed, np.uint8)
     scales = _scales(fmt, scales)
     zeros = _c(zeros, np.uint8)
+    _check_sizes(fmt, N, K, packed, scales, zeros)
     w = np.empty((N, K), np.float64)
     wb = np.empty((N, K), np.uint16)
     rc = _load().orc_dequant(fmt, _ptr(packed), _ptr(scales), _ptr(zeros), N, K,
@@ -152,6 +170,7 @@ def gemm(fmt: int, A_bits, packed, scales, zeros, M: int, N: int, K: int,
     packed = _c(packed, np.uint8)
     scales = _scales(fmt, scales)
     zeros = _c(zeros, np.uint8)
+    _check_sizes(fmt, N, K, packed, scales, zeros, A_bits, M)
     C = np.empty((M, N), np.float64)
     S = np.empty((M, N), np.float64)
     rc = _load().orc_gemm(fmt, _ptr(A_bits), _ptr(packed), _ptr(scales), _ptr(zeros),
@@ -168,6 +187,7 @@ def gemm_at(fmt: int, A_bits, packed, scales, zeros, M: int, N: int, K: int,
     packed = _c(packed, np.uint8)
     scales = _scales(fmt, scales)
     zeros = _c(zeros, np.uint8)
+    _check_sizes(fmt, N, K, packed, scales, zeros, A_bits, M)
     mi = _c(m_idx, np.int64)
     ni = _c(n_idx, np.int64)
     C = np.empty(len(mi), np.float64)

@@ -45,6 +45,9 @@
  *   - the int4 group is a parameter of the format ([KB]'s configuration
  *     carries it as `group`, 128 in its fixture): formats 3 and 4 are the
  *     same asymmetric int4 with groups of 32 and 64 contiguous inputs.
+ *   - groups start at k = 0 and run along K ([KB]'s group index i // 128);
+ *     when K is not a multiple of the group, the last group of a row is the
+ *     shorter rest with its own scale (and zero): ceil(K/G) per row.
  *   - format 5, symmetric int4: [KB] names only the cost of ignoring its
  *     weights' zero point; the symmetric encoding read here is the usual one
  *     for unsigned 4-bit codes -- no zero array, the zero point of every
@@ -173,7 +176,7 @@ double orc_weight(int fmt, const uint8_t* packed, const void* scales,
                   int64_t k) {
   (void)N;
   int64_t G = group_of(fmt);
-  int64_t g = k / G, groups = K / G;
+  int64_t g = k / G, groups = (K + G - 1) / G; /* the last group may be shorter */
   unsigned code = code_at(packed, K, n, k);
   if (is_int4(fmt)) {
     double s = orc_bf16_value(((const uint16_t*)scales)[n * groups + g]);
@@ -192,7 +195,7 @@ double orc_weight(int fmt, const uint8_t* packed, const void* scales,
 int orc_dequant(int fmt, const uint8_t* packed, const void* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, double* w_exact,
                 uint16_t* w_bf16) {
-  if (fmt < 0 || fmt >= ORC_NFORMATS || N < 0 || K <= 0 || K % group_of(fmt) != 0) return -1;
+  if (fmt < 0 || fmt >= ORC_NFORMATS || N < 0 || K <= 0 || K % 2 != 0) return -1;
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) {
       double w = orc_weight(fmt, packed, scales, zeros, N, K, n, k);
@@ -227,7 +230,7 @@ static void dot_row(const uint16_t* A, int64_t K, int64_t m, const double* wrow,
 int orc_gemm(int fmt, const uint16_t* A, const uint8_t* packed,
              const void* scales, const uint8_t* zeros, int64_t M, int64_t N,
              int64_t K, int weights_bf16, double* C, double* S) {
-  if (fmt < 0 || fmt >= ORC_NFORMATS || M < 0 || N < 0 || K <= 0 || K % group_of(fmt) != 0)
+  if (fmt < 0 || fmt >= ORC_NFORMATS || M < 0 || N < 0 || K <= 0 || K % 2 != 0)
     return -1;
   int err = 0;
 #pragma omp parallel
@@ -258,7 +261,7 @@ int orc_gemm_at(int fmt, const uint16_t* A, const uint8_t* packed,
                 const void* scales, const uint8_t* zeros, int64_t M, int64_t N,
                 int64_t K, int64_t count, const int64_t* m_idx,
                 const int64_t* n_idx, double* C, double* S) {
-  if (fmt < 0 || fmt >= ORC_NFORMATS || K <= 0 || K % group_of(fmt) != 0) return -1;
+  if (fmt < 0 || fmt >= ORC_NFORMATS || K <= 0 || K % 2 != 0) return -1;
   for (int64_t i = 0; i < count; ++i)
     if (m_idx[i] < 0 || m_idx[i] >= M || n_idx[i] < 0 || n_idx[i] >= N) return -1;
   int err = 0;

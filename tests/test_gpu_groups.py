@@ -49,8 +49,7 @@ def _bits(t):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(8192, 3072), (33, 160), (7, 64)])
 def test_dequant_bit_exact(fmt, N, K):
-    if K % oracle.GROUP[fmt]:
-        pytest.skip("K not a multiple of the group")
+    # K = 160 with groups of 64: a last group of 32 (its own scale and zero)
     case = inputs.make_case(fmt, 0, N, K, seed=N + K)
     _, p, s, z = _dev(case)
     W = _bits(w4.dequant(fmt, p, s, z))

@@ -75,8 +75,22 @@ def test_code_equal_to_zero_is_zero_and_steps_by_the_scale(fmt):
                 assert w[n, k] == 0.0
 
 
-def test_group_size_must_divide_k():
-    case = inputs.make_case(oracle.INT4_G32, 0, 2, 96, seed=14)
-    oracle.dequant(oracle.INT4_G32, case.packed, case.scales, case.zeros, 2, 96)
+def test_ragged_last_group_is_the_shorter_rest():
+    # K = 96 with groups of 64: group 0 covers k 0..63, group 1 the rest
+    # (k 64..95) with its own scale and zero -- the same weights as groups of
+    # 32 carrying (g0, g0, g1); likewise K = 160 with groups of 128
+    for fmt, K, expand in ((oracle.INT4_G64, 96, [0, 0, 1]), (oracle.INT4_G128, 160, [0, 0, 0, 0, 1])):
+        case = inputs.make_case(fmt, 2, 3, K, seed=14)
+        assert case.scales.shape == (3, 2) and case.zeros.shape == (3, 2)
+        w, b = oracle.dequant(fmt, case.packed, case.scales, case.zeros, 3, K)
+        w32, b32 = oracle.dequant(oracle.INT4_G32, case.packed, case.scales[:, expand],
+                                  case.zeros[:, expand], 3, K)
+        assert np.array_equal(w, w32) and np.array_equal(b, b32)
+        C, S = oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, 2, 3, K)
+        C32, S32 = oracle.gemm(oracle.INT4_G32, case.A, case.packed, case.scales[:, expand],
+                               case.zeros[:, expand], 2, 3, K)
+        assert np.array_equal(C, C32) and np.array_equal(S, S32)
+    # arrays short of ceil(K / G) groups are refused before the C code runs
+    case = inputs.make_case(oracle.INT4_G64, 0, 2, 96, seed=15)
     with pytest.raises(ValueError):
         oracle.dequant(oracle.INT4_G64, case.packed, case.scales[:, :1], case.zeros[:, :1], 2, 96)

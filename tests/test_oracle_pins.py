@@ -339,7 +339,7 @@ def test_gemm_at_matches_full():
 def test_bad_shapes_rejected():
     with pytest.raises(ValueError):
         oracle.dequant(oracle.INT4_G128, np.zeros((1, 50), np.uint8), np.zeros((1, 1), np.uint16),
-                       np.zeros((1, 1), np.uint8), 1, 100)
+                       np.zeros((1, 1), np.uint8), 1, 101)   # odd K
     with pytest.raises(ValueError):
         oracle.gemm(7, np.zeros((1, 32), np.uint16), np.zeros((1, 16), np.uint8),
                     np.zeros((1, 1), np.uint8), None, 1, 1, 32)

@@ -130,14 +130,15 @@ def _check_weights(fmt, packed, scales, zeros, N, K, device):
     if fmt not in GROUP:
         raise ValueError(f"unknown format {fmt}")
     G = GROUP[fmt]
-    if K % 32 or K % G:
-        raise ValueError(f"K={K} must be a multiple of 32 and of the group size {G}")
+    if K % 32:
+        raise ValueError(f"K={K} must be a multiple of 32")
+    groups = (K + G - 1) // G  # the last group may be shorter
     _check(packed, "packed", (N, K // 2), 1, device)
-    _check(scales, "scales", (N, K // G), 2 if fmt in INT4_FORMATS else 1, device)
+    _check(scales, "scales", (N, groups), 2 if fmt in INT4_FORMATS else 1, device)
     if fmt in ZERO_FORMATS:
         if zeros is None:
             raise ValueError("asymmetric int4 weights need zeros")
-        _check(zeros, "zeros", (N, K // G), 1, device)
+        _check(zeros, "zeros", (N, groups), 1, device)
     elif zeros is not None:
         raise ValueError(f"{FORMAT_NAMES[fmt]} weights take no zeros")
 

@@ -17,16 +17,6 @@ bool has_zeros(int fmt) {
   return fmt == W4A16_INT4_G128 || fmt == W4A16_INT4_G32 || fmt == W4A16_INT4_G64;
 }
 
-int group_of(int fmt) {
-  switch (fmt) {
-    case W4A16_INT4_G128: return 128;
-    case W4A16_INT4_SYM: return 128;
-    case W4A16_NVFP4: return 16;
-    case W4A16_INT4_G64: return 64;
-    default: return 32;  // MXFP4, INT4_G32
-  }
-}
-
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // format, flags and shape checks shared by w4a16_gemm and w4a16_gemm_path
@@ -40,7 +30,7 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
     return W4A16_ERR_FORMAT;
   }
   if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_SHAPE;
-  if (K % 32 != 0 || K % group_of(fmt) != 0) return W4A16_ERR_SHAPE;
+  if (K % 32 != 0) return W4A16_ERR_SHAPE;  // the last group may be shorter than G
   if (M >= kMaxDim || N >= kMaxDim || K > kMaxK) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t chunks_per_row = K / 32;
   const int64_t total = N * chunks_per_row;
   constexpr int G = FormatTraits<FMT>::kGroup;
-  const int64_t groups = K / G;
+  const int64_t groups = (K + G - 1) / G;  // the last group may be shorter
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t n = i / chunks_per_row;

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
   constexpr int SB = mid_sb<FMT>();
   // int4: the group of 32-code chunk c is c >> GS (the k-block for G = 128)
   constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
-  const int groups = K / G;
+  const int groups = (K + G - 1) / G;  // the last group may be shorter
   const uint32_t rowb = (uint32_t)(K >> 1);
   const int rows = min(kMidCols, N - n0);
   const int arows = min(16 * MS, M - m0);
@@ -187,9 +187,12 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
         q[u][h] = buf_load_b128(wr, ok ? r * rowb + (uint32_t)c * 16u : kBufferOOB);
         if constexpr (!S_LDS) {
           if constexpr (is_int4(FMT)) {
+            // groups of 128: the k-block's group for every chunk, also past
+            // K (the MFMA sums the four chunks before the scale is applied)
             const uint32_t gi = r * (uint32_t)groups + (uint32_t)(is_int4_g128(FMT) ? kb : c >> GS);
-            sraw[u][h] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
-            zraw[u][h] = has_zeros(FMT) ? buf_load_b8(zr, ok ? gi : kBufferOOB) : kSymZero;
+            const bool sok = is_int4_g128(FMT) ? kb < KB : ok;
+            sraw[u][h] = buf_load_b16(sr, sok ? gi * 2u : kBufferOOB);
+            zraw[u][h] = has_zeros(FMT) ? buf_load_b8(zr, sok ? gi : kBufferOOB) : kSymZero;
           } else if constexpr (FMT == kNvfp4) {
             sraw[u][h] = buf_load_b16(sr, ok ? r * (uint32_t)groups + 2u * (uint32_t)c : kBufferOOB);
           } else {
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
   constexpr int G = FormatTraits<FMT>::kGroup;
   constexpr int SB = mid_sb<FMT>();
   constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
-  const int groups = K / G;
+  const int groups = (K + G - 1) / G;  // the last group may be shorter
   const uint32_t rowb = (uint32_t)(K >> 1);
   const int rows = min(kMidCols, N - n0);
   const int arows = min(16 * MS, M - m0);
@@ -548,7 +551,8 @@ MidPlan mid_plan(int fmt, int64_t M, int64_t K) {
   if (p.MS < 2) p.MS = 2;
   // scale windows in LDS when every dword has a staging register
   const bool int4 = is_int4(fmt);
-  const int64_t groups = K / (is_int4_g128(fmt) ? 128 : fmt == kNvfp4 ? 16 : fmt == kInt4G64 ? 64 : 32);
+  const int64_t G = is_int4_g128(fmt) ? 128 : fmt == kNvfp4 ? 16 : fmt == kInt4G64 ? 64 : 32;
+  const int64_t groups = (K + G - 1) / G;
   const int64_t sb = int4 ? 2 : 1;
   const int64_t slots = (int64_t)kMidSStage * 64 * p.waves;
   const int64_t s_cap = mid_cap((uint32_t)(kMidCols * groups * sb));
@@ -627,7 +631,7 @@ bool try_mid_ring(const GemmArgs& a, int MS, hipError_t& err) {
   }();
   if (env == 0) return false;
   constexpr int SB = mid_sb<FMT>();
-  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t groups = (a.K + FormatTraits<FMT>::kGroup - 1) / FormatTraits<FMT>::kGroup;
   const int64_t win = mid_ring_window((uint32_t)(kMidCols * groups * SB)) +
                       (has_zeros(FMT) ? mid_ring_window((uint32_t)(kMidCols * groups)) : 0);
   constexpr int64_t kLds = 160 * 1024;

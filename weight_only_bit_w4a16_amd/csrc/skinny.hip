@@ -217,7 +217,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   constexpr int SB = is_int4(FMT) ? 2 : 1;  // bytes per scale
   // int4: the group of 32-code chunk c is c >> GS (the k-block for G = 128)
   constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
-  const int groups = K / G;
+  const int groups = (K + G - 1) / G;  // the last group may be shorter
 
   // Buffer descriptors over exactly this workgroup's 16 weight rows and 16 A
   // rows: rows past N or M, and k past K, read as 0 (hardware range check).
@@ -322,9 +322,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
       if constexpr (is_int4(FMT)) {
+        // groups of 128: every chunk of a k-block takes the k-block's group,
+        // also chunks past K -- the MFMA sums the four chunks before the
+        // lane applies the scale to its rows of the sum
         const uint32_t gi = (uint32_t)(nl * groups + (is_int4_g128(FMT) ? kb : c >> GS));
-        sraw[u] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
-        zraw[u] = has_zeros(FMT) ? buf_load_b8(zr, ok ? gi : kBufferOOB) : kSymZero;
+        const bool sok = is_int4_g128(FMT) ? kb < KB : ok;
+        sraw[u] = buf_load_b16(sr, sok ? gi * 2u : kBufferOOB);
+        zraw[u] = has_zeros(FMT) ? buf_load_b8(zr, sok ? gi : kBufferOOB) : kSymZero;
       } else if constexpr (FMT == kNvfp4) {
         // the chunk's two e4m3 scales (blocks 2c and 2c+1), one 16-bit load
         sraw[u] = buf_load_b16(sr, ok ? (uint32_t)(nl * groups + 2 * c) : kBufferOOB);
@@ -399,7 +403,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
         const bool ok = FULL || c < chunks;
         const uint8_t* sb = a_lds + s_off + s_delta;
         if constexpr (is_int4(FMT)) {
-          const int gi = nl * groups + (ok ? (is_int4_g128(FMT) ? kb : c >> GS) : 0);
+          // groups of 128: the k-block's group for every chunk (see issue);
+          // past the last k-block (nothing loaded) group 0 keeps the read
+          // inside the window
+          const int gi = nl * groups + (is_int4_g128(FMT) ? (kb < KB ? kb : 0) : (ok ? c >> GS : 0));
           sraw[u] = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
           zraw[u] = has_zeros(FMT) ? (uint32_t)(a_lds + z_off + z_delta)[gi] : kSymZero;
         } else if constexpr (FMT == kNvfp4) {
@@ -517,7 +524,7 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
   constexpr int G = FormatTraits<FMT>::kGroup;
   constexpr int SB = is_int4(FMT) ? 2 : 1;
   constexpr int GS = G == 128 ? 2 : (G == 64 ? 1 : 0);
-  const int groups = K / G;
+  const int groups = (K + G - 1) / G;  // the last group may be shorter
   const int rows = min(grp.rows, N - n0);
   const int arows = min(16, M - m0);
 
@@ -601,7 +608,9 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
     const bool ok = FULL || c < chunks;
     uint32_t sraw, zraw = 0u;
     if constexpr (is_int4(FMT)) {
-      const int gi = nl * groups + (ok ? (is_int4_g128(FMT) ? kb : c >> GS) : 0);
+      // groups of 128: the k-block's group for every chunk, also past K (the
+      // MFMA sums the four chunks before the scale is applied)
+      const int gi = nl * groups + (is_int4_g128(FMT) ? kb : (ok ? c >> GS : 0));
       sraw = *reinterpret_cast<const uint16_t*>(sb + 2 * gi);
       zraw = has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero;
     } else if constexpr (FMT == kNvfp4) {
@@ -655,7 +664,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
   const int KB = K >> 7;
   constexpr int G = FormatTraits<FMT>::kGroup;
   constexpr int SB = is_int4_g128(FMT) ? 2 : 1;
-  const int groups = K / G;
+  const int groups = (K + G - 1) / G;  // the last group may be shorter
   const uint32_t rowb = (uint32_t)(K >> 1);
   const uint32_t wave_slot0 = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 64u;
   const int kw = __builtin_amdgcn_readfirstlane(wave) * U;  // this wave's first k-block
@@ -977,7 +986,7 @@ bool try_ring(const GroupedArgs& a, hipError_t& err) {
   }();
   if (env == 0) return false;
   constexpr int SB = is_int4(FMT) ? 2 : 1;
-  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t groups = (a.K + FormatTraits<FMT>::kGroup - 1) / FormatTraits<FMT>::kGroup;
   const int64_t win = ring_window_cap((uint32_t)(16 * groups * SB)) +
                       (has_zeros(FMT) ? ring_window_cap((uint32_t)(16 * groups)) : 0);
   dim3 grid;
@@ -1009,7 +1018,7 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   // LDS: A rows + a zero row (16-byte aligned), then the scale and zero windows
   const unsigned lds_a = a_lds ? (unsigned)(((arows + 1) * a.K * 2 + 15) & ~15) : 0u;
   constexpr int SB = is_int4(FMT) ? 2 : 1;
-  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t groups = (a.K + FormatTraits<FMT>::kGroup - 1) / FormatTraits<FMT>::kGroup;
   const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
   const int64_t z_cap = has_zeros(FMT) ? (16 * groups + 6 + 15) & ~15 : 0;
   const int64_t lds_s = s_cap + z_cap;
@@ -1113,7 +1122,7 @@ bool try_stream(const GroupedArgs& a, int64_t min_tiles, hipError_t& err) {
   const int64_t a16 = a.M * a.K / 8;
   if (a16 > kAStage * threads || a.M * a.K * 2 > 64 * 1024) return false;
   constexpr int SB = is_int4_g128(FMT) ? 2 : 1;
-  const int64_t groups = a.K / FormatTraits<FMT>::kGroup;
+  const int64_t groups = (a.K + FormatTraits<FMT>::kGroup - 1) / FormatTraits<FMT>::kGroup;
   const int64_t s_words = (16 * groups * SB + 6) / 4, z_words = (16 * groups + 6) / 4;
   const int NS = s_words <= threads ? 1 : (s_words <= 2 * threads ? 2 : 0);
   if (NS == 0 || (FMT == kInt4 && z_words > threads)) return false;

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   const int n_base = tn * BN;
   const int KT = (K + BK - 1) / BK;
   constexpr int G = FormatTraits<FMT>::kGroup;
-  const int groups = K / G;
+  const int groups = (K + G - 1) / G;  // the last group may be shorter
 
   // Buffer descriptors over this workgroup's rows: rows past M / N read as 0.
   const uint32_t arow_b = (uint32_t)K * 2u, brow_b = (uint32_t)K >> 1;

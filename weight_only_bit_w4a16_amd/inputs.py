@@ -64,19 +64,20 @@ def make_activations(rng: np.random.Generator, M: int, K: int) -> np.ndarray:
 
 def make_weights(rng: np.random.Generator, fmt: int, N: int, K: int):
     G = GROUP[fmt]
-    if K % G or K % 2:
-        raise ValueError(f"K={K} must be a multiple of the group size {G}")
+    if K % 2:
+        raise ValueError(f"K={K} must be even")
+    ng = (K + G - 1) // G  # groups per row; the last one may be shorter
     packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     zeros = None
     if fmt in ZERO_FORMATS:
-        zeros = rng.integers(0, 16, size=(N, K // G), dtype=np.uint8)
-        scales = bf16_bits(rng.uniform(0.005, 0.02, size=(N, K // G)))
+        zeros = rng.integers(0, 16, size=(N, ng), dtype=np.uint8)
+        scales = bf16_bits(rng.uniform(0.005, 0.02, size=(N, ng)))
     elif fmt == INT4_SYM:
-        scales = bf16_bits(rng.uniform(0.005, 0.02, size=(N, K // G)))
+        scales = bf16_bits(rng.uniform(0.005, 0.02, size=(N, ng)))
     elif fmt == NVFP4:
-        scales = e4m3_bytes(rng.uniform(2.0 ** -4, 4.0, size=(N, K // G)))
+        scales = e4m3_bytes(rng.uniform(2.0 ** -4, 4.0, size=(N, ng)))
     elif fmt == MXFP4:
-        scales = (127 + rng.integers(-4, 5, size=(N, K // G))).astype(np.uint8)
+        scales = (127 + rng.integers(-4, 5, size=(N, ng))).astype(np.uint8)
     else:
         raise ValueError(f"unknown format {fmt}")
     return packed, scales, zeros
