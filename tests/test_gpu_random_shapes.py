@@ -1,0 +1,61 @@
+"""Seeded random shapes: every format, every kernel choice, through the C ABI.
+
+A hundred and twenty cases drawn once from a fixed seed: format (all six),
+M in 1 .. 300, N in 1 .. 600, K a multiple of 32 up to 4096 (so int4 with
+groups of 128 or 64 often has a shorter last group), output bf16 or fp32,
+path auto / skinny / mid / tiled.  Each must meet the gate |C - C_ref| <= 2e-3 S + 1e-6 (+ 2^-8 |C_ref|
+for bf16 output) against the oracle in every element.  The case list is
+printed before each launch so that a failure names its shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_bit_w4a16_amd as w4
+from weight_only_bit_w4a16_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+FMTS = [w4.INT4_G128, w4.NVFP4, w4.MXFP4, w4.INT4_G32, w4.INT4_G64, w4.INT4_SYM]
+PATHS = ["auto", "skinny", "mid", "tiled"]
+
+
+def _cases(n=120, seed=2024, budget=12_000_000):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        fmt = FMTS[rng.integers(len(FMTS))]
+        M = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 17, 24, 33, 48, 64, 100, 130, 200, 300]))
+        N = int(rng.integers(1, 601))
+        K = 32 * int(rng.integers(1, 129))
+        if M * N * K > budget:
+            continue
+        out.append((fmt, M, N, K, PATHS[rng.integers(len(PATHS))], bool(rng.integers(2)), len(out)))
+    return out
+
+
+def _dev(case):
+    A = torch.from_numpy(case.A.view(np.int16)).to(DEV).view(torch.bfloat16)
+    p = torch.from_numpy(case.packed).to(DEV)
+    if case.fmt in w4.INT4_FORMATS:
+        s = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        s = torch.from_numpy(case.scales).to(DEV)
+    z = torch.from_numpy(case.zeros).to(DEV) if case.zeros is not None else None
+    return A, p, s, z
+
+
+@pytest.mark.parametrize("fmt,M,N,K,path,f32,i", _cases())
+def test_random_shape(fmt, M, N, K, path, f32, i):
+    odt = torch.float32 if f32 else torch.bfloat16
+    print(f"[random {i}] fmt {fmt} {M}x{N}x{K} path {path} -> {w4.gemm_path(fmt, M, N, K, path)} "
+          f"out {odt}", flush=True)
+    case = inputs.make_case(fmt, M, N, K, seed=7000 + i)
+    A, p, s, z = _dev(case)
+    C = w4.gemm(fmt, A, p, s, z, out_dtype=odt, path=path)
+    torch.cuda.synchronize()
+    Cref, S = oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
+    r = oracle.gate_ratio(C.double().cpu().numpy(), Cref, S, not f32)
+    print(f"[gate] max err/bound = {r:.3e}", flush=True)
+    assert r <= 1.0
