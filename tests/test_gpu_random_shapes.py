@@ -3,9 +3,10 @@
 A hundred and twenty cases drawn once from a fixed seed: format (all six),
 M in 1 .. 300, N in 1 .. 600, K a multiple of 32 up to 4096 (so int4 with
 groups of 128 or 64 often has a shorter last group), output bf16 or fp32,
-path auto / skinny / mid / tiled.  Each must meet the gate |C - C_ref| <= 2e-3 S + 1e-6 (+ 2^-8 |C_ref|
-for bf16 output) against the oracle in every element.  The case list is
-printed before each launch so that a failure names its shape.
+path auto / skinny / mid / tiled.  Each must meet the gate
+|C - C_ref| <= 2e-3 S + 1e-6 (+ 2^-8 |C_ref| for bf16 output) against the
+oracle in every element.  Each case prints its shape before its launch, so
+that a failure names it.
 """
 import numpy as np
 import pytest

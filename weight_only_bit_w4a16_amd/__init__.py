@@ -3,8 +3,10 @@
 ``C = A . dequant(packed, scales, zeros)^T`` with bf16 activations A (M, K),
 4-bit weights packed (N, K/2) uint8 (low nibble = even k) and fp32
 accumulation.  Formats: ``INT4_G128`` (bf16 scale + uint8 zero per 128 k;
-``INT4_G32`` / ``INT4_G64``: the same per 32 / 64 k), ``NVFP4`` (e2m1 codes,
-e4m3 scale per 16 k), ``MXFP4`` (e2m1 codes, e8m0 scale per 32 k).
+``INT4_G32`` / ``INT4_G64``: the same per 32 / 64 k; ``INT4_SYM``: bf16 scale
+per 128 k, zero point 8, no zero array), ``NVFP4`` (e2m1 codes, e4m3 scale per
+16 k), ``MXFP4`` (e2m1 codes, e8m0 scale per 32 k).  K is a multiple of 32;
+the last group of a row may be shorter than the group size.
 
 This module only marshals arguments to the C ABI declared in
 ``include/w4a16.h``: it checks that tensor shapes, dtypes and devices agree
