@@ -1,12 +1,15 @@
-"""Seeded random shapes: every format, every kernel choice, through the C ABI.
+"""Seeded random shapes: every format, every kernel choice, single and grouped
+launches, through the C ABI.
 
 A hundred and twenty cases drawn once from a fixed seed: format (all six),
 M in 1 .. 300, N in 1 .. 600, K a multiple of 32 up to 4096 (so int4 with
 groups of 128 or 64 often has a shorter last group), output bf16 or fp32,
 path auto / skinny / mid / tiled.  Each must meet the gate
 |C - C_ref| <= 2e-3 S + 1e-6 (+ 2^-8 |C_ref| for bf16 output) against the
-oracle in every element.  Each case prints its shape before its launch, so
-that a failure names it.
+oracle in every element.  Forty grouped launches (1 .. 8 members of N up to
+4000, M up to 64, path auto or skinny) must in addition equal their single
+launches bit for bit.  Each case prints its shape before its launch, so that a
+failure names it.
 """
 import numpy as np
 import pytest
@@ -60,3 +63,33 @@ def test_random_shape(fmt, M, N, K, path, f32, i):
     r = oracle.gate_ratio(C.double().cpu().numpy(), Cref, S, not f32)
     print(f"[gate] max err/bound = {r:.3e}", flush=True)
     assert r <= 1.0
+
+
+def _grouped_cases(n=40, seed=2025):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = FMTS[rng.integers(len(FMTS))]
+        M = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 32, 64]))
+        K = 32 * int(rng.integers(1, 161))
+        Ns = tuple(int(rng.integers(1, 4001)) for _ in range(int(rng.integers(1, 9))))
+        out.append((fmt, M, K, Ns, ["auto", "skinny"][rng.integers(2)], bool(rng.integers(2)), i))
+    return out
+
+
+@pytest.mark.parametrize("fmt,M,K,Ns,path,f32,i", _grouped_cases())
+def test_random_grouped(fmt, M, K, Ns, path, f32, i):
+    """Grouped launches of 1 .. 8 members sharing A: every member within the
+    gate against the oracle and equal bit for bit to its single launch."""
+    odt, view = (torch.float32, torch.int32) if f32 else (torch.bfloat16, torch.int16)
+    print(f"[random grouped {i}] fmt {fmt} M {M} K {K} N {Ns} path {path} out {odt}", flush=True)
+    cases = [inputs.make_case(fmt, M, N, K, seed=8000 + 10 * i + j) for j, N in enumerate(Ns)]
+    A = _dev(cases[0])[0]
+    weights = [_dev(c)[1:] for c in cases]
+    outs = w4.gemm_grouped(fmt, A, weights, out_dtype=odt, path=path)
+    singles = [w4.gemm(fmt, A, p, s, z, out_dtype=odt, path=path) for p, s, z in weights]
+    torch.cuda.synchronize()
+    for j, (case, out, single) in enumerate(zip(cases, outs, singles)):
+        assert torch.equal(out.view(view), single.view(view)), f"member {j}"
+        Cref, S = oracle.gemm(fmt, cases[0].A, case.packed, case.scales, case.zeros, M, Ns[j], K)
+        assert oracle.gate_ratio(out.double().cpu().numpy(), Cref, S, not f32) <= 1.0, f"member {j}"
