@@ -38,7 +38,7 @@ def _dev(case):
     p = torch.from_numpy(case.packed).to(DEV)
     if case.fmt in w4.INT4_FORMATS:
         s = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
-        z = torch.from_numpy(case.zeros).to(DEV)
+        z = torch.from_numpy(case.zeros).to(DEV) if case.zeros is not None else None
     else:
         s = torch.from_numpy(case.scales).to(DEV)
         z = None
@@ -135,3 +135,31 @@ def test_epilogue_identity_settings_match_plain_gemm():
         ex = w4.gemm(fmt, A, p, s, z, path=path, residual=R, beta=0.0, activation="none")
         torch.cuda.synchronize()
         assert torch.equal(plain.view(torch.int16), ex.view(torch.int16)), kernel
+
+
+def _random_cases(n=48, seed=2026):
+    rng = np.random.default_rng(seed)
+    fmts = [w4.INT4_G128, w4.NVFP4, w4.MXFP4, w4.INT4_G32, w4.INT4_G64, w4.INT4_SYM]
+    out = []
+    while len(out) < n:
+        fmt = fmts[rng.integers(len(fmts))]
+        M = int(rng.choice([1, 2, 5, 16, 17, 40, 64, 130, 260]))
+        N = int(rng.integers(1, 700))
+        K = 32 * int(rng.integers(1, 200))
+        if M * N * K > 15_000_000:
+            continue
+        path = ["auto", "skinny", "mid", "tiled"][rng.integers(4)]
+        act = ACTS[rng.integers(len(ACTS))]
+        odt = [torch.bfloat16, torch.float32][rng.integers(2)]
+        wb, wr, inp = bool(rng.integers(2)), bool(rng.integers(2)), bool(rng.integers(4) == 0)
+        alpha = float(rng.choice([1.0, 0.5, -1.25, 2.0]))
+        beta = float(rng.choice([1.0, 0.0, 0.75, -2.0])) if (wr or inp) else 0.0
+        out.append((fmt, M, N, K, path, act, odt, wb, wr or inp, alpha, beta, inp, len(out)))
+    return out
+
+
+@pytest.mark.parametrize("fmt,M,N,K,path,act,odt,wb,wr,alpha,beta,inp,i", _random_cases())
+def test_epilogue_random(fmt, M, N, K, path, act, odt, wb, wr, alpha, beta, inp, i):
+    """Seeded random shapes, formats, paths and epilogue settings (bias or not,
+    residual or not, in place or not, alpha / beta, every activation)."""
+    _check(f"random {i}", fmt, M, N, K, path, act, odt, wb, wr, alpha, beta, in_place=inp, seed=600 + i)
