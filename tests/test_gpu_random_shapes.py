@@ -8,8 +8,9 @@ path auto / skinny / mid / tiled.  Each must meet the gate
 |C - C_ref| <= 2e-3 S + 1e-6 (+ 2^-8 |C_ref| for bf16 output) against the
 oracle in every element.  Forty grouped launches (1 .. 8 members of N up to
 4000, M up to 64, path auto or skinny) must in addition equal their single
-launches bit for bit.  Each case prints its shape before its launch, so that a
-failure names it.
+launches bit for bit.  Thirty dequantisations of random N and K must equal
+the oracle's bf16 weights bit for bit.  Each case prints its shape before its
+launch, so that a failure names it.
 """
 import numpy as np
 import pytest
@@ -93,3 +94,23 @@ def test_random_grouped(fmt, M, K, Ns, path, f32, i):
         assert torch.equal(out.view(view), single.view(view)), f"member {j}"
         Cref, S = oracle.gemm(fmt, cases[0].A, case.packed, case.scales, case.zeros, M, Ns[j], K)
         assert oracle.gate_ratio(out.double().cpu().numpy(), Cref, S, not f32) <= 1.0, f"member {j}"
+
+
+def _dequant_cases(n=30, seed=2027):
+    rng = np.random.default_rng(seed)
+    return [(FMTS[rng.integers(len(FMTS))], int(rng.integers(1, 3000)), 32 * int(rng.integers(1, 257)), i)
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("fmt,N,K,i", _dequant_cases())
+def test_random_dequant_bit_exact(fmt, N, K, i):
+    """Random N (1 .. 2999) and K (multiples of 32 up to 8192): the bf16
+    weights equal the oracle's bit for bit."""
+    print(f"[random dequant {i}] fmt {fmt} {N}x{K}", flush=True)
+    case = inputs.make_case(fmt, 0, N, K, seed=9000 + i)
+    _, p, s, z = _dev(case)
+    W = w4.dequant(fmt, p, s, z)
+    torch.cuda.synchronize()
+    got = W.view(torch.int16).cpu().numpy().view(np.uint16)
+    _, ref = oracle.dequant(fmt, case.packed, case.scales, case.zeros, N, K)
+    assert np.array_equal(got, ref)
