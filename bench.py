@@ -6,20 +6,29 @@ asymmetric group-128 weights, M = 1, N = 8192, K = 3072, bf16 output.  One
 step = one w4a16_gemm call.  `value` = weight GB/s = (packed + scales +
 zeros bytes) per step / time per step, inputs resident in HBM.  The weights
 rotate over enough distinct copies (>= 1 GiB) that no step finds them in the
-256 MB last-level cache.  The same line also carries the compute-bound point
-of the metric: MXFP4, M = 4096, N = 8192, K = 3072, in TFLOP/s.
+256 MB last-level cache.  The same line carries the other workloads of the
+metric, each with its own roofline fraction: the tiny int4 GEMM (M = 16), the
+NVFP4 M = 16 GEMM, the compute-bound MXFP4 M = 4096 GEMM (TFLOP/s) and the
+197-GEMV decode chain of a 3B decoder.
 
-Timing: W warm-up steps, then a spin kernel fills the stream so that the K
-timed launches run back to back; two HIP events on the launch stream bracket
-the K steps, `ms_per_step` = their distance / K, and the roofline's `achieved`
-uses the same mean duration per launch.  The 197-GEMV decode chain is
-captured once as a HIP graph and replayed (its eager time is reported too).
+Timing.  Warm-up: the W requested steps, then whole passes over every
+rotating weight copy until at least two passes and 50 ms of GPU work have run
+(first touch of each copy, clock ramp).  Then a spin kernel fills the stream
+so that the K timed launches run back to back, with about 1 ms of untimed
+steps queued right behind it (the spin idles the GPU, whose clocks would
+otherwise still be ramping for the first timed steps); HIP events on the
+launch stream bracket the K steps (from 500 steps on they split them into 5
+equal repeats, whose median per-step time is reported beside the mean).  `ms_per_step` = total / K, and
+the roofline's `achieved` uses the same mean duration per launch.  The decode
+chain is captured once as a HIP graph and replayed (its eager time and the
+time of 197 single launches are reported too).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Inputs are synthetic (seeded numpy draws: A ~ N(0, 1) in bf16, uniform codes,
 scales / zeros drawn as the workload states).  The CPU baseline is the plain
-fp64 oracle on the same workload (a bounded number of repetitions).
+fp64 oracle on the same workload (a bounded number of repetitions, on all host
+threads and on one).
 """
 from __future__ import annotations
 
@@ -28,6 +37,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "W4A16 GEMM: weight GB/s at M=1 and TFLOP/s at M=4096 vs MI355X roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+REPEATS = 5                  # the timed steps are split into this many repeats
 
 # name -> (format, M, N, K, output dtype name)
 WORKLOADS = {
@@ -68,9 +79,11 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
+CSRC = "weight_only_bit_w4a16_amd/csrc/"
 KERNEL_SOURCES = {
-    "skinny": ["weight_only_bit_w4a16_amd/csrc/skinny.hip", "weight_only_bit_w4a16_amd/csrc/common.hpp"],
-    "tiled": ["weight_only_bit_w4a16_amd/csrc/tiled.hip", "weight_only_bit_w4a16_amd/csrc/common.hpp"],
+    "skinny": [CSRC + "skinny.hip", CSRC + "common.hpp"],
+    "mid": [CSRC + "mid.hip", CSRC + "common.hpp"],
+    "tiled": [CSRC + "tiled.hip", CSRC + "common.hpp"],
 }
 
 
@@ -79,7 +92,7 @@ def traffic_from_profile(kernel, workload):
     profiles/traffic_<kernel>_<workload>.txt (lines "key value"), or None when
     there is none or the kernel's source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
     rec = {}
     with open(path) as f:
@@ -90,6 +103,39 @@ def traffic_from_profile(kernel, workload):
     if rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return int(float(rec["hbm_bytes_per_launch"]))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def hbm_roofline(bytes_per_launch, launch_ms, kernel, workload, traffic=True):
+    ach = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(kernel, workload) if traffic else None,
+            "kernel": kernel, "mean_launch_us": round(launch_ms * 1e3, 3),
+            "bytes_per_launch": int(bytes_per_launch)}
+
+
+def mfma_roofline(flops, launch_ms, kernel, workload, traffic=True):
+    ach = flops / (launch_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profile(kernel, workload) if traffic else None,
+            "kernel": kernel, "mean_launch_us": round(launch_ms * 1e3, 3), "flops_per_launch": flops}
+
+
+def progress(msg):
+    """One line on stderr per finished piece of work (the JSON line is stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -107,8 +153,10 @@ def main():
                          "activation into the GEMM (w4a16_gemm_ex); their bytes count as traffic")
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight copies to rotate over (0: enough for >= 1 GiB)")
-    ap.add_argument("--m4096-steps", type=int, default=300)
-    ap.add_argument("--no-m4096", action="store_true")
+    ap.add_argument("--side-steps", type=int, default=300,
+                    help="timed steps of each additional workload on the default line")
+    ap.add_argument("--no-side", action="store_true",
+                    help="default line: time the decode GEMV only")
     ap.add_argument("--no-ungrouped", action="store_true",
                     help="decode chain: skip timing the 197 ungrouped launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -175,18 +223,16 @@ def main():
 
     cyc_per_ms = spin_cycles_per_ms()
 
-    def timed(calls_per_step, steps, warmup, graph=False):
+    def timed(calls_per_step, steps, warmup, graph=False, min_warm_ms=50.0):
         """Time `steps` steps; step i runs the prepared calls
-        calls_per_step[i % len(calls_per_step)].  Returns total ms between
-        HIP events recorded on the launch stream around the timed steps.
+        calls_per_step[i % len(calls_per_step)].  Returns (total ms between
+        HIP events around the timed steps, per-step ms of each of the
+        REPEATS equal parts).  Warm-up: `warmup` steps, then whole passes over
+        every rotation until >= 2 passes and >= min_warm_ms of GPU time.
         Eager: a spin kernel first fills the stream so the launches queue up
         and run back to back.  Graph: each rotation's calls are captured
         once into a HIP graph and the graphs are replayed."""
         nrot = len(calls_per_step)
-        for i in range(warmup):
-            for c in calls_per_step[i % nrot]:
-                c()
-        torch.cuda.synchronize()
         runs = [None] * nrot
         if graph:
             for r in range(nrot):
@@ -195,28 +241,50 @@ def main():
                     for c in calls_per_step[r]:
                         c()
                 runs[r] = g
-            for r in range(nrot):
-                runs[r].replay()
-            torch.cuda.synchronize()
-        launches = steps * len(calls_per_step[0])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        # queue fill: ~10 us of host time per eager launch (~50 per replay), plus margin
-        torch.cuda._sleep(int(cyc_per_ms * (((0.05 * steps) if graph else (0.010 * launches)) + 20.0)))
-        e0.record()
-        for i in range(steps):
+
+        def one(i):
             if graph:
                 runs[i % nrot].replay()
             else:
                 for c in calls_per_step[i % nrot]:
                     c()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
 
-    def measure_single(fmt, M, N, K, out, steps, warmup):
+        for i in range(warmup):
+            one(i)
+        torch.cuda.synchronize()
+        t0, passes = time.perf_counter(), 0
+        while passes < 2 or (time.perf_counter() - t0) * 1e3 < min_warm_ms:
+            for i in range(nrot):
+                one(i)
+            torch.cuda.synchronize()
+            passes += 1
+        step_ms = (time.perf_counter() - t0) * 1e3 / (passes * nrot)  # upper bound (host-paced)
+        # untimed steps queued behind the spin kernel, >= ~1 ms of GPU work,
+        # so the timed steps start at working clocks (the spin idles the GPU)
+        pre = max(8, min(4000, math.ceil(1.0 / max(step_ms, 1e-4))))
+        launches = (steps + pre) * len(calls_per_step[0])
+        # each event recorded between launches costs about a launch gap, so a
+        # short run keeps the one pair around all of its steps
+        parts = REPEATS if steps >= 100 * REPEATS else 1
+        bounds = [round(steps * j / parts) for j in range(parts + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(parts + 1)]
+        # queue fill: ~10 us of host time per eager launch (~50 per replay), plus margin
+        torch.cuda._sleep(int(cyc_per_ms * (((0.05 * (steps + pre)) if graph else (0.010 * launches)) + 20.0)))
+        for i in range(pre):
+            one(steps + i)
+        ev[0].record()
+        for j in range(parts):
+            for i in range(bounds[j], bounds[j + 1]):
+                one(i)
+            ev[j + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[j].elapsed_time(ev[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(parts)]
+        return ev[0].elapsed_time(ev[parts]), per
+
+    def measure_single(fmt, M, N, K, out, steps, warmup, epilogue=None):
         """One GEMM workload timed over `steps` launches that rotate over
         enough distinct weight copies (>= 1 GiB together) that every launch
-        reads its weights from HBM.  Returns (case, total ms, copies, kernel)."""
+        reads its weights from HBM."""
         case = inputs.make_case(fmt, M, N, K, seed=0)
         A, p, s, z = to_dev(case)
         _, tbytes = algorithmic_bytes(fmt, M, N, K, out)
@@ -224,29 +292,49 @@ def main():
         odt = torch.float32 if out == "f32" else torch.bfloat16
         C = torch.empty((M, N), dtype=odt, device=dev)
         epi = {}
-        if args.epilogue:
+        if epilogue:
             g = torch.Generator(device="cpu").manual_seed(1)
             epi = dict(bias=torch.randn(N, generator=g).to(dev, torch.bfloat16),
                        residual=torch.randn((M, N), generator=g).to(dev, odt),
-                       alpha=1.0, beta=1.0, activation=args.epilogue)
+                       alpha=1.0, beta=1.0, activation=epilogue)
         calls = []
         for r in range(copies):
             pr = p if r == 0 else p.clone()
             sr = s if r == 0 else s.clone()
             zr = z if (r == 0 or z is None) else z.clone()
             calls.append([w4.PreparedGemm(fmt, A, pr, sr, zr, C, path=args.path, **epi)])
-        total = timed(calls, steps, warmup)
+        total, per = timed(calls, steps, warmup)
         kernel = calls[0][0].kernel
         del calls, C
-        return case, total, copies, kernel
+        progress(f"{w4.FORMAT_NAMES[fmt]} M={M} N={N} K={K}: {total / steps * 1e3:.3f} us per launch "
+                 f"({kernel}, {steps} steps)")
+        return {"case": case, "ms": total / steps, "median_ms": statistics.median(per),
+                "copies": copies, "kernel": kernel}
 
-    result = {}
-    if args.workload == CHAIN:
+    def single_entry(name, steps, warmup):
+        fmt, M, N, K, out = WORKLOADS[name]
+        r = measure_single(fmt, M, N, K, out, steps, warmup)
+        wbytes, tbytes = algorithmic_bytes(fmt, M, N, K, out)
+        e = {"workload": name, "format": w4.FORMAT_NAMES[fmt], "M": M, "N": N, "K": K, "out": out,
+             "kernel": r["kernel"], "steps": steps, "weight_copies": r["copies"],
+             "ms_per_step": round(r["ms"], 6), "median_ms_per_step": round(r["median_ms"], 6)}
+        if M > 16:
+            e["tflops"] = round(2.0 * M * N * K / (r["ms"] * 1e-3) / 1e12, 1)
+            e["roofline"] = mfma_roofline(2 * M * N * K, r["ms"], r["kernel"], name)
+        else:
+            e["weight_gbs"] = round(wbytes / (r["ms"] * 1e-3) / 1e9, 1)
+            e["roofline"] = hbm_roofline(tbytes, r["ms"], r["kernel"], name)
+        return e, r
+
+    def measure_chain(steps, warmup, ungrouped=True):
+        """The 197 int4 GEMVs of a 3B decoder's decode step (per layer q, k,
+        v, o, gate, up, down, then the LM head), each with its own A, timed as
+        replays of one captured HIP graph per pass."""
         shapes = inputs.decoder_chain_shapes()
         calls, wbytes, tbytes = [], 0, 0
         out = torch.empty((1, max(n for _, n, _ in shapes)), dtype=torch.bfloat16, device=dev)
         dev_w, dev_a = [], []
-        for i, (name, n, k) in enumerate(shapes):
+        for i, (_, n, k) in enumerate(shapes):
             case = inputs.make_case(0, 1, n, k, inputs.chain_seed(0, i))
             A, p, s, z = to_dev(case)
             dev_w.append((p, s, z))
@@ -255,72 +343,61 @@ def main():
             wb, tb = algorithmic_bytes(0, 1, n, k, "bf16")
             wbytes += wb
             tbytes += tb
-        # the framework's decode step: matrices that read the same input in one launch
-        gcalls, gouts = [], []
+        # matrices that read the same input in one launch
+        gcalls = []
         for grp in inputs.decoder_chain_groups():
             A = dev_a[grp[0]]
             if len(grp) == 1:
                 gcalls.append(calls[grp[0]])
                 continue
             outs = [torch.empty((1, shapes[i][1]), dtype=torch.bfloat16, device=dev) for i in grp]
-            gouts.append(outs)
             gcalls.append(w4.PreparedGroupedGemm(0, A, [dev_w[i] for i in grp], outs, path=args.path))
-        eager_ms = timed([gcalls], max(1, args.steps // 10), args.warmup) / max(1, args.steps // 10)
-        ungrouped_ms = None if args.no_ungrouped else \
-            timed([calls], args.steps, args.warmup, graph=True) / args.steps
-        total_ms = timed([gcalls], args.steps, args.warmup, graph=True)
-        ms = total_ms / args.steps
-        launches_per_step = len(gcalls)
-        kernel = calls[0].kernel
-        bytes_per_launch = tbytes / len(gcalls)
-        config = {"workload": CHAIN, "matrices": len(calls), "M": 1, "format": "int4_g128",
-                  "out": "bf16", "launches_per_step": len(gcalls),
-                  "grouping": "per layer [q,k,v] [o] [gate,up] [down], then [lm_head]",
-                  "timing": "hip_graph_replay", "eager_ms_per_step": round(eager_ms, 4),
-                  "ungrouped_launches_per_step": len(calls),
-                  "ungrouped_ms_per_step": None if ungrouped_ms is None else round(ungrouped_ms, 4)}
-        value = wbytes / (ms * 1e-3) / 1e9
-        unit = "GB/s"
-        workload = CHAIN
-        weight_bytes = wbytes
+        esteps = max(1, steps // 10)
+        eager_ms = timed([gcalls], esteps, warmup)[0] / esteps
+        ungrouped_ms = timed([calls], steps, warmup, graph=True)[0] / steps if ungrouped else None
+        total_ms, per = timed([gcalls], steps, warmup, graph=True)
+        ms = total_ms / steps
+        progress(f"decode chain: {ms * 1e3:.1f} us per pass (graph), eager {eager_ms * 1e3:.1f} us")
+        e = {"workload": CHAIN, "matrices": len(calls), "M": 1, "format": "int4_g128", "out": "bf16",
+             "launches_per_step": len(gcalls),
+             "grouping": "per layer [q,k,v] [o] [gate,up] [down], then [lm_head]",
+             "timing": "hip_graph_replay", "steps": steps, "ms_per_step": round(ms, 6),
+             "median_ms_per_step": round(statistics.median(per), 6),
+             "eager_ms_per_step": round(eager_ms, 4), "ungrouped_launches_per_step": len(calls),
+             "ungrouped_ms_per_step": None if ungrouped_ms is None else round(ungrouped_ms, 4),
+             "weight_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1)}
+        # the roofline of the whole pass: all its bytes over the step time
+        e["roofline"] = hbm_roofline(tbytes, ms, calls[0].kernel, CHAIN)
+        e["roofline"]["bytes_per_launch"] = None
+        e["roofline"]["bytes_per_step"] = int(tbytes)
+        e["roofline"]["mean_launch_us"] = round(ms * 1e3 / len(gcalls), 3)
+        return e, wbytes
+
+    if args.workload == CHAIN:
+        e, wbytes = measure_chain(args.steps, args.warmup, ungrouped=not args.no_ungrouped)
+        ms = e["ms_per_step"]
+        value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
+        roof = e.pop("roofline")
+        config = e
     else:
         fmt, M, N, K, out = WORKLOADS[args.workload]
-        case, total_ms, copies, kernel = measure_single(fmt, M, N, K, out, args.steps, args.warmup)
+        r = measure_single(fmt, M, N, K, out, args.steps, args.warmup, epilogue=args.epilogue)
+        ms = r["ms"]
         wbytes, tbytes = algorithmic_bytes(fmt, M, N, K, out)
         if args.epilogue:  # + bias (bf16) + residual (C's dtype)
             tbytes += N * 2 + M * N * (4 if out == "f32" else 2)
-        ms = total_ms / args.steps
-        launches_per_step = 1
-        bytes_per_launch = tbytes
         config = {"workload": args.workload, "format": w4.FORMAT_NAMES[fmt], "M": M, "N": N, "K": K,
-                  "out": out, "weight_copies": copies, "kernel": kernel}
+                  "out": out, "weight_copies": r["copies"], "kernel": r["kernel"],
+                  "median_ms_per_step": round(r["median_ms"], 6)}
         if args.epilogue:
             config["epilogue"] = {"bias": "bf16", "residual": out, "beta": 1.0,
                                   "activation": args.epilogue}
-        workload = args.workload
-        weight_bytes = wbytes
         if M > 16:
-            value = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-            unit = "TFLOP/s"
+            value, unit = 2.0 * M * N * K / (ms * 1e-3) / 1e12, "TFLOP/s"
+            roof = mfma_roofline(2 * M * N * K, ms, r["kernel"], args.workload, traffic=not args.epilogue)
         else:
-            value = wbytes / (ms * 1e-3) / 1e9
-            unit = "GB/s"
-
-    mean_launch_ms = ms / launches_per_step
-    if args.workload != CHAIN and WORKLOADS[args.workload][1] > 16:
-        fmt, M, N, K, out = WORKLOADS[args.workload]
-        ach = 2.0 * M * N * K / (mean_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                "traffic": None if args.epilogue else traffic_from_profile(kernel, workload)}
-    else:
-        ach = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": None if args.epilogue else traffic_from_profile(kernel, workload)}
-    roof["kernel"] = kernel
-    roof["mean_launch_us"] = round(mean_launch_ms * 1e3, 3)
-    roof["bytes_per_launch"] = int(bytes_per_launch) if unit == "GB/s" else None
+            value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
+            roof = hbm_roofline(tbytes, ms, r["kernel"], args.workload, traffic=not args.epilogue)
 
     result = {
         "metric": METRIC,
@@ -339,46 +416,61 @@ def main():
         "roofline": roof,
     }
 
-    # ---- the compute-bound point of the metric: MXFP4 at M = 4096 -------------
-    if args.workload == "decode_gemv_int4_m1" and not args.no_m4096:
-        fmt, M, N, K, out = WORKLOADS["mxfp4_m4096"]
-        _, t4, copies4, kernel4 = measure_single(fmt, M, N, K, out, args.m4096_steps, 10)
-        tfl = 2.0 * M * N * K / (t4 / args.m4096_steps * 1e-3) / 1e12
-        result["m4096"] = {"workload": "mxfp4_m4096", "kernel": kernel4, "steps": args.m4096_steps,
-                           "weight_copies": copies4,
-                           "ms_per_step": round(t4 / args.m4096_steps, 4),
-                           "tflops": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
-                           "frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
+    # ---- the metric's other workloads, each with its own roofline -------------
+    if args.workload == "decode_gemv_int4_m1" and not args.no_side and not args.shape:
+        side = {}
+        for name in ("tiny_int4_m16", "nvfp4_m16", "mxfp4_m4096"):
+            side[name] = single_entry(name, args.side_steps, 10)[0]
+        side[CHAIN] = measure_chain(min(args.side_steps, 200), 5)[0]
+        result["workloads"] = side
 
     # ---- CPU baseline: the oracle on the same workload ------------------------
     if not args.no_cpu_baseline and args.workload != CHAIN and not args.shape:
         import oracle
         fmt, M, N, K, out = WORKLOADS[args.workload]
-        if args.workload == "mxfp4_m4096":
+        case = inputs.make_case(fmt, M, N, K, seed=0)
+        if M > 16:
             # 256 sampled outputs per repetition (the full product is 103 G MACs)
             rng = np.random.default_rng(0)
             mi, ni = rng.integers(0, M, 256), rng.integers(0, N, 256)
             fn = lambda: oracle.gemm_at(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K, mi, ni)
             per_rep_units = 2.0 * 256 * K / 1e12
-            cunit, sample = "TFLOP/s", "256 sampled outputs of the M=4096 MXFP4 GEMM per repetition"
+            cunit, sample = "TFLOP/s", f"256 sampled outputs of the {args.workload} GEMM per repetition"
         else:
-            case = inputs.make_case(fmt, M, N, K, seed=0)
             fn = lambda: oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
-            per_rep_units = weight_bytes / 1e9
+            per_rep_units = wbytes / 1e9
             cunit = "GB/s"
             sample = f"the full {args.workload} GEMM (M={M}, N={N}, K={K}) per repetition"
-        fn()  # warm
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            fn()
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        result["cpu_baseline"] = {"value": round(per_rep_units * reps / el, 6), "unit": cunit,
-                                  "cores": oracle.num_threads(), "kind": "oracle",
-                                  "sample": f"{sample}, {reps} repetitions in {el:.1f} s "
-                                            "(plain fp64 C oracle, OpenMP over output rows)"}
+
+        def rate(seconds):
+            fn()  # warm
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    return per_rep_units * reps / el, reps, el
+
+        threads = oracle.num_threads()
+        v_all, reps, el = rate(args.cpu_seconds)
+        progress(f"cpu baseline: {v_all:.4f} {cunit} on {threads} threads")
+        oracle.set_num_threads(1)
+        v_one, reps1, el1 = rate(max(1.0, args.cpu_seconds / 2))
+        # the dequantisation alone (single-threaded loop in the oracle)
+        t0 = time.perf_counter()
+        oracle.dequant(fmt, case.packed, case.scales, case.zeros, N, K)
+        dq_s = time.perf_counter() - t0
+        oracle.set_num_threads(threads)
+        result["cpu_baseline"] = {
+            "value": round(v_all, 6), "unit": cunit, "cores": threads, "kind": "oracle",
+            "sample": f"{sample}, {reps} repetitions in {el:.1f} s on {threads} threads "
+                      "(plain fp64 C oracle, OpenMP over output rows)",
+            "single_thread_value": round(v_one, 6),
+            "single_thread_sample": f"{reps1} repetitions in {el1:.1f} s on 1 thread",
+            "dequant_ms": round(dq_s * 1e3, 1),
+            "dequant_sample": f"oracle dequantisation of the {N} x {K} weights, once, 1 thread",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
     print(json.dumps(result), flush=True)
 
 

@@ -342,3 +342,14 @@ int orc_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Set the number of threads of later parallel loops (timing only; the
+ * results do not depend on it: each output element is one thread's sum). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}
