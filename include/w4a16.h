@@ -57,8 +57,15 @@
  *
  * Errors: every argument is checked on the host BEFORE anything is enqueued;
  * a failed check returns its code and enqueues nothing.  A launch failure
- * reported by the HIP runtime returns W4A16_ERR_HIP.  The library keeps no
- * mutable global state and is safe to call from several host threads.
+ * reported by the HIP runtime for the call's own launch returns W4A16_ERR_HIP
+ * (an earlier error of the calling thread is neither reported nor cleared).
+ *
+ * Threads: the library's only global state is a cache of device properties
+ * (compute units per device, resident workgroups per kernel), filled on first
+ * use through atomics and a mutex; calls are safe from several host threads.
+ * The kernel choice and the summation order depend only on the format, the
+ * flags and M, N, K: nothing read at run time (environment, device state)
+ * changes the output bits.
  */
 #ifndef W4A16_H
 #define W4A16_H

@@ -82,6 +82,8 @@ def _load():
     lib.orc_epilogue.restype = I
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = I
+    lib.orc_set_num_threads.argtypes = [I]
+    lib.orc_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -127,6 +129,18 @@ def bf16_values(bits: np.ndarray) -> np.ndarray:
     f = _load().orc_bf16_value
     flat = np.asarray(bits, dtype=np.uint16).ravel()
     return np.array([f(int(b)) for b in flat], dtype=np.float64).reshape(np.shape(bits))
+
+
+_BF16_TABLE = None
+
+
+def _bf16_table() -> np.ndarray:
+    """bf16_value of all 65536 bit patterns (the C decoder, called once per
+    pattern), for decoding large arrays by lookup."""
+    global _BF16_TABLE
+    if _BF16_TABLE is None:
+        _BF16_TABLE = bf16_values(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    return _BF16_TABLE
 
 
 # ---- dequant / GEMM ---------------------------------------------------------
@@ -180,6 +194,24 @@ def gemm(fmt: int, A_bits, packed, scales, zeros, M: int, N: int, K: int,
     return C, S
 
 
+def gemm_matmul(fmt: int, A_bits, packed, scales, zeros, M: int, N: int, K: int):
+    """The (C, S) of :func:`gemm` for shapes too large for its element-by-element
+    loop: the oracle's exact dequantisation, then binary64 matrix products
+    (numpy's, a library primitive) C = A . W^T and S = |A| . |W|^T.  The sums
+    run in another order than gemm()'s k-ascending loop, so the two differ by
+    binary64 rounding only (at most about K * 2^-53 * S).  Finite weights only:
+    a BLAS product is not required to propagate NaN."""
+    A_bits = _c(A_bits, np.uint16)
+    _check_sizes(fmt, N, K, _c(packed, np.uint8), _scales(fmt, scales), _c(zeros, np.uint8), A_bits, M)
+    w, _ = dequant(fmt, packed, scales, zeros, N, K)
+    if not np.all(np.isfinite(w)):
+        raise ValueError("oracle gemm_matmul: weights must be finite")
+    a = _bf16_table()[A_bits].reshape(M, K)
+    C = a @ w.T
+    S = np.abs(a) @ np.abs(w).T
+    return C, S
+
+
 def gemm_at(fmt: int, A_bits, packed, scales, zeros, M: int, N: int, K: int,
             m_idx, n_idx):
     """Sampled reference: (C[i], S[i]) for each (m_idx[i], n_idx[i])."""
@@ -230,6 +262,11 @@ def epilogue(C, alpha: float = 1.0, bias=None, act: int = ACT_NONE, beta: float 
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (timing only: results do not depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---- the correctness gate ---------------------------------------------------

@@ -28,3 +28,50 @@ def read_golden(name):
             if line:
                 rows.append(line.split())
     return rows
+
+
+def int4_rounding_adversary(fmt, M, N, K, seed):
+    """An int4 case on which weights rounded to bf16 BEFORE the sum fail the
+    GEMM gate by a wide margin (with fp32 output), while exact weights pass.
+
+    Every group holds one repeated code c with zero point z and a bf16 scale s
+    chosen so that the exact weight (c - z) * s lies just above a bf16
+    rounding boundary: rounding it moves it down by more than 3e-3 of its
+    value (the gate allows 2e-3 of S).  Every activation is positive, so the
+    rounding errors of a row add up coherently: |sum a w~ - sum a w| > 3e-3 S.
+    Returns an inputs.Case (the oracle's round_bf16 / bf16_value choose the
+    pairs; nothing comes from the GPU path)."""
+    import numpy as np
+    import oracle
+    from weight_only_bit_w4a16_amd import inputs
+
+    # (d, scale bits) with d = c - z in 1..7 and scale m * 2^-14, m = 128..255:
+    # relative change of d * s when rounded to bf16
+    pairs = []
+    for d in range(1, 8):
+        for m in range(128, 256):
+            bits = (120 << 7) | (m - 128)
+            s = oracle.bf16_value(bits)
+            w = d * s
+            r = (oracle.bf16_value(oracle.round_bf16(w)) - w) / w
+            if r < -3e-3:
+                pairs.append((d, bits))
+    assert pairs, "no adversarial (code - zero, scale) pair"
+    case = inputs.make_case(fmt, M, N, K, seed)
+    rng = np.random.default_rng(seed + 7)
+    G = oracle.GROUP[fmt]
+    ng = (K + G - 1) // G
+    pick = rng.integers(0, len(pairs), size=(N, ng))
+    d = np.array([p[0] for p in pairs])[pick]
+    sbits = np.array([p[1] for p in pairs], dtype=np.uint16)[pick]
+    if fmt == oracle.INT4_SYM:
+        z = np.full((N, ng), 8)
+    else:
+        z = (rng.integers(0, 16, size=(N, ng)) % (16 - d)).astype(np.int64)
+        case.zeros[:] = z.astype(np.uint8)
+    c = (z + d).astype(np.uint8)                       # the code of every weight of the group
+    codes = np.repeat(c, G, axis=1)[:, :K]
+    case.packed[:] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    case.scales[:] = sbits
+    case.A[:] = case.A & np.uint16(0x7FFF)             # |a|: every product has the weight's sign
+    return case

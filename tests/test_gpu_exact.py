@@ -1,0 +1,145 @@
+"""Exactness edges of the HIP kernels (through the C ABI), against the oracle.
+
+* int4 weights enter the sum exactly on every kernel and group size: on data
+  where weights rounded to bf16 before the sum miss the gate by almost 2x
+  (tests/conftest.py int4_rounding_adversary, fp32 output), and on random
+  data at small K, where rounding errors do not average out;
+* an e8m0 scale byte 0xFF (NaN) makes every output of its weight row NaN on
+  every kernel variant, as it makes the oracle's weights NaN; all other
+  outputs stay within the gate.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_bit_w4a16_amd as w4
+from conftest import int4_rounding_adversary
+from weight_only_bit_w4a16_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+INT4 = [w4.INT4_G128, w4.INT4_G32, w4.INT4_G64, w4.INT4_SYM]
+
+
+def to_dev(case):
+    A = torch.from_numpy(case.A.view(np.int16)).to(DEV).view(torch.bfloat16)
+    packed = torch.from_numpy(case.packed).to(DEV)
+    if case.fmt in w4.INT4_FORMATS:
+        scales = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
+        zeros = torch.from_numpy(case.zeros).to(DEV) if case.zeros is not None else None
+    else:
+        scales = torch.from_numpy(case.scales).to(DEV)
+        zeros = None
+    return A, packed, scales, zeros
+
+
+def run(case, path, out_dtype=torch.float32):
+    A, p, s, z = to_dev(case)
+    C = w4.gemm(case.fmt, A, p, s, z, out_dtype=out_dtype, path=path)
+    torch.cuda.synchronize()
+    return C.double().cpu().numpy()
+
+
+def gate(C, case, bf16_out, what, ref=None):
+    if ref is None:
+        ref = oracle.gemm(case.fmt, case.A, case.packed, case.scales, case.zeros, case.M, case.N, case.K)
+    Cref, S = ref
+    r = oracle.gate_ratio(C, Cref, S, bf16_out)
+    print(f"[gate] {what}: max err/bound = {r:.3e}", flush=True)
+    assert r <= 1.0, f"{what}: gate ratio {r}"
+    return r
+
+
+# ---- int4 weights are exact in the sum -----------------------------------------
+
+@pytest.mark.parametrize("K", [32, 64, 160])
+@pytest.mark.parametrize("path", ["skinny", "mid", "tiled"])
+@pytest.mark.parametrize("fmt", INT4)
+def test_int4_coherent_rounding_data(fmt, path, K):
+    """64 x 1024 outputs (fp32) on which bf16-rounded weights reach ~1.9x the
+    gate; exact weights leave only fp32 accumulation error."""
+    case = int4_rounding_adversary(fmt, 64, 1024, K, seed=K + fmt)
+    C = run(case, path)
+    r = gate(C, case, False, f"int4 fmt {fmt} coherent {path} K={K}")
+    assert r < 0.05
+
+
+@pytest.mark.parametrize("fmt", INT4)
+def test_int4_coherent_rounding_data_large_tiles(fmt):
+    """The tiled kernel's 256 x 256 configuration (>= 192 tiles), every output."""
+    M, N, K = 1536, 8200, 64
+    case = int4_rounding_adversary(fmt, M, N, K, seed=5 + fmt)
+    assert w4.gemm_path(fmt, M, N, K) == "tiled"
+    C = run(case, "auto")
+    ref = oracle.gemm_matmul(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
+    r = gate(C, case, False, f"int4 fmt {fmt} coherent large tiles", ref)
+    assert r < 0.05
+
+
+@pytest.mark.parametrize("what,M,N,K,path", [
+    ("stream", 1, 16384, 256, "auto"),    # the streaming skinny variant (groups of 128)
+    ("ring", 16, 512, 8192, "skinny"),    # the skinny ring variant
+    ("mid-ring", 64, 2048, 512, "mid"),   # the mid kernel's ring variant
+])
+def test_int4_coherent_rounding_data_variants(what, M, N, K, path):
+    for fmt in (w4.INT4_G128, w4.INT4_SYM) if what == "stream" else INT4:
+        case = int4_rounding_adversary(fmt, M, N, K, seed=11 + fmt)
+        C = run(case, path)
+        gate(C, case, False, f"int4 fmt {fmt} coherent {what}")
+
+
+@pytest.mark.parametrize("K", [32, 64])
+@pytest.mark.parametrize("path", ["skinny", "mid", "tiled"])
+@pytest.mark.parametrize("fmt", INT4)
+def test_int4_small_k_random(fmt, path, K):
+    """Random data at K = 32 / 64 (fp32 out, 64k outputs, seeds 0-3): bf16
+    rounded weights exceed the gate for some seed here; exact ones do not."""
+    for seed in range(4):
+        case = inputs.make_case(fmt, 64, 1024, K, seed)
+        C = run(case, path)
+        gate(C, case, False, f"int4 fmt {fmt} random {path} K={K} seed {seed}")
+
+
+# ---- NaN e8m0 scales -------------------------------------------------------------
+
+NAN_CASES = [
+    ("skinny A in LDS", 1, 200, 512, "skinny"),
+    ("skinny 16 rows", 16, 96, 1024, "skinny"),
+    ("skinny ring", 16, 80, 8192, "skinny"),
+    ("skinny stream", 1, 16384, 256, "auto"),
+    ("mid ring", 64, 2048, 512, "mid"),
+    ("mid per-lane", 40, 64, 98304, "mid"),
+    ("tiled small tiles", 300, 512, 256, "tiled"),
+    ("tiled large tiles", 1536, 8200, 256, "auto"),
+]
+
+
+@pytest.mark.parametrize("what,M,N,K,path", NAN_CASES, ids=[c[0] for c in NAN_CASES])
+def test_mxfp4_nan_scale_rows(what, M, N, K, path):
+    case = inputs.make_case(w4.MXFP4, M, N, K, seed=M + N)
+    rng = np.random.default_rng(N)
+    ng = K // 32
+    rows = np.unique(np.concatenate([rng.choice(N, min(N, 9), replace=False), [0, N - 1]]))
+    cols = rng.integers(0, ng, size=len(rows))
+    cols[0], cols[-1] = 0, ng - 1          # first and last block of a row
+    case.scales[rows, cols] = 0xFF
+    print(f"[nan] {what}: {M}x{N}x{K} path {path}, NaN blocks in rows {rows.tolist()}", flush=True)
+    for odt in (torch.float32, torch.bfloat16):
+        C = run(case, path, odt)
+        nan_cols = np.zeros(N, bool)
+        nan_cols[rows] = True
+        assert np.all(np.isnan(C[:, nan_cols])), f"{what}: a row with a NaN scale has a non-NaN output"
+        assert not np.any(np.isnan(C[:, ~nan_cols])), f"{what}: NaN outside the NaN rows"
+        keep = np.flatnonzero(~nan_cols)
+        if N * K > 20_000_000:
+            ni = rng.choice(keep, 256, replace=False)
+            mi = rng.integers(0, M, 256)
+            Cref, S = oracle.gemm_at(w4.MXFP4, case.A, case.packed, case.scales, None, M, N, K, mi, ni)
+            r = oracle.gate_ratio(C[mi, ni], Cref, S, odt == torch.bfloat16)
+        else:
+            Cref, S = oracle.gemm(w4.MXFP4, case.A, case.packed, case.scales, None, M, N, K)
+            assert np.all(np.isnan(Cref[:, nan_cols]))
+            r = oracle.gate_ratio(C[:, keep], Cref[:, keep], S[:, keep], odt == torch.bfloat16)
+        print(f"[gate] nan {what} {odt}: max err/bound = {r:.3e}", flush=True)
+        assert r <= 1.0

@@ -360,3 +360,22 @@ def test_decode_chain_bytes_match_page():
     assert packed + meta + kv == g["bytes_per_step"]
     head = [s for s in shapes if s[0] == "lm_head"][0]
     assert head[1] * head[2] // 2 == g["lm_head_packed_bytes"]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_matmul_matches_gemm(fmt):
+    """The matrix-product form (exact dequantisation + binary64 BLAS product,
+    used for the large full-output comparisons) agrees with the
+    element-by-element oracle to binary64 rounding, ragged last group included."""
+    G = oracle.GROUP[fmt]
+    M, N = 24, 96
+    K = 3 * G + 32 if fmt in (oracle.INT4_G128, oracle.INT4_G64, oracle.INT4_SYM) else 8 * G
+    case = inputs.make_case(fmt, M, N, K, seed=23)
+    C, S = oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
+    Cm, Sm = oracle.gemm_matmul(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
+    assert np.all(np.abs(Cm - C) <= K * 2.0 ** -52 * S)
+    assert np.all(np.abs(Sm - S) <= K * 2.0 ** -52 * S)
+    # a planted transposition of the weight is caught
+    Ct, _ = oracle.gemm_matmul(fmt, case.A, case.packed[::-1].copy(), case.scales[::-1].copy(),
+                               None if case.zeros is None else case.zeros[::-1].copy(), M, N, K)
+    assert not np.allclose(Ct, C)

@@ -313,6 +313,61 @@ __device__ __forceinline__ u32x4_t int4x8_to_bf16_weights(uint32_t q, float s, f
   return r;
 }
 
+// 8 int4 codes to their exact weights (code - zero) * scale (at most 16
+// significant bits, exact in fp32) as the sum of two bf16 fragments hi + lo,
+// both exact: hi is the weight rounded to nearest even, lo = weight - hi has
+// at most 8 significant bits.  Two MFMAs over hi and lo then accumulate the
+// exact weights (natural k order).
+__device__ __forceinline__ void int4x8_to_bf16_hilo(uint32_t q, float s, float zf, u32x4_t& hi,
+                                                    u32x4_t& lo) {
+  const uint32_t l = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
+  const uint32_t h = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+  const f32x2_t e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, false);  // k0, k2
+  const f32x2_t e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, true);   // k4, k6
+  const f32x2_t o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 512.0f, false);  // k1, k3
+  const f32x2_t o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 512.0f, true);   // k5, k7
+  const float w[8] = {(e0[0] - zf) * s, (o0[0] - zf) * s, (e0[1] - zf) * s, (o0[1] - zf) * s,
+                      (e1[0] - zf) * s, (o1[0] - zf) * s, (e1[1] - zf) * s, (o1[1] - zf) * s};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p = pack_bf16x2(w[2 * i], w[2 * i + 1]);
+    hi[i] = p;
+    lo[i] = pack_bf16x2(w[2 * i] - __uint_as_float(p << 16), w[2 * i + 1] - __uint_as_float(p & 0xFFFF0000u));
+  }
+}
+
+// 8 int4 codes to code - zero, exact in bf16 (an integer in -255 .. 15),
+// natural k order; the group scale is applied to the fp32 sum afterwards.
+__device__ __forceinline__ u32x4_t int4x8_minus_zero(uint32_t q, float zf) {
+  const uint32_t l = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
+  const uint32_t h = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+  const f32x2_t e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, false);  // k0, k2
+  const f32x2_t e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, true);   // k4, k6
+  const f32x2_t o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 512.0f, false);  // k1, k3
+  const f32x2_t o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 512.0f, true);   // k5, k7
+  u32x4_t r;
+  r[0] = pack_bf16x2(e0[0] - zf, o0[0] - zf);
+  r[1] = pack_bf16x2(e0[1] - zf, o0[1] - zf);
+  r[2] = pack_bf16x2(e1[0] - zf, o1[0] - zf);
+  r[3] = pack_bf16x2(e1[1] - zf, o1[1] - zf);
+  return r;
+}
+
+// ---- NaN e8m0 scales ------------------------------------------------------------
+// An e8m0 byte of 0xFF is NaN, so every weight of its block is NaN and so is
+// every output of that weight row.  The scaled fp4 converters read only the
+// exponent field of their scale, so they cannot produce it: each lane records
+// whether it met such a byte for the weight row it supplies (lane l, row
+// l % 16), and nan_rows16 ORs the records of the four lanes of each row (the
+// lane groups hold different parts of K) into a 16-bit row mask, uniform over
+// the wave.
+__device__ __forceinline__ bool e8m0_is_nan(uint32_t E) { return (E & 0xFFu) == 0xFFu; }
+__device__ __forceinline__ uint32_t nan_rows16(bool bad) {
+  const uint64_t m = __ballot(bad);
+  return (uint32_t)((m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu);
+}
+constexpr uint32_t kQuietNaN = 0x7FC00000u;
+
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
 // does not wait for this wave's outstanding global loads (the fences carry
 // the local address space alone, so only lgkmcnt is drained).

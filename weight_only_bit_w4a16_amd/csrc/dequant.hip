@@ -74,31 +74,24 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, co
   if (blocks > 65536) blocks = 65536;  // grid-stride loop covers the rest
   switch (fmt) {
     case kInt4:
-      hipLaunchKernelGGL(dequant_kernel<kInt4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         packed, scales, zeros, W, N, K);
-      break;
+      return launch_kernel(dequant_kernel<kInt4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           packed, scales, zeros, W, N, K);
     case kNvfp4:
-      hipLaunchKernelGGL(dequant_kernel<kNvfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         packed, scales, zeros, W, N, K);
-      break;
+      return launch_kernel(dequant_kernel<kNvfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           packed, scales, zeros, W, N, K);
     case kInt4G32:
-      hipLaunchKernelGGL(dequant_kernel<kInt4G32>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         packed, scales, zeros, W, N, K);
-      break;
+      return launch_kernel(dequant_kernel<kInt4G32>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           packed, scales, zeros, W, N, K);
     case kInt4G64:
-      hipLaunchKernelGGL(dequant_kernel<kInt4G64>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         packed, scales, zeros, W, N, K);
-      break;
+      return launch_kernel(dequant_kernel<kInt4G64>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           packed, scales, zeros, W, N, K);
     case kInt4Sym:
-      hipLaunchKernelGGL(dequant_kernel<kInt4Sym>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         packed, scales, zeros, W, N, K);
-      break;
+      return launch_kernel(dequant_kernel<kInt4Sym>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           packed, scales, zeros, W, N, K);
     default:
-      hipLaunchKernelGGL(dequant_kernel<kMxfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         packed, scales, zeros, W, N, K);
-      break;
+      return launch_kernel(dequant_kernel<kMxfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                           packed, scales, zeros, W, N, K);
   }
-  return hipGetLastError();
 }
 
 }  // namespace w4a16

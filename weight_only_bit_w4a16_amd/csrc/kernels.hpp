@@ -6,7 +6,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 namespace w4a16 {
+
+// Enqueue `kernel` on `stream` and return the status of this launch itself
+// (hipLaunchKernel's own result: an earlier, unrelated error of the calling
+// thread is neither reported nor cleared).  The arguments are converted to
+// the kernel's parameter types and passed by address.
+template <typename... Params, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, unsigned lds,
+                                hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<std::decay_t<Params>...> vals(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
+  std::apply([&ptrs](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream);
+}
 
 // Fused epilogue on the fp32 accumulator c: C = act(alpha * c + bias[n]) +
 // beta * R[m, n] (bias bf16 (N) or null; R (M, N) in C's dtype, read only

@@ -27,8 +27,6 @@
 // fits) keeps the tile and the operand layouts but moves every operand by
 // global -> LDS copies, and decodes int4 with groups of 128 as the exact
 // code - zero (one MFMA chain, the scale once per k-block).
-#include <stdlib.h>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -170,6 +168,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
   f32x4_t acc[MS][2];
 #pragma unroll
   for (int s = 0; s < MS; ++s) acc[s][0] = acc[s][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool bad[2] = {false, false};  // MXFP4: this lane met a NaN scale of its row in slice h
   u32x4_t q[U][2];
   uint32_t sraw[U][2], zraw[U][2];
 
@@ -214,8 +213,9 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
       const int c = kb * 4 + g;
       const bool ok = c < KC;
       const int cc = ok ? c : 0;  // LDS reads stay inside the window
-      // both column slices decoded once, to bf16 MFMA operands
-      u32x4_t b[2][4];
+      // both column slices decoded once, to bf16 MFMA operands (int4 with
+      // groups of 32 / 64: the exact weights as hi + lo fragments)
+      u32x4_t b[2][4], bl[2][4];
       float sc[2];
       u32x4_t nz[2];
 #pragma unroll
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
           for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_natural(q[u][h][j]);
         } else if constexpr (is_int4(FMT)) {
           // groups shorter than a k-block: the chunk's group, applied in the
-          // decode, (code - zero) * scale rounded once to bf16
+          // decode, the exact weight (code - zero) * scale as hi + lo
           const int gi = r * groups + (cc >> GS);
           uint32_t sbits, z;
           if constexpr (S_LDS) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
           }
           const float s = bf16_bits_to_f32(sbits), zf = (float)z;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_weights(q[u][h][j], s, zf);
+          for (int j = 0; j < 4; ++j) int4x8_to_bf16_hilo(q[u][h][j], s, zf, b[h][j], bl[h][j]);
         } else if constexpr (FMT == kNvfp4) {
           const uint32_t s2 = S_LDS ? *reinterpret_cast<const uint16_t*>(sb + r * groups + 2 * cc) : sraw[u][h];
           const float s0 = e4m3_magnitude(s2 & 0xFFu), s1 = e4m3_magnitude(s2 >> 8);
@@ -258,7 +258,9 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
           b[h][2] = fp4x8_to_bf16_fscale(q[u][h][2], s1);
           b[h][3] = fp4x8_to_bf16_fscale(q[u][h][3], s1);
         } else {
-          const float es = e8m0_as_exponent_scale(S_LDS ? (uint32_t)sb[r * groups + cc] : sraw[u][h]);
+          const uint32_t E = S_LDS ? (uint32_t)sb[r * groups + cc] : sraw[u][h];
+          bad[h] = bad[h] || e8m0_is_nan(E);
+          const float es = e8m0_as_exponent_scale(E);
 #pragma unroll
           for (int j = 0; j < 4; ++j) b[h][j] = fp4x8_to_bf16_escale(q[u][h][j], es);
         }
@@ -282,6 +284,12 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[s][h][i] = __builtin_fmaf(sc[h], dp[i] + dn[i], acc[s][h][i]);
+          } else if constexpr (is_int4(FMT)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              acc[s][h] = mfma16x16x32(a[j], b[h][j], acc[s][h]);
+              acc[s][h] = mfma16x16x32(a[j], bl[h][j], acc[s][h]);
+            }
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[s][h] = mfma16x16x32(a[j], b[h][j], acc[s][h]);
@@ -311,6 +319,16 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     compute(kbase);
   }
 
+  if constexpr (FMT == kMxfp4) {
+    // a NaN scale makes its row's outputs NaN, whatever the other waves add
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((nan_rows16(bad[h]) >> nl) & 1u) {
+#pragma unroll
+        for (int s = 0; s < MS; ++s) acc[s][h] = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
+      }
+    }
+  }
   // ---- split-K sum over the waves through LDS ----
   constexpr int P = MS * 2;
 #pragma unroll
@@ -441,6 +459,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
   f32x4_t acc[MS][2];
 #pragma unroll
   for (int s = 0; s < MS; ++s) acc[s][0] = acc[s][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool bad[2] = {false, false};  // MXFP4: this lane met a NaN scale of its row in slice h
   const uint8_t* sb = lds + s_delta;
   const uint8_t* zb = lds + s_cap + z_delta;
   for (int i = 0; i < nk; ++i) {
@@ -456,7 +475,8 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
     // equal the zero point contributes exactly 0); this costs 10 more VALU
     // per 8 codes than the exact codes but half the MFMAs of the +-zero pair
     // (measured 64 x 8192 x 3072: 13.5 -> 12.1 us)
-    u32x4_t b[2][4];
+    // (int4 with groups of 32 / 64: the exact weights as hi + lo fragments)
+    u32x4_t b[2][4], bl[2][4];
     float sc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -473,7 +493,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
         const float sv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
         const float zf = (float)zb[gi];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_weights(q[j], sv, zf);
+        for (int j = 0; j < 4; ++j) int4x8_to_bf16_hilo(q[j], sv, zf, b[h][j], bl[h][j]);
       } else if constexpr (FMT == kNvfp4) {
         const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sb + r * groups + 2 * cc);
         const float s0 = e4m3_magnitude(s2 & 0xFFu), s1 = e4m3_magnitude(s2 >> 8);
@@ -482,7 +502,9 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
         b[h][2] = fp4x8_to_bf16_fscale(q[2], s1);
         b[h][3] = fp4x8_to_bf16_fscale(q[3], s1);
       } else {
-        const float es = e8m0_as_exponent_scale((uint32_t)sb[r * groups + cc]);
+        const uint32_t E = sb[r * groups + cc];
+        bad[h] = bad[h] || e8m0_is_nan(E);
+        const float es = e8m0_as_exponent_scale(E);
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[h][j] = fp4x8_to_bf16_escale(q[j], es);
       }
@@ -502,6 +524,12 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
           for (int j = 0; j < 4; ++j) dp = mfma16x16x32(a[j], b[h][j], dp);
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc[s][h][t] = __builtin_fmaf(sc[h], dp[t], acc[s][h][t]);
+        } else if constexpr (is_int4(FMT)) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[s][h] = mfma16x16x32(a[j], b[h][j], acc[s][h]);
+            acc[s][h] = mfma16x16x32(a[j], bl[h][j], acc[s][h]);
+          }
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[s][h] = mfma16x16x32(a[j], b[h][j], acc[s][h]);
@@ -515,6 +543,16 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
     }
   }
 
+  if constexpr (FMT == kMxfp4) {
+    // a NaN scale makes its row's outputs NaN, whatever the other waves add
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((nan_rows16(bad[h]) >> nl) & 1u) {
+#pragma unroll
+        for (int s = 0; s < MS; ++s) acc[s][h] = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
+      }
+    }
+  }
   // ---- split-K sum: the partial sums take the ring's place once every wave
   // is past its last k-block (its copies all waited for) ----
   constexpr int P = MS * 2;
@@ -574,10 +612,10 @@ hipError_t launch_v(const GemmArgs& a, const MidPlan& p) {
     const dim3 grid((unsigned)((a.N + kMidCols - 1) / kMidCols), (unsigned)((rows + 16 * MS - 1) / (16 * MS)));
     Epilogue epi = a.epi;
     if (epi.res) epi.res = static_cast<const uint8_t*>(epi.res) + m * a.N * es;
-    hipLaunchKernelGGL((mid_kernel<FMT, OUT_F32, U, MS, S_LDS>), grid, dim3(64 * p.waves), p.lds, a.stream,
-                       a.A + m * a.K, a.packed, a.scales, a.zeros, static_cast<uint8_t*>(a.C) + m * a.N * es,
-                       (int)rows, (int)a.N, (int)a.K, epi);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        launch_kernel(mid_kernel<FMT, OUT_F32, U, MS, S_LDS>, grid, dim3(64 * p.waves), p.lds, a.stream,
+                      a.A + m * a.K, a.packed, a.scales, a.zeros, static_cast<uint8_t*>(a.C) + m * a.N * es,
+                      (int)rows, (int)a.N, (int)a.K, epi);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -606,15 +644,13 @@ hipError_t launch_ring(const GemmArgs& a, unsigned lds) {
     const dim3 grid((unsigned)((a.N + kMidCols - 1) / kMidCols), (unsigned)((rows + 16 * MS - 1) / (16 * MS)));
     Epilogue epi = a.epi;
     if (epi.res) epi.res = static_cast<const uint8_t*>(epi.res) + m * a.N * es;
-    if (full)
-      hipLaunchKernelGGL((mid_ring_kernel<FMT, OUT_F32, MS, D, true>), grid, dim3(64 * kMidRingWaves), lds,
-                         a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
-                         static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi);
-    else
-      hipLaunchKernelGGL((mid_ring_kernel<FMT, OUT_F32, MS, D, false>), grid, dim3(64 * kMidRingWaves), lds,
-                         a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
-                         static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        full ? launch_kernel(mid_ring_kernel<FMT, OUT_F32, MS, D, true>, grid, dim3(64 * kMidRingWaves), lds,
+                             a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
+                             static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi)
+             : launch_kernel(mid_ring_kernel<FMT, OUT_F32, MS, D, false>, grid, dim3(64 * kMidRingWaves), lds,
+                             a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
+                             static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -622,14 +658,9 @@ hipError_t launch_ring(const GemmArgs& a, unsigned lds) {
 
 // The ring variant when its LDS fits beside the scale windows, 2 slots per
 // wave (measured: 3 slots or 2 / 3 waves are no faster); tiles of 48 or 64
-// rows that do not fit become 32-row tiles.  W4A16_MID_RING=0 never (tuning).
+// rows that do not fit become 32-row tiles.
 template <int FMT, bool OUT_F32>
 bool try_mid_ring(const GemmArgs& a, int MS, hipError_t& err) {
-  static const int env = [] {
-    const char* e = getenv("W4A16_MID_RING");
-    return e ? atoi(e) : 1;
-  }();
-  if (env == 0) return false;
   constexpr int SB = mid_sb<FMT>();
   const int64_t groups = (a.K + FormatTraits<FMT>::kGroup - 1) / FormatTraits<FMT>::kGroup;
   const int64_t win = mid_ring_window((uint32_t)(kMidCols * groups * SB)) +

@@ -24,8 +24,7 @@
 //     k-block (k-block = int4 group);
 //   * NVFP4: e2m1 -> fp32, times |e4m3 scale| (exact), -> bf16 (exact);
 //   * MXFP4: hardware e2m1 conversion scaled by 2^(E-127) (exact).
-#include <stdlib.h>
-
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -66,8 +65,9 @@ struct SkinnyGroup {
 //     even / odd k order of the shorter decode, and the codes convert in that
 //     order; otherwise in natural k order, like A.
 //   int4 g32 / g64: groups shorter than a k-block; the lane's chunk has one
-//     group, whose (code - zero) * scale is applied in the decode (one bf16
-//     rounding per weight, a weight equal to its zero point exactly 0).
+//     group, whose exact weights (code - zero) * scale are split into two
+//     bf16 fragments hi + lo (both exact) that feed two MFMAs, so the
+//     weights enter the sum unrounded.
 //   NVFP4: chunk = two blocks of 16, one e4m3 scale each (low byte first).
 //   MXFP4: chunk = one block of 32, one e8m0 scale.
 template <int FMT, bool EVEN_ODD>
@@ -92,7 +92,12 @@ __device__ __forceinline__ f32x4_t kblock_mac(const u32x4_t (&a)[4], const u32x4
     const float s = bf16_bits_to_f32(sraw);
     const float zf = (float)zraw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[j], int4x8_to_bf16_weights(q[j], s, zf), acc);
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t hi, lo;
+      int4x8_to_bf16_hilo(q[j], s, zf, hi, lo);
+      acc = mfma16x16x32(a[j], hi, acc);
+      acc = mfma16x16x32(a[j], lo, acc);
+    }
   } else if constexpr (FMT == kNvfp4) {
     const float s0 = e4m3_magnitude(sraw & 0xFFu);
     const float s1 = e4m3_magnitude(sraw >> 8);
@@ -305,6 +310,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   }
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  bool bad = false;  // MXFP4: this lane met a NaN (0xFF) scale of its row
   u32x4_t q[U];
   u32x4_t a[U][4];
   uint32_t sraw[U];
@@ -415,6 +421,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
           sraw[u] = sb[nl * groups + (ok ? c : 0)];
         }
       }
+      if constexpr (FMT == kMxfp4) bad = bad || e8m0_is_nan(sraw[u]);
       acc = kblock_mac<FMT, A_LDS>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc);
     }
   };
@@ -445,6 +452,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   for (kbase += waves * U; kbase < KB; kbase += waves * U) {
     issue(kbase);
     compute(kbase);
+  }
+
+  // a NaN scale makes its row's outputs NaN, whatever the other waves add
+  if constexpr (FMT == kMxfp4) {
+    if ((nan_rows16(bad) >> nl) & 1u) acc = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
   }
 
   // ---- split-K reduction across the waves, through LDS ----------------------
@@ -587,6 +599,7 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
   f32x4_t acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;  // MXFP4: this lane met a NaN (0xFF) scale of its row
   const uint8_t* sb = lds + s_delta;
   const uint8_t* zb = lds + s_cap + z_delta;
   for (int i0 = 0; i0 < nk; i0 += R) {
@@ -618,6 +631,7 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
     } else {
       sraw = sb[nl * groups + (ok ? c : 0)];
     }
+    if constexpr (FMT == kMxfp4) bad = bad || e8m0_is_nan(sraw);
     acc[r] = kblock_mac<FMT, false>(a, q, sraw, zraw, acc[r]);
     if (i + D < nk) {
       // the slot's reads have completed before its next copy is issued
@@ -627,6 +641,12 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
    }
   }
 
+  if constexpr (FMT == kMxfp4) {
+    if ((nan_rows16(bad) >> nl) & 1u) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) red[(wave + waves * r) * 64 + lane] = acc[r];
   lds_barrier();
@@ -762,6 +782,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
     const uint8_t* sb = lds + buf0 + (uint32_t)b * (s_cap + z_cap) + sdelta[b];
     const uint8_t* zb = lds + buf0 + (uint32_t)b * (s_cap + z_cap) + s_cap + zdelta[b];
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    bool bad = false;  // MXFP4: this lane met a NaN (0xFF) scale of its row
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = kw + u;
@@ -796,10 +817,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
         acc = mfma16x16x32(a[2], fp4x8_to_bf16_fscale(T.q[u][2], s1), acc);
         acc = mfma16x16x32(a[3], fp4x8_to_bf16_fscale(T.q[u][3], s1), acc);
       } else {
-        const float es = e8m0_as_exponent_scale(sb[nl * groups + c]);
+        const uint32_t E = sb[nl * groups + c];
+        bad = bad || e8m0_is_nan(E);
+        const float es = e8m0_as_exponent_scale(E);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[j], fp4x8_to_bf16_escale(T.q[u][j], es), acc);
       }
+    }
+    if constexpr (FMT == kMxfp4) {
+      if ((nan_rows16(bad) >> nl) & 1u) acc = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
     }
     return acc;
   };
@@ -887,12 +913,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, bool S_LDS>
 hipError_t launch_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim3 block, unsigned lds) {
   if (a.count > 1)
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, true>), grid, block,
-                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
-  else
-    hipLaunchKernelGGL((skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, false>), grid, block,
-                       lds, a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
-  return hipGetLastError();
+    return launch_kernel(skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, true>, grid, block, lds,
+                         a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
+  return launch_kernel(skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, false>, grid, block, lds,
+                       a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
 }
 
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA>
@@ -908,14 +932,8 @@ hipError_t launch_s(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim
 // rounds of 256 (one per CU) better -- e.g. N = 3072 gives 192 workgroups of
 // 16 rows but 256 of 12.  Lanes of the missing rows read zeros.  A workgroup
 // keeps >= 12 KB of weights (fewer rows would only add per-workgroup
-// overhead).  W4A16_SKINNY_ROWS=1..16 fixes the rows (tuning).
+// overhead).
 int skinny_rows(const GroupedArgs& a) {
-  static const int rows_env = [] {
-    const char* e = getenv("W4A16_SKINNY_ROWS");
-    const int r = e ? atoi(e) : 0;
-    return r >= 1 && r <= 16 ? r : 0;
-  }();
-  if (rows_env) return rows_env;
   int rows = 16;
   const int64_t r_min = (12288 + a.K / 2 - 1) / (a.K / 2);
   double best = -1.0;
@@ -955,12 +973,10 @@ template <int FMT, bool OUT_F32, int D, int R, bool FULL>
 hipError_t launch_ring_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, unsigned lds) {
   const dim3 block(64 * (kRingVirt / R));
   if (a.count > 1)
-    hipLaunchKernelGGL((skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, true>), grid, block, lds, a.stream,
+    return launch_kernel(skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, true>, grid, block, lds, a.stream,
+                         a.A, grp, (int)a.M, (int)a.K, a.epi);
+  return launch_kernel(skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, false>, grid, block, lds, a.stream,
                        a.A, grp, (int)a.M, (int)a.K, a.epi);
-  else
-    hipLaunchKernelGGL((skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, false>), grid, block, lds, a.stream,
-                       a.A, grp, (int)a.M, (int)a.K, a.epi);
-  return hipGetLastError();
 }
 template <int FMT, bool OUT_F32, int D, int R>
 hipError_t launch_ring_f(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, unsigned lds) {
@@ -975,23 +991,16 @@ hipError_t launch_ring_f(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid
 // round's copies overlap the current one's arithmetic (measured, e.g.
 // 8 x 32000 x 4096 int4: 36.6 us with the per-pass kernel, 26.6 with 8 x 3
 // slots, 23.7 with 4 x 2).  2 slots when the scale windows leave no room for
-// 3; false when even that does not fit the 160 KB of LDS.  Tuning:
-// W4A16_SKINNY_RING=0 never, =8 / =4 force 8 x 3 / 4 x 2 (8 x 2 when the
-// windows leave no room for 3 slots).
+// 3; false when even that does not fit the 160 KB of LDS.
 template <int FMT, bool OUT_F32>
 bool try_ring(const GroupedArgs& a, hipError_t& err) {
-  static const int env = [] {
-    const char* e = getenv("W4A16_SKINNY_RING");
-    return e ? atoi(e) : 1;
-  }();
-  if (env == 0) return false;
   constexpr int SB = is_int4(FMT) ? 2 : 1;
   const int64_t groups = (a.K + FormatTraits<FMT>::kGroup - 1) / FormatTraits<FMT>::kGroup;
   const int64_t win = ring_window_cap((uint32_t)(16 * groups * SB)) +
                       (has_zeros(FMT) ? ring_window_cap((uint32_t)(16 * groups)) : 0);
   dim3 grid;
   const SkinnyGroup grp = skinny_group(a, skinny_rows(a), grid);
-  const bool one_round = env == 8 || (env != 4 && (int64_t)grid.x * grid.y * grid.z <= 256);
+  const bool one_round = (int64_t)grid.x * grid.y * grid.z <= 256;
   auto lds_of = [&](int w, int d) { return win + (int64_t)w * d * kRingSlot + (int64_t)kRingVirt * 1024; };
   constexpr int64_t kLds = 160 * 1024;
   if (!one_round && lds_of(4, 2) <= kLds) {
@@ -1033,11 +1042,7 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
                      (!has_zeros(FMT) || (16 * groups + 6) / 4 <= kZStage * threads) && lds_s <= 32 * 1024;
   const bool full = a.K % 128 == 0;
   const dim3 block(64 * waves);
-  static const bool no_dma = [] {
-    const char* e = getenv("W4A16_SKINNY_NO_ADMA");
-    return e && atoi(e) == 1;
-  }();
-  const bool a_dma = !a_lds && !no_dma && waves * U * 4096 <= 128 * 1024;
+  const bool a_dma = !a_lds && waves * U * 4096 <= 128 * 1024;
   const unsigned ls = (unsigned)lds_s;
   if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true, false>(a, grp, grid, block, s_lds, lds_a, ls);
   if (a_lds) return launch_s<FMT, OUT_F32, U, true, false, false>(a, grp, grid, block, s_lds, lds_a, ls);
@@ -1047,34 +1052,22 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   return launch_s<FMT, OUT_F32, U, false, false, false>(a, grp, grid, block, s_lds, lds_a, ls);
 }
 
-// W4A16_SKINNY_U (1, 2 or 4) overrides the k-blocks per wave (tuning)
-int skinny_u_env() {
-  static const int u = [] {
-    const char* e = getenv("W4A16_SKINNY_U");
-    const int v = e ? atoi(e) : 0;
-    return v == 1 || v == 2 || v == 4 ? v : 0;
-  }();
-  return u;
-}
-
 // k-blocks of 128 per wave: 2 while K fits 16 waves that way, else 4.  The
 // split sets the summation order, so every kernel for few rows uses it.
-int skinny_split_u(int KB) {
-  if (skinny_u_env()) return skinny_u_env();
-  return (KB + 1) / 2 <= kMaxWaves ? 2 : 4;
-}
+int skinny_split_u(int KB) { return (KB + 1) / 2 <= kMaxWaves ? 2 : 4; }
 
-// compute units of the current device (cached per device)
+// compute units of the current device, cached per device (threads that race
+// on a first call store the same value; the slots are atomic)
 int device_cus() {
-  static int cus[64] = {};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // resident workgroups per compute unit of a kernel at a block size and
@@ -1098,9 +1091,8 @@ hipError_t launch_stream_k(const GroupedArgs& a, const SkinnyGroup& grp, int til
   const int resident = resident_per_cu(kern, 64 * waves, lds) * device_cus();
   const dim3 grid((unsigned)(tiles < resident ? tiles : resident));
   const dim3 block(64 * waves);
-  hipLaunchKernelGGL((skinny_stream_kernel<FMT, OUT_F32, U, NS>), grid, block, lds, a.stream, a.A, grp, (int)a.M,
-                     (int)a.K, tiles, a.epi);
-  return hipGetLastError();
+  return launch_kernel(skinny_stream_kernel<FMT, OUT_F32, U, NS>, grid, block, lds, a.stream, a.A, grp,
+                       (int)a.M, (int)a.K, tiles, a.epi);
 }
 
 // The streaming kernel when its conditions hold and the launch (one weight
@@ -1153,19 +1145,13 @@ bool try_stream(const GroupedArgs& a, int64_t min_tiles, hipError_t& err) {
 
 // Work split: each wave takes U consecutive k-blocks per pass (U 16-byte
 // weight loads in flight per lane), and the workgroup has enough waves
-// (at most 16) to cover K in one pass when it can.  W4A16_SKINNY_U (1, 2 or 4)
-// overrides U for tuning.
+// (at most 16) to cover K in one pass when it can.  The streaming variant
+// serves single matrices of 1024 tiles of 16 columns or more.
 template <int FMT, bool OUT_F32>
 hipError_t launch_fmt(const GroupedArgs& a) {
-  // W4A16_SKINNY_STREAM: 0 never, 1 whenever possible (tuning); default from
-  // 1024 tiles of 16 columns on
-  static const int stream_env = [] {
-    const char* e = getenv("W4A16_SKINNY_STREAM");
-    return e ? atoi(e) : -1;
-  }();
-  if (stream_env != 0) {
+  {
     hipError_t err = hipSuccess;
-    if (try_stream<FMT, OUT_F32>(a, stream_env == 1 ? 1 : 1024, err)) return err;
+    if (try_stream<FMT, OUT_F32>(a, 1024, err)) return err;
   }
   const int chunks = (int)(a.K >> 5);
   const int KB = (chunks + 3) >> 2;
@@ -1181,7 +1167,7 @@ hipError_t launch_fmt(const GroupedArgs& a) {
     hipError_t err = hipSuccess;
     if (try_ring<FMT, OUT_F32>(a, err)) return err;
   }
-  if (!skinny_u_env() && a_big && waves * U > 32) U = 32 / waves > 0 ? 32 / waves : 1;
+  if (a_big && waves * U > 32) U = 32 / waves > 0 ? 32 / waves : 1;
   if (U == 1) return launch_u<FMT, OUT_F32, 1>(a, waves);
   if (U == 2) return launch_u<FMT, OUT_F32, 2>(a, waves);
   return launch_u<FMT, OUT_F32, 4>(a, waves);

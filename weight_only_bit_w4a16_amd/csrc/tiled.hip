@@ -269,6 +269,14 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // MXFP4: this lane met a NaN (0xFF) scale of the weight row it supplies in tile t
+  bool bad[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) bad[t] = false;
+  // int4 whose group covers the k-tile (groups of 128 or 64): the MFMAs sum
+  // the exact code - zero over the k-tile and the group scale of each output
+  // row multiplies that partial sum in fp32 (exact weights, no bf16 rounding)
+  constexpr bool kFold = is_int4(FMT) && FMT != kInt4G32;
 
   issue_scales(0);
   issue(0, 0);
@@ -322,37 +330,96 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
       } else if constexpr (FMT == kNvfp4) {
         bs[t] = e4m3_magnitude((sw[t] >> (8 * (g & 1))) & 0xFFu);
       } else {
+        bad[t] = bad[t] || e8m0_is_nan(sw[t]);
         bs[t] = e8m0_as_exponent_scale(sw[t]);
       }
     }
+    // kFold: the group scales of the lane's output rows 4g .. 4g+3 of tile t
+    // (the MFMA result rows; the lane supplies weight row l16)
+    auto row_scales = [&](int t) {
+      const uint8_t* Sb = smem + L::kSOff + ((j / ST::kKTiles) & 1) * L::kSBytes;
+      f32x4_t so;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wn * TN * 16 + t * 16 + 4 * g + r;
+        so[r] = bf16_bits_to_f32(
+            *reinterpret_cast<const uint32_t*>(Sb + (row * E + (se ^ scale_swz<E>(row))) * 4));
+      }
+      return so;
+    };
     auto decode = [&](int s, int t) -> u32x4_t {
-      if constexpr (is_int4(FMT)) {
-        return int4x8_to_bf16_weights(bq[t][s], bs[t], bz[t]);
-      } else if constexpr (FMT == kNvfp4) {
+      if constexpr (FMT == kNvfp4) {
         return fp4x8_to_bf16_fscale(bq[t][s], bs[t]);
       } else {
         return fp4x8_to_bf16_escale(bq[t][s], bs[t]);
       }
     };
-    // step 0: B column tile t is decoded right before its MFMAs (one decoded
-    // fragment live at a time); the step-1 A reads are issued first
+    // the step-1 A reads are issued before the step-0 MFMAs
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       af1[i] = *reinterpret_cast<const u32x4_t*>(As + i * 16 * 128 + a_rd1);
+    if constexpr (kFold) {
+      // per (i, t): two MFMAs over the k-tile's exact code - zero from zero,
+      // then the row scales fold the partial sum into the accumulator
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const u32x4_t bf = decode(0, t);
+      for (int t = 0; t < TN; ++t) {
+        const f32x4_t so = row_scales(t);
+        const u32x4_t b0 = int4x8_minus_zero(bq[t][0], bz[t]);
+        const u32x4_t b1 = int4x8_minus_zero(bq[t][1], bz[t]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(bf, af0[i], acc[i][t]);
-    }
+        for (int i = 0; i < TM; ++i) {
+          f32x4_t p = mfma16x16x32(b0, af0[i], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          p = mfma16x16x32(b1, af1[i], p);
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const u32x4_t bf = decode(1, t);
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = __builtin_fmaf(so[r], p[r], acc[i][t][r]);
+        }
+      }
+    } else if constexpr (is_int4(FMT)) {
+      // groups of 32 (two per k-tile): the exact weights as hi + lo fragments
 #pragma unroll
-      for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(bf, af1[i], acc[i][t]);
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+          u32x4_t hi, lo;
+          int4x8_to_bf16_hilo(bq[t][st], bs[t], bz[t], hi, lo);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            acc[i][t] = mfma16x16x32(hi, st ? af1[i] : af0[i], acc[i][t]);
+            acc[i][t] = mfma16x16x32(lo, st ? af1[i] : af0[i], acc[i][t]);
+          }
+        }
+    } else {
+      // step 0: B column tile t is decoded right before its MFMAs (one
+      // decoded fragment live at a time)
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const u32x4_t bf = decode(0, t);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(bf, af0[i], acc[i][t]);
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const u32x4_t bf = decode(1, t);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i][t] = mfma16x16x32(bf, af1[i], acc[i][t]);
+      }
     }
     cur = cur == kStages - 1 ? 0 : cur + 1;
     nxt = nxt == kStages - 1 ? 0 : nxt + 1;
+  }
+
+  // MXFP4: a NaN scale makes every output of its weight row NaN
+  if constexpr (FMT == kMxfp4) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const uint32_t rows16 = nan_rows16(bad[t]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if ((rows16 >> (4 * g + r)) & 1u) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) acc[i][t][r] = __uint_as_float(kQuietNaN);
+        }
+    }
   }
 
 // ---- epilogue: lane holds output row l16 of each 16x16 tile, columns
@@ -514,10 +581,9 @@ using CfgSmall = TileCfg<2, 2, 4, 4>;
 template <int FMT, bool OUT_F32, class CFG>
 hipError_t launch_cfg(const GemmArgs& a) {
   const int64_t tiles = ((a.N + CFG::BN - 1) / CFG::BN) * ((a.M + CFG::BM - 1) / CFG::BM);
-  hipLaunchKernelGGL((tiled_kernel<FMT, OUT_F32, CFG>), dim3((unsigned)tiles), dim3(CFG::kThreads),
-                     0, a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N,
-                     (int)a.K, a.epi);
-  return hipGetLastError();
+  return launch_kernel(tiled_kernel<FMT, OUT_F32, CFG>, dim3((unsigned)tiles), dim3(CFG::kThreads), 0,
+                       a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K,
+                       a.epi);
 }
 
 template <int FMT, bool OUT_F32>
