@@ -168,7 +168,6 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
   f32x4_t acc[MS][2];
 #pragma unroll
   for (int s = 0; s < MS; ++s) acc[s][0] = acc[s][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bool bad[2] = {false, false};  // MXFP4: this lane met a NaN scale of its row in slice h
   u32x4_t q[U][2];
   uint32_t sraw[U][2], zraw[U][2];
 
@@ -258,9 +257,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
           b[h][2] = fp4x8_to_bf16_fscale(q[u][h][2], s1);
           b[h][3] = fp4x8_to_bf16_fscale(q[u][h][3], s1);
         } else {
-          const uint32_t E = S_LDS ? (uint32_t)sb[r * groups + cc] : sraw[u][h];
-          bad[h] = bad[h] || e8m0_is_nan(E);
-          const float es = e8m0_as_exponent_scale(E);
+          const float es = e8m0_as_exponent_scale(S_LDS ? (uint32_t)sb[r * groups + cc] : sraw[u][h]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) b[h][j] = fp4x8_to_bf16_escale(q[u][h][j], es);
         }
@@ -319,16 +316,6 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     compute(kbase);
   }
 
-  if constexpr (FMT == kMxfp4) {
-    // a NaN scale makes its row's outputs NaN, whatever the other waves add
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if ((nan_rows16(bad[h]) >> nl) & 1u) {
-#pragma unroll
-        for (int s = 0; s < MS; ++s) acc[s][h] = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
-      }
-    }
-  }
   // ---- split-K sum over the waves through LDS ----
   constexpr int P = MS * 2;
 #pragma unroll
@@ -459,7 +446,6 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
   f32x4_t acc[MS][2];
 #pragma unroll
   for (int s = 0; s < MS; ++s) acc[s][0] = acc[s][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bool bad[2] = {false, false};  // MXFP4: this lane met a NaN scale of its row in slice h
   const uint8_t* sb = lds + s_delta;
   const uint8_t* zb = lds + s_cap + z_delta;
   for (int i = 0; i < nk; ++i) {
@@ -502,9 +488,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
         b[h][2] = fp4x8_to_bf16_fscale(q[2], s1);
         b[h][3] = fp4x8_to_bf16_fscale(q[3], s1);
       } else {
-        const uint32_t E = sb[r * groups + cc];
-        bad[h] = bad[h] || e8m0_is_nan(E);
-        const float es = e8m0_as_exponent_scale(E);
+        const float es = e8m0_as_exponent_scale((uint32_t)sb[r * groups + cc]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[h][j] = fp4x8_to_bf16_escale(q[j], es);
       }
@@ -543,16 +527,6 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
     }
   }
 
-  if constexpr (FMT == kMxfp4) {
-    // a NaN scale makes its row's outputs NaN, whatever the other waves add
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if ((nan_rows16(bad[h]) >> nl) & 1u) {
-#pragma unroll
-        for (int s = 0; s < MS; ++s) acc[s][h] = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
-      }
-    }
-  }
   // ---- split-K sum: the partial sums take the ring's place once every wave
   // is past its last k-block (its copies all waited for) ----
   constexpr int P = MS * 2;

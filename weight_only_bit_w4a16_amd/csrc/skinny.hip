@@ -310,7 +310,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   }
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  bool bad = false;  // MXFP4: this lane met a NaN (0xFF) scale of its row
   u32x4_t q[U];
   u32x4_t a[U][4];
   uint32_t sraw[U];
@@ -421,7 +420,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
           sraw[u] = sb[nl * groups + (ok ? c : 0)];
         }
       }
-      if constexpr (FMT == kMxfp4) bad = bad || e8m0_is_nan(sraw[u]);
       acc = kblock_mac<FMT, A_LDS>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc);
     }
   };
@@ -452,11 +450,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* 
   for (kbase += waves * U; kbase < KB; kbase += waves * U) {
     issue(kbase);
     compute(kbase);
-  }
-
-  // a NaN scale makes its row's outputs NaN, whatever the other waves add
-  if constexpr (FMT == kMxfp4) {
-    if ((nan_rows16(bad) >> nl) & 1u) acc = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
   }
 
   // ---- split-K reduction across the waves, through LDS ----------------------
@@ -599,7 +592,6 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
   f32x4_t acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bool bad = false;  // MXFP4: this lane met a NaN (0xFF) scale of its row
   const uint8_t* sb = lds + s_delta;
   const uint8_t* zb = lds + s_cap + z_delta;
   for (int i0 = 0; i0 < nk; i0 += R) {
@@ -631,7 +623,6 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
     } else {
       sraw = sb[nl * groups + (ok ? c : 0)];
     }
-    if constexpr (FMT == kMxfp4) bad = bad || e8m0_is_nan(sraw);
     acc[r] = kblock_mac<FMT, false>(a, q, sraw, zraw, acc[r]);
     if (i + D < nk) {
       // the slot's reads have completed before its next copy is issued
@@ -641,12 +632,6 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
    }
   }
 
-  if constexpr (FMT == kMxfp4) {
-    if ((nan_rows16(bad) >> nl) & 1u) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
-    }
-  }
 #pragma unroll
   for (int r = 0; r < R; ++r) red[(wave + waves * r) * 64 + lane] = acc[r];
   lds_barrier();
@@ -782,7 +767,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
     const uint8_t* sb = lds + buf0 + (uint32_t)b * (s_cap + z_cap) + sdelta[b];
     const uint8_t* zb = lds + buf0 + (uint32_t)b * (s_cap + z_cap) + s_cap + zdelta[b];
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    bool bad = false;  // MXFP4: this lane met a NaN (0xFF) scale of its row
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = kw + u;
@@ -817,15 +801,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
         acc = mfma16x16x32(a[2], fp4x8_to_bf16_fscale(T.q[u][2], s1), acc);
         acc = mfma16x16x32(a[3], fp4x8_to_bf16_fscale(T.q[u][3], s1), acc);
       } else {
-        const uint32_t E = sb[nl * groups + c];
-        bad = bad || e8m0_is_nan(E);
-        const float es = e8m0_as_exponent_scale(E);
+        const float es = e8m0_as_exponent_scale(sb[nl * groups + c]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = mfma16x16x32(a[j], fp4x8_to_bf16_escale(T.q[u][j], es), acc);
       }
-    }
-    if constexpr (FMT == kMxfp4) {
-      if ((nan_rows16(bad) >> nl) & 1u) acc = f32x4_t{0.f, 0.f, 0.f, 0.f} + __uint_as_float(kQuietNaN);
     }
     return acc;
   };

@@ -269,10 +269,6 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // MXFP4: this lane met a NaN (0xFF) scale of the weight row it supplies in tile t
-  bool bad[TN];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) bad[t] = false;
   // int4 whose group covers the k-tile (groups of 128 or 64): the MFMAs sum
   // the exact code - zero over the k-tile and the group scale of each output
   // row multiplies that partial sum in fp32 (exact weights, no bf16 rounding)
@@ -330,7 +326,6 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
       } else if constexpr (FMT == kNvfp4) {
         bs[t] = e4m3_magnitude((sw[t] >> (8 * (g & 1))) & 0xFFu);
       } else {
-        bad[t] = bad[t] || e8m0_is_nan(sw[t]);
         bs[t] = e8m0_as_exponent_scale(sw[t]);
       }
     }
@@ -406,20 +401,6 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     }
     cur = cur == kStages - 1 ? 0 : cur + 1;
     nxt = nxt == kStages - 1 ? 0 : nxt + 1;
-  }
-
-  // MXFP4: a NaN scale makes every output of its weight row NaN
-  if constexpr (FMT == kMxfp4) {
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const uint32_t rows16 = nan_rows16(bad[t]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if ((rows16 >> (4 * g + r)) & 1u) {
-#pragma unroll
-          for (int i = 0; i < TM; ++i) acc[i][t][r] = __uint_as_float(kQuietNaN);
-        }
-    }
   }
 
 // ---- epilogue: lane holds output row l16 of each 16x16 tile, columns
