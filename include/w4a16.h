@@ -183,6 +183,39 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
                        const void* const* scales, const void* const* zeros, void* const* C,
                        const int64_t* N, int64_t M, int64_t K, void* stream);
 
+/* ---- batched independent GEMMs -----------------------------------------------
+ * Item i computes C_i = A_i . dequant(packed_i, scales_i, zeros_i)^T with its
+ * own activations A_i (M, K_i), weights (N_i rows) and output C_i (M, N_i);
+ * the items share only the format, the output type and M.  In the decode
+ * regime (M <= 16) the items of one (K, N) run in ONE launch (up to 32 items
+ * per launch), so the weight matrices of a decoder step (page
+ * "megakernel_int4_weight_decode.py": seven int4 projections per layer plus
+ * the LM head, and its performance section's per-kernel overhead, eager vs
+ * graph) take a handful of launches instead of one each.  Larger M: one
+ * launch per item.  Each item's C equals, bit for bit, what w4a16_gemm gives
+ * for that item alone.
+ * The items must be independent: no item's C may overlap another item's C or
+ * any item's input, since items run concurrently and in no fixed order.
+ * `items` is a HOST array of `count` entries (device pointers and sizes),
+ * read during the call only; every entry follows w4a16_gemm's layout,
+ * alignment and zeros rules; entries with N == 0 are skipped and their
+ * pointers not checked.  `format`: a weight format, optionally OR-ed with
+ * W4A16_OUT_F32 (no W4A16_PATH_* flag).  count == 0 or M == 0 enqueues
+ * nothing.  Errors: as w4a16_gemm, every item is checked before anything is
+ * enqueued (W4A16_ERR_SHAPE also for count < 0); a launch failure
+ * (W4A16_ERR_HIP) may leave the call's earlier launches enqueued. */
+typedef struct w4a16_batch_item {
+  const void* A;      /* bf16 (M, K) device array, 16-byte aligned            */
+  const void* packed; /* uint8 (N, K/2) device array, 16-byte aligned         */
+  const void* scales; /* per the format, as for w4a16_gemm                    */
+  const void* zeros;  /* uint8 zeros for the int4 formats with zeros, else NULL */
+  void* C;            /* (M, N) device array, bf16 or fp32                    */
+  int64_t N;          /* output columns (weight rows), 0 <= N < 2^31          */
+  int64_t K;          /* inputs, 0 < K <= 2^22, K % 32 == 0                   */
+} w4a16_batch_item;
+int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item* items,
+                       void* stream);
+
 /* W = dequant(packed, scales, zeros) as bf16 (N, K): each weight's exact value
  * rounded once to nearest even (bit-exact; fp4 weights are exact in bf16 at
  * normal scale ranges).  `format` takes only the format bits.  A checking

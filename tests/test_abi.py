@@ -29,8 +29,8 @@ def _header_defines():
 def test_library_exports_every_declared_function():
     lib = w4.load_library()
     names = _header_functions()
-    assert set(names) == {"w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped", "w4a16_dequant",
-                          "w4a16_gemm_path", "w4a16_strerror", "w4a16_version"}
+    assert set(names) == {"w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped", "w4a16_gemm_batched",
+                          "w4a16_dequant", "w4a16_gemm_path", "w4a16_strerror", "w4a16_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -60,7 +60,7 @@ def test_epilogue_struct_layout():
 
 
 def test_version_and_strerror():
-    assert w4.version() == 104
+    assert w4.version() == 105
     for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP,
                  w4.ERR_EPILOGUE):
         assert w4.strerror(code) != "unknown status"
@@ -269,3 +269,54 @@ def test_grouped_zero_extents_check_no_pointer():
     assert _grouped(w4.MXFP4, N=(0, 0, 0), A=None, packed=False, scales=False, C=False) == w4.OK
     # a skipped member's pointers are not checked, the others still are
     assert _grouped(w4.NVFP4, N=(64, 0, 32), bad=("P", 1, None), C=False) == w4.ERR_NULL
+
+
+# ---- w4a16_gemm_batched validation (no call below reaches a launch) ---------
+
+def test_batch_item_struct_layout():
+    # struct w4a16_batch_item: five pointers, two int64
+    assert ctypes.sizeof(w4.BatchItem) == 56
+    assert w4.BatchItem.N.offset == 40 and w4.BatchItem.K.offset == 48
+
+
+def _batched(fmt, n=3, M=1, items=None, bad=None, count=None):
+    arr = (w4.BatchItem * max(n, 1))()
+    for i in range(n):
+        z = 0x100000 * (40 + i) if (fmt & 0xFF) in w4.ZERO_FORMATS else None
+        arr[i] = w4.BatchItem(0x100000 * (8 + i), 0x100000 * (16 + i), 0x100000 * (24 + i), z,
+                              0x100000 * (32 + i), 64 + 32 * i, 128)
+    if bad:
+        i, field, val = bad
+        setattr(arr[i], field, val)
+    return w4.load_library().w4a16_gemm_batched(fmt, M, n if count is None else count,
+                                                None if items == "null" else arr, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(fmt=6), w4.ERR_FORMAT),
+    (dict(fmt=w4.MXFP4 | w4.PATH_SKINNY), w4.ERR_FORMAT),      # no path flags
+    (dict(fmt=w4.MXFP4, count=-1), w4.ERR_SHAPE),
+    (dict(fmt=w4.MXFP4, M=-1), w4.ERR_SHAPE),
+    (dict(fmt=w4.MXFP4, items="null"), w4.ERR_NULL),
+    (dict(fmt=w4.NVFP4, bad=(1, "K", 48)), w4.ERR_SHAPE),      # K % 32
+    (dict(fmt=w4.NVFP4, bad=(2, "K", 0)), w4.ERR_SHAPE),
+    (dict(fmt=w4.NVFP4, bad=(0, "N", -1)), w4.ERR_SHAPE),
+    (dict(fmt=w4.NVFP4, bad=(1, "A", None)), w4.ERR_NULL),
+    (dict(fmt=w4.NVFP4, bad=(2, "C", None)), w4.ERR_NULL),
+    (dict(fmt=w4.NVFP4, bad=(0, "zeros", 0x100000)), w4.ERR_NULL),   # fp4 takes no zeros
+    (dict(fmt=w4.INT4_G128, bad=(1, "zeros", None)), w4.ERR_NULL),   # int4 needs zeros
+    (dict(fmt=w4.MXFP4, bad=(1, "A", 0x100008)), w4.ERR_ALIGN),
+    (dict(fmt=w4.MXFP4, bad=(2, "packed", 0x100008)), w4.ERR_ALIGN),
+    (dict(fmt=w4.NVFP4, bad=(0, "scales", 0x100001)), w4.ERR_ALIGN),
+    (dict(fmt=w4.NVFP4 | w4.OUT_F32, bad=(2, "C", 0x100002)), w4.ERR_ALIGN),
+])
+def test_batched_validation(kw, expect):
+    assert _batched(**kw) == expect
+
+
+def test_batched_empty_calls_check_no_pointer():
+    assert _batched(w4.MXFP4, count=0, items="null") == w4.OK
+    assert _batched(w4.MXFP4, M=0, bad=(1, "A", None)) == w4.OK          # M = 0: nothing read
+    # an item with N = 0 is skipped unchecked; the others still are
+    arr_ok = _batched(w4.NVFP4, n=1, bad=(0, "N", 0))
+    assert arr_ok == w4.OK

@@ -46,6 +46,13 @@ class Epilogue(ctypes.Structure):
                 ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
                 ("activation", ctypes.c_int), ("reserved", ctypes.c_int)]
 
+class BatchItem(ctypes.Structure):
+    """struct w4a16_batch_item of include/w4a16.h."""
+    _fields_ = [("A", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 _lib = None
@@ -75,6 +82,8 @@ def load_library():
     PP = ctypes.POINTER(ctypes.c_void_p)
     lib.w4a16_gemm_grouped.argtypes = [I, P, I, PP, PP, PP, PP, ctypes.POINTER(I64), I64, I64, P]
     lib.w4a16_gemm_grouped.restype = I
+    lib.w4a16_gemm_batched.argtypes = [I, I64, I, ctypes.POINTER(BatchItem), P]
+    lib.w4a16_gemm_batched.restype = I
     lib.w4a16_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
     lib.w4a16_dequant.restype = I
     lib.w4a16_gemm_path.argtypes = [I, I64, I64, I64]
@@ -257,6 +266,67 @@ class PreparedGroupedGemm:
         rc = self._fn(*self._args, _stream_handle(stream))
         if rc != OK:
             raise W4A16Error(rc, "w4a16_gemm_grouped")
+
+
+def _batched_args(fmt, items, outs, out_dtype):
+    """Check a batched call's tensors; return (flags, outs, item array, M)."""
+    items = list(items)
+    if not items:
+        return (OUT_F32 if out_dtype == torch.float32 else OUT_BF16), [], (BatchItem * 1)(), 0
+    if outs is None:
+        outs = [torch.empty((A.shape[0], packed.shape[0]), dtype=out_dtype, device=A.device)
+                for A, packed, _, _ in items]
+    if len(outs) != len(items):
+        raise ValueError("one output per item")
+    dt = outs[0].dtype
+    if dt not in (torch.bfloat16, torch.float32) or any(o.dtype != dt for o in outs):
+        raise ValueError("outputs must all be bf16 or all fp32")
+    M = items[0][0].shape[0]
+    arr = (BatchItem * len(items))()
+    for i, ((A, packed, scales, zeros), out) in enumerate(zip(items, outs)):
+        if not A.is_cuda:
+            raise ValueError(f"A[{i}] must be a GPU tensor")
+        device = A.device
+        if A.dim() != 2 or A.shape[0] != M:
+            raise ValueError(f"A[{i}] must have the batch's M = {M} rows")
+        K = A.shape[1]
+        N = packed.shape[0]
+        _check(A, f"A[{i}]", (M, K), 2, device)
+        _check_weights(fmt, packed, scales, zeros, N, K, device)
+        _check(out, f"out[{i}]", (M, N), out.element_size(), device)
+        arr[i] = BatchItem(A.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                           None if zeros is None else zeros.data_ptr(), out.data_ptr(), N, K)
+    flags = OUT_F32 if dt == torch.float32 else OUT_BF16
+    return flags, outs, arr, M
+
+
+def gemm_batched(fmt: int, items, outs=None, out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """C_i = A_i . dequant(packed_i, scales_i, zeros_i)^T for every item
+    (A_i, packed_i, scales_i, zeros_i) -- independent GEMMs with their own
+    activations (all with M rows) and outputs; for M <= 16 the items of one
+    (K, N) share a launch.  Returns the list of outputs (asynchronous)."""
+    flags, outs, arr, M = _batched_args(fmt, items, outs, out_dtype)
+    rc = load_library().w4a16_gemm_batched(int(fmt) | flags, M, len(outs), arr, _stream_handle(stream))
+    if rc != OK:
+        raise W4A16Error(rc, "w4a16_gemm_batched")
+    return outs
+
+
+class PreparedBatchedGemm:
+    """One w4a16_gemm_batched call marshalled once (see :class:`PreparedGemm`)."""
+
+    def __init__(self, fmt: int, items, outs):
+        items = list(items)
+        flags, outs, arr, M = _batched_args(fmt, items, outs, torch.bfloat16)
+        self.tensors = (items, outs)
+        self.kernel = gemm_path(fmt, M, int(arr[0].N), int(arr[0].K)) if items else None
+        self._fn = load_library().w4a16_gemm_batched
+        self._args = (int(fmt) | flags, M, len(outs), arr)
+
+    def __call__(self, stream=None):
+        rc = self._fn(*self._args, _stream_handle(stream))
+        if rc != OK:
+            raise W4A16Error(rc, "w4a16_gemm_batched")
 
 
 def dequant(fmt: int, packed: torch.Tensor, scales: torch.Tensor,

@@ -3,6 +3,9 @@
 // enqueues nothing (and never touches the HIP runtime).
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "w4a16.h"
 #include "kernels.hpp"
 
@@ -72,7 +75,7 @@ hipError_t launch_path(int path, const w4a16::GemmArgs& a) {
 
 extern "C" {
 
-int w4a16_version(void) { return 104; }
+int w4a16_version(void) { return 105; }
 
 const char* w4a16_strerror(int status) {
   switch (status) {
@@ -186,9 +189,9 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     w4a16::GroupedArgs g = {};
     g.fmt = fmt;
     g.out_f32 = out_f32;
-    g.A = static_cast<const uint16_t*>(A);
     for (int i = 0; i < count; ++i) {
       if (N[i] == 0) continue;
+      g.A[g.count] = static_cast<const uint16_t*>(A);
       g.packed[g.count] = static_cast<const uint8_t*>(packed[i]);
       g.scales[g.count] = scales[i];
       g.zeros[g.count] = has_zeros(fmt) ? static_cast<const uint8_t*>(zeros[i]) : nullptr;
@@ -218,6 +221,94 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     a.K = K;
     a.stream = static_cast<hipStream_t>(stream);
     if (launch_path(path, a) != hipSuccess) return W4A16_ERR_HIP;
+  }
+  return W4A16_OK;
+}
+
+int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item* items, void* stream) {
+  // format and flags (output dtype only: the kernel is chosen per launch)
+  const int fmt = format & W4A16_FORMAT_MASK;
+  if (fmt > W4A16_INT4_SYM || (format & ~(W4A16_FORMAT_MASK | W4A16_OUT_F32))) return W4A16_ERR_FORMAT;
+  if (count < 0 || M < 0) return W4A16_ERR_SHAPE;
+  if (count > 0 && !items) return W4A16_ERR_NULL;
+  const bool out_f32 = (format & W4A16_OUT_F32) != 0;
+  // every item is checked before anything is enqueued
+  int rc = W4A16_OK;
+  for (int i = 0; i < count; ++i)
+    if ((rc = check_format_shape(fmt, M, items[i].N, items[i].K, false)) != W4A16_OK) return rc;
+  if (M == 0) return W4A16_OK;
+  for (int i = 0; i < count; ++i) {
+    const w4a16_batch_item& it = items[i];
+    if (it.N == 0) continue;  // nothing is read or written
+    if (!it.A || !it.packed || !it.scales || !it.C) return W4A16_ERR_NULL;
+    if (has_zeros(fmt) ? !it.zeros : it.zeros != nullptr) return W4A16_ERR_NULL;
+    if (!aligned(it.A, 16) || !aligned(it.packed, 16)) return W4A16_ERR_ALIGN;
+    if (fmt != W4A16_MXFP4 && !aligned(it.scales, 2)) return W4A16_ERR_ALIGN;
+    if (!aligned(it.C, out_f32 ? 4 : 2)) return W4A16_ERR_ALIGN;
+  }
+  auto single = [&](const w4a16_batch_item& it) {
+    w4a16::GemmArgs a;
+    a.epi = w4a16::Epilogue{};
+    a.fmt = fmt;
+    a.out_f32 = out_f32;
+    a.A = static_cast<const uint16_t*>(it.A);
+    a.packed = static_cast<const uint8_t*>(it.packed);
+    a.scales = it.scales;
+    a.zeros = static_cast<const uint8_t*>(it.zeros);
+    a.C = it.C;
+    a.M = M;
+    a.N = it.N;
+    a.K = it.K;
+    a.stream = static_cast<hipStream_t>(stream);
+    return launch_path(choose_path(fmt, M, it.N), a);
+  };
+  if (choose_path(fmt, M, 1) != W4A16_PATH_SKINNY) {
+    // larger M: every item is its own mid or tiled launch
+    for (int i = 0; i < count; ++i)
+      if (items[i].N > 0 && single(items[i]) != hipSuccess) return W4A16_ERR_HIP;
+    return W4A16_OK;
+  }
+  // M <= 16: the items of one (K, N) share a skinny launch, up to kMaxGroup
+  // members each (workgroup z = member); an item alone on its shape takes
+  // the single-GEMM launch (which may be the streaming variant).  The skinny
+  // kernel's split of K depends on the format, M and K only, so every item's
+  // output equals w4a16_gemm's for it, bit for bit.
+  std::vector<int> order;
+  order.reserve((size_t)count);
+  for (int i = 0; i < count; ++i)
+    if (items[i].N > 0) order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    return items[x].K != items[y].K ? items[x].K < items[y].K : items[x].N < items[y].N;
+  });
+  for (size_t b = 0; b < order.size();) {
+    size_t e = b + 1;
+    while (e < order.size() && items[order[e]].K == items[order[b]].K && items[order[e]].N == items[order[b]].N)
+      ++e;
+    for (size_t c = b; c < e; c += w4a16::kMaxGroup) {
+      const size_t n = std::min(e - c, (size_t)w4a16::kMaxGroup);
+      if (n == 1) {
+        if (single(items[order[c]]) != hipSuccess) return W4A16_ERR_HIP;
+        continue;
+      }
+      w4a16::GroupedArgs g = {};
+      g.fmt = fmt;
+      g.out_f32 = out_f32;
+      for (size_t j = 0; j < n; ++j) {
+        const w4a16_batch_item& it = items[order[c + j]];
+        g.A[g.count] = static_cast<const uint16_t*>(it.A);
+        g.packed[g.count] = static_cast<const uint8_t*>(it.packed);
+        g.scales[g.count] = it.scales;
+        g.zeros[g.count] = has_zeros(fmt) ? static_cast<const uint8_t*>(it.zeros) : nullptr;
+        g.C[g.count] = it.C;
+        g.N[g.count] = it.N;
+        ++g.count;
+      }
+      g.M = M;
+      g.K = items[order[c]].K;
+      g.stream = static_cast<hipStream_t>(stream);
+      if (w4a16::launch_skinny_grouped(g) != hipSuccess) return W4A16_ERR_HIP;
+    }
+    b = e;
   }
   return W4A16_OK;
 }

@@ -53,14 +53,15 @@ struct GemmArgs {
   Epilogue epi;
 };
 
-// Several weight matrices sharing one A (and K): member i has its own
-// packed / scales / zeros / C and N[i] output columns.
-constexpr int kMaxGroup = 8;
+// Several weight matrices of one K in one launch: member i has its own
+// activations A[i] (the same pointer for every member of a w4a16_gemm_grouped
+// call), packed / scales / zeros / C and N[i] output columns.
+constexpr int kMaxGroup = 32;
 struct GroupedArgs {
   int fmt;
   bool out_f32;
-  const uint16_t* A;
   int count;  // 1 .. kMaxGroup, every member with N[i] > 0
+  const uint16_t* A[kMaxGroup];
   const uint8_t* packed[kMaxGroup];
   const void* scales[kMaxGroup];
   const uint8_t* zeros[kMaxGroup];

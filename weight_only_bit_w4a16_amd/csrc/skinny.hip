@@ -41,20 +41,26 @@ constexpr int kAStage = 2;  // 16-byte chunks of A per thread when A is staged i
 constexpr int kSStage = 3;  // scale dwords per thread when the scales are staged in LDS
 constexpr int kZStage = 2;  // zero dwords per thread (int4)
 
-// The weight matrices of one launch: a single GEMM, or several sharing A and
-// K (member i: packed / scales / zeros / C, N[i] columns).  Workgroup
-// (x, y, z) runs columns x * rows .. of member z (none if past its N).
+// The GEMMs of one launch: a single one, or several of one K (member i: its
+// A, packed / scales / zeros / C, N[i] columns).  Workgroup (x, y, z) runs
+// columns x * rows .. of member z (none if past its N).  A single GEMM's
+// launch carries one member (kernel arguments stay small), a grouped or
+// batched one up to kMaxGroup.
 struct SkinnyMember {
+  const uint16_t* A;
   const uint8_t* packed;
   const void* scales;
   const uint8_t* zeros;
   void* C;
   int N;
 };
+template <int CAP>
 struct SkinnyGroup {
-  SkinnyMember m[kMaxGroup];  // one member's fields are contiguous
+  SkinnyMember m[CAP];  // one member's fields are contiguous
   int rows;  // weight rows (output columns) per workgroup, 1 .. 16
 };
+template <bool GROUPED>
+using SkinnyGroupOf = SkinnyGroup<GROUPED ? kMaxGroup : 1>;
 
 // One k-block of 128 codes into acc: a[j] is the lane's A fragment of MFMA
 // step j (32 codes), q[j] its 8 codes of that step, sraw / zraw the raw scale
@@ -192,12 +198,12 @@ __device__ __forceinline__ void skinny_store(const f32x4_t* red, int waves, int 
 // contiguous 256-byte row pieces) instead of per-lane A loads.
 // GROUPED: more than one member, blockIdx.z (a single GEMM reads member 0).
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED>
-__global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(const uint16_t* __restrict__ A,
-                                                                SkinnyGroup grp, int M, int K,
+__global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GROUPED> grp, int M, int K,
                                                                 Epilogue epi) {
   // the group member whose columns this workgroup computes: its fields come
   // in one scalar load round trip at a workgroup-uniform offset
   const SkinnyMember& mem = grp.m[GROUPED ? (int)blockIdx.z : 0];
+  const uint16_t* A = mem.A;
   const uint8_t* packed = mem.packed;
   const void* scales = mem.scales;
   const uint8_t* zeros = mem.zeros;
@@ -504,10 +510,10 @@ __host__ __device__ constexpr uint32_t ring_window_cap(uint32_t bytes) {
 }
 
 template <int FMT, bool OUT_F32, int D, int R, bool FULL, bool GROUPED>
-__global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint16_t* __restrict__ A,
-                                                                     SkinnyGroup grp, int M, int K,
+__global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(SkinnyGroupOf<GROUPED> grp, int M, int K,
                                                                      Epilogue epi) {
   const SkinnyMember& mem = grp.m[GROUPED ? (int)blockIdx.z : 0];
+  const uint16_t* A = mem.A;
   const uint8_t* packed = mem.packed;
   const uint8_t* scales = reinterpret_cast<const uint8_t*>(mem.scales);
   const uint8_t* zeros = mem.zeros;
@@ -656,9 +662,9 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(const uint1
 // A fit the staging registers; NS scale dwords per lane (and one zero dword,
 // int4) cover a tile's scale window.
 template <int FMT, bool OUT_F32, int U, int NS>
-__global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uint16_t* __restrict__ A,
-                                                                       SkinnyGroup grp, int M, int K,
+__global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(SkinnyGroup<1> grp, int M, int K,
                                                                        int tiles, Epilogue epi) {
+  const uint16_t* A = grp.m[0].A;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -889,22 +895,46 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(const uin
   if (i + 1 < mine) step(T1, T0, 1);
 }
 
+// The launch's members (CAP slots: 1 for a single GEMM) and its grid: x =
+// column tiles of `rows` (of the widest member), y = 16-row slices of A,
+// z = members; a member with fewer tiles than the widest has workgroups that
+// exit at once.
+template <int CAP>
+SkinnyGroup<CAP> skinny_group(const GroupedArgs& a, int rows) {
+  SkinnyGroup<CAP> grp = {};
+  for (int i = 0; i < a.count && i < CAP; ++i) {
+    grp.m[i].A = a.A[i];
+    grp.m[i].packed = a.packed[i];
+    grp.m[i].scales = a.scales[i];
+    grp.m[i].zeros = a.zeros[i];
+    grp.m[i].C = a.C[i];
+    grp.m[i].N = (int)a.N[i];
+  }
+  grp.rows = rows;
+  return grp;
+}
+dim3 skinny_grid(const GroupedArgs& a, int rows) {
+  int64_t max_n = 0;
+  for (int i = 0; i < a.count; ++i) max_n = a.N[i] > max_n ? a.N[i] : max_n;
+  return dim3((unsigned)((max_n + rows - 1) / rows), (unsigned)((a.M + 15) / 16), (unsigned)a.count);
+}
+
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, bool S_LDS>
-hipError_t launch_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim3 block, unsigned lds) {
+hipError_t launch_k(const GroupedArgs& a, int rows, dim3 grid, dim3 block, unsigned lds) {
   if (a.count > 1)
     return launch_kernel(skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, true>, grid, block, lds,
-                         a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
+                         a.stream, skinny_group<kMaxGroup>(a, rows), (int)a.M, (int)a.K, a.epi);
   return launch_kernel(skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, false>, grid, block, lds,
-                       a.stream, a.A, grp, (int)a.M, (int)a.K, a.epi);
+                       a.stream, skinny_group<1>(a, rows), (int)a.M, (int)a.K, a.epi);
 }
 
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA>
-hipError_t launch_s(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, dim3 block, bool s_lds,
+hipError_t launch_s(const GroupedArgs& a, int rows, dim3 grid, dim3 block, bool s_lds,
                     unsigned lds_a, unsigned lds_s) {
   const unsigned lds_dma = A_DMA ? block.x / 64 * U * 4096u : 0u;
   if (s_lds)
-    return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, true>(a, grp, grid, block, lds_a + lds_s + lds_dma);
-  return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, false>(a, grp, grid, block, lds_a + lds_dma);
+    return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, true>(a, rows, grid, block, lds_a + lds_s + lds_dma);
+  return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, false>(a, rows, grid, block, lds_a + lds_dma);
 }
 
 // Rows per workgroup: 16 unless fewer make the workgroup count fill whole
@@ -929,38 +959,20 @@ int skinny_rows(const GroupedArgs& a) {
   return rows;
 }
 
-// The launch's members and its grid: x = column tiles of `rows` (of the
-// widest member), y = 16-row slices of A, z = members; a member with fewer
-// tiles than the widest has workgroups that exit at once.
-SkinnyGroup skinny_group(const GroupedArgs& a, int rows, dim3& grid) {
-  SkinnyGroup grp = {};
-  int64_t max_n = 0;
-  for (int i = 0; i < a.count; ++i) {
-    grp.m[i].packed = a.packed[i];
-    grp.m[i].scales = a.scales[i];
-    grp.m[i].zeros = a.zeros[i];
-    grp.m[i].C = a.C[i];
-    grp.m[i].N = (int)a.N[i];
-    max_n = a.N[i] > max_n ? a.N[i] : max_n;
-  }
-  grp.rows = rows;
-  grid = dim3((unsigned)((max_n + rows - 1) / rows), (unsigned)((a.M + 15) / 16), (unsigned)a.count);
-  return grp;
-}
 
 template <int FMT, bool OUT_F32, int D, int R, bool FULL>
-hipError_t launch_ring_k(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, unsigned lds) {
+hipError_t launch_ring_k(const GroupedArgs& a, int rows, dim3 grid, unsigned lds) {
   const dim3 block(64 * (kRingVirt / R));
   if (a.count > 1)
     return launch_kernel(skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, true>, grid, block, lds, a.stream,
-                         a.A, grp, (int)a.M, (int)a.K, a.epi);
+                         skinny_group<kMaxGroup>(a, rows), (int)a.M, (int)a.K, a.epi);
   return launch_kernel(skinny_ring_kernel<FMT, OUT_F32, D, R, FULL, false>, grid, block, lds, a.stream,
-                       a.A, grp, (int)a.M, (int)a.K, a.epi);
+                       skinny_group<1>(a, rows), (int)a.M, (int)a.K, a.epi);
 }
 template <int FMT, bool OUT_F32, int D, int R>
-hipError_t launch_ring_f(const GroupedArgs& a, const SkinnyGroup& grp, dim3 grid, unsigned lds) {
-  return a.K % 128 == 0 ? launch_ring_k<FMT, OUT_F32, D, R, true>(a, grp, grid, lds)
-                        : launch_ring_k<FMT, OUT_F32, D, R, false>(a, grp, grid, lds);
+hipError_t launch_ring_f(const GroupedArgs& a, int rows, dim3 grid, unsigned lds) {
+  return a.K % 128 == 0 ? launch_ring_k<FMT, OUT_F32, D, R, true>(a, rows, grid, lds)
+                        : launch_ring_k<FMT, OUT_F32, D, R, false>(a, rows, grid, lds);
 }
 
 // The ring variant for A slices past the one-time LDS copy.  A grid of one
@@ -977,17 +989,17 @@ bool try_ring(const GroupedArgs& a, hipError_t& err) {
   const int64_t groups = (a.K + FormatTraits<FMT>::kGroup - 1) / FormatTraits<FMT>::kGroup;
   const int64_t win = ring_window_cap((uint32_t)(16 * groups * SB)) +
                       (has_zeros(FMT) ? ring_window_cap((uint32_t)(16 * groups)) : 0);
-  dim3 grid;
-  const SkinnyGroup grp = skinny_group(a, skinny_rows(a), grid);
+  const int rows = skinny_rows(a);
+  const dim3 grid = skinny_grid(a, rows);
   const bool one_round = (int64_t)grid.x * grid.y * grid.z <= 256;
   auto lds_of = [&](int w, int d) { return win + (int64_t)w * d * kRingSlot + (int64_t)kRingVirt * 1024; };
   constexpr int64_t kLds = 160 * 1024;
   if (!one_round && lds_of(4, 2) <= kLds) {
-    err = launch_ring_f<FMT, OUT_F32, 2, 2>(a, grp, grid, (unsigned)lds_of(4, 2));
+    err = launch_ring_f<FMT, OUT_F32, 2, 2>(a, rows, grid, (unsigned)lds_of(4, 2));
   } else if (lds_of(8, 3) <= kLds) {
-    err = launch_ring_f<FMT, OUT_F32, 3, 1>(a, grp, grid, (unsigned)lds_of(8, 3));
+    err = launch_ring_f<FMT, OUT_F32, 3, 1>(a, rows, grid, (unsigned)lds_of(8, 3));
   } else if (lds_of(8, 2) <= kLds) {
-    err = launch_ring_f<FMT, OUT_F32, 2, 1>(a, grp, grid, (unsigned)lds_of(8, 2));
+    err = launch_ring_f<FMT, OUT_F32, 2, 1>(a, rows, grid, (unsigned)lds_of(8, 2));
   } else {
     return false;
   }
@@ -997,8 +1009,7 @@ bool try_ring(const GroupedArgs& a, hipError_t& err) {
 template <int FMT, bool OUT_F32, int U>
 hipError_t launch_u(const GroupedArgs& a, int waves) {
   const int rows = skinny_rows(a);
-  dim3 grid;
-  const SkinnyGroup grp = skinny_group(a, rows, grid);
+  const dim3 grid = skinny_grid(a, rows);
   // stage A in LDS when the workgroup's A slice fits its staging registers
   const int64_t arows = a.M < 16 ? a.M : 16;
   const int64_t a_bytes = arows * a.K * 2;
@@ -1023,12 +1034,12 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   const dim3 block(64 * waves);
   const bool a_dma = !a_lds && waves * U * 4096 <= 128 * 1024;
   const unsigned ls = (unsigned)lds_s;
-  if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true, false>(a, grp, grid, block, s_lds, lds_a, ls);
-  if (a_lds) return launch_s<FMT, OUT_F32, U, true, false, false>(a, grp, grid, block, s_lds, lds_a, ls);
-  if (a_dma && full) return launch_s<FMT, OUT_F32, U, false, true, true>(a, grp, grid, block, s_lds, lds_a, ls);
-  if (a_dma) return launch_s<FMT, OUT_F32, U, false, false, true>(a, grp, grid, block, s_lds, lds_a, ls);
-  if (full) return launch_s<FMT, OUT_F32, U, false, true, false>(a, grp, grid, block, s_lds, lds_a, ls);
-  return launch_s<FMT, OUT_F32, U, false, false, false>(a, grp, grid, block, s_lds, lds_a, ls);
+  if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true, false>(a, rows, grid, block, s_lds, lds_a, ls);
+  if (a_lds) return launch_s<FMT, OUT_F32, U, true, false, false>(a, rows, grid, block, s_lds, lds_a, ls);
+  if (a_dma && full) return launch_s<FMT, OUT_F32, U, false, true, true>(a, rows, grid, block, s_lds, lds_a, ls);
+  if (a_dma) return launch_s<FMT, OUT_F32, U, false, false, true>(a, rows, grid, block, s_lds, lds_a, ls);
+  if (full) return launch_s<FMT, OUT_F32, U, false, true, false>(a, rows, grid, block, s_lds, lds_a, ls);
+  return launch_s<FMT, OUT_F32, U, false, false, false>(a, rows, grid, block, s_lds, lds_a, ls);
 }
 
 // k-blocks of 128 per wave: 2 while K fits 16 waves that way, else 4.  The
@@ -1065,12 +1076,12 @@ int resident_per_cu(const void* kernel, int threads, unsigned lds) {
 }
 
 template <int FMT, bool OUT_F32, int U, int NS>
-hipError_t launch_stream_k(const GroupedArgs& a, const SkinnyGroup& grp, int tiles, int waves, unsigned lds) {
+hipError_t launch_stream_k(const GroupedArgs& a, const SkinnyGroup<1>& grp, int tiles, int waves, unsigned lds) {
   const void* kern = reinterpret_cast<const void*>(&skinny_stream_kernel<FMT, OUT_F32, U, NS>);
   const int resident = resident_per_cu(kern, 64 * waves, lds) * device_cus();
   const dim3 grid((unsigned)(tiles < resident ? tiles : resident));
   const dim3 block(64 * waves);
-  return launch_kernel(skinny_stream_kernel<FMT, OUT_F32, U, NS>, grid, block, lds, a.stream, a.A, grp,
+  return launch_kernel(skinny_stream_kernel<FMT, OUT_F32, U, NS>, grid, block, lds, a.stream, grp,
                        (int)a.M, (int)a.K, tiles, a.epi);
 }
 
@@ -1099,13 +1110,7 @@ bool try_stream(const GroupedArgs& a, int64_t min_tiles, hipError_t& err) {
   if (NS == 0 || (FMT == kInt4 && z_words > threads)) return false;
   const int64_t tiles = (a.N[0] + 15) / 16;
   if (tiles < min_tiles || tiles < 1) return false;
-  SkinnyGroup grp = {};
-  grp.m[0].packed = a.packed[0];
-  grp.m[0].scales = a.scales[0];
-  grp.m[0].zeros = a.zeros[0];
-  grp.m[0].C = a.C[0];
-  grp.m[0].N = (int)a.N[0];
-  grp.rows = 16;
+  const SkinnyGroup<1> grp = skinny_group<1>(a, 16);
   const int64_t s_cap = (16 * groups * SB + 6 + 15) & ~15;
   const int64_t z_cap = FMT == kInt4 ? (16 * groups + 6 + 15) & ~15 : 0;
   const unsigned lds = (unsigned)((((a.M + 1) * a.K * 2 + 15) & ~15) + 3 * (s_cap + z_cap) + 3 * threads * 16);
@@ -1175,7 +1180,7 @@ hipError_t launch_skinny(const GemmArgs& a) {
   GroupedArgs g = {};
   g.fmt = a.fmt;
   g.out_f32 = a.out_f32;
-  g.A = a.A;
+  g.A[0] = a.A;
   g.count = 1;
   g.packed[0] = a.packed;
   g.scales[0] = a.scales;
