@@ -133,3 +133,21 @@ def test_batched_graph_capture_replay():
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert same_bits(o, e), rep
+
+
+@pytest.mark.parametrize("fmt,M,K", [(w4.INT4_G128, 1, 3072), (w4.NVFP4, 4, 2048), (w4.MXFP4, 16, 1024),
+                                     (w4.INT4_SYM, 2, 4096), (w4.INT4_G32, 1, 1024)])
+def test_wave_count_does_not_change_bits(fmt, M, K):
+    """A launch of many workgroups computes two of the K split's partial sums
+    per wave (half the waves); a launch that fits the CUs at once computes one.
+    A column's bits must not depend on which: every 1024-column slice of a
+    wide matrix equals the same columns computed by a narrow launch."""
+    N = 12288
+    case = inputs.make_case(fmt, M, N, K, seed=fmt + M)
+    A, p, s, z = to_dev(case)
+    wide = w4.gemm(fmt, A, p, s, z)
+    for c0 in range(0, N, 4096):
+        sl = slice(c0, c0 + 1024)
+        narrow = w4.gemm(fmt, A, p[sl].contiguous(), s[sl].contiguous(), None if z is None else z[sl].contiguous())
+        torch.cuda.synchronize()
+        assert same_bits(wide[:, sl].contiguous(), narrow), c0

@@ -37,6 +37,7 @@ namespace w4a16 {
 namespace {
 
 constexpr int kMaxWaves = 16;
+int device_cus();
 constexpr int kAStage = 2;  // 16-byte chunks of A per thread when A is staged in LDS
 constexpr int kSStage = 3;  // scale dwords per thread when the scales are staged in LDS
 constexpr int kZStage = 2;  // zero dwords per thread (int4)
@@ -197,9 +198,17 @@ __device__ __forceinline__ void skinny_store(const f32x4_t* red, int waves, int 
 // straight into a private LDS region (asynchronous global -> LDS copies of
 // contiguous 256-byte row pieces) instead of per-lane A loads.
 // GROUPED: more than one member, blockIdx.z (a single GEMM reads member 0).
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED>
+// R: virtual waves per wave.  The split of K is into virtual waves of U
+// k-blocks each (virtual wave v sums k-blocks v U .. v U + U - 1, and the
+// partial sums are added in v order); a wave computes R consecutive virtual
+// waves into R accumulators.  The bits never depend on R, which launches of
+// many workgroups set to 2 (half the waves per workgroup, so more of them
+// fit a CU and more weight loads are in flight); R = 2 needs K covered in
+// one pass.
+template <int FMT, bool OUT_F32, int U, int R, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GROUPED> grp, int M, int K,
                                                                 Epilogue epi) {
+  constexpr int UR = U * R;  // k-blocks per wave and pass
   // the group member whose columns this workgroup computes: its fields come
   // in one scalar load round trip at a workgroup-uniform offset
   const SkinnyMember& mem = grp.m[GROUPED ? (int)blockIdx.z : 0];
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
   // per-wave A regions (A_DMA) after the scale and zero windows
   const uint32_t a_dma_off = S_LDS ? z_off + z_cap : s_off;
   const uint32_t a_wave = lds_address(a_lds) + a_dma_off +
-                          (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (uint32_t)(U * 4096);
+                          (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (uint32_t)(UR * 4096);
   uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
   // staging loads are issued only by waves that hold some in-range slot
   // (a wave whose first slot is past the block skips the instruction)
@@ -315,20 +324,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
     }
   }
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  u32x4_t q[U];
-  u32x4_t a[U][4];
-  uint32_t sraw[U];
-  uint32_t zraw[U];
+  f32x4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t q[UR];
+  u32x4_t a[UR][4];
+  uint32_t sraw[UR];
+  uint32_t zraw[UR];
 
-  // Each wave owns U consecutive k-blocks per pass (contiguous bytes of every
-  // row it reads); pass p covers k-blocks [(p * waves + wave) * U, +U).
+  // Each wave owns UR consecutive k-blocks per pass (contiguous bytes of every
+  // row it reads); pass p covers k-blocks [(p * waves + wave) * UR, +UR).
   auto valid = [&](int kb, int c) { return FULL ? (kb < KB) : (kb < KB && c < chunks); };
   auto issue = [&](int kbase) {
     // scales first: vmcnt retires in issue order, so the first k-block's
     // arithmetic then waits only for its own weights
 #pragma unroll
-    for (int u = 0; u < (S_LDS ? 0 : U); ++u) {
+    for (int u = 0; u < (S_LDS ? 0 : UR); ++u) {
       const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
       // LDS chunk l%16, which holds 16-byte chunk (l%16) ^ row of the row's
       // 256 bytes (the fragment reads of 16 rows then hit distinct banks)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UR; ++u) {
         const int kb = kbase + u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UR; ++u) {
       const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
@@ -389,11 +400,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
     // this pass's loads (whatever order they were issued in)
     if constexpr (A_DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < UR; ++u) {
       const int kb = kbase + u;
       if (FULL && kb >= KB) break;  // wave-uniform: nothing was loaded
       if constexpr (A_DMA) {
-        const uint8_t* src = a_lds + a_dma_off + (size_t)wave * (U * 4096) + u * 4096 + nl * 256;
+        const uint8_t* src = a_lds + a_dma_off + (size_t)wave * (UR * 4096) + u * 4096 + nl * 256;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           a[u][j] = *reinterpret_cast<const u32x4_t*>(src + (((4 * g + j) ^ nl) * 16));
@@ -426,11 +437,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
           sraw[u] = sb[nl * groups + (ok ? c : 0)];
         }
       }
-      acc = kblock_mac<FMT, A_LDS>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc);
+      acc[u / U] = kblock_mac<FMT, A_LDS>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc[u / U]);
     }
   };
 
-  int kbase = wave * U;
+  int kbase = wave * UR;
   issue(kbase);
   // LDS-only barriers: each wave's weights stay in flight, and its first
   // k-block's arithmetic waits for that k-block's load alone
@@ -453,17 +464,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
     lds_barrier();
   }
   compute(kbase);
-  for (kbase += waves * U; kbase < KB; kbase += waves * U) {
+  for (kbase += waves * UR; kbase < KB; kbase += waves * UR) {
     issue(kbase);
     compute(kbase);
   }
 
   // ---- split-K reduction across the waves, through LDS ----------------------
+  // (virtual wave wave * R + r)
   __shared__ f32x4_t red[kMaxWaves][64];
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int r = 0; r < R; ++r) red[wave * R + r][lane] = acc[r];
   lds_barrier();
   if (wave != 0) return;
-  skinny_store<OUT_F32>(&red[0][0], waves, lane, nl, g, rows, arows, m0, n, M, N, C, epi);
+  skinny_store<OUT_F32>(&red[0][0], waves * R, lane, nl, g, rows, arows, m0, n, M, N, C, epi);
 }
 
 // ---- ring variant: every per-k-block operand through LDS copies ----------
@@ -919,22 +932,22 @@ dim3 skinny_grid(const GroupedArgs& a, int rows) {
   return dim3((unsigned)((max_n + rows - 1) / rows), (unsigned)((a.M + 15) / 16), (unsigned)a.count);
 }
 
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, bool S_LDS>
+template <int FMT, bool OUT_F32, int U, int R, bool A_LDS, bool FULL, bool A_DMA, bool S_LDS>
 hipError_t launch_k(const GroupedArgs& a, int rows, dim3 grid, dim3 block, unsigned lds) {
   if (a.count > 1)
-    return launch_kernel(skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, true>, grid, block, lds,
+    return launch_kernel(skinny_kernel<FMT, OUT_F32, U, R, A_LDS, FULL, S_LDS, A_DMA, true>, grid, block, lds,
                          a.stream, skinny_group<kMaxGroup>(a, rows), (int)a.M, (int)a.K, a.epi);
-  return launch_kernel(skinny_kernel<FMT, OUT_F32, U, A_LDS, FULL, S_LDS, A_DMA, false>, grid, block, lds,
+  return launch_kernel(skinny_kernel<FMT, OUT_F32, U, R, A_LDS, FULL, S_LDS, A_DMA, false>, grid, block, lds,
                        a.stream, skinny_group<1>(a, rows), (int)a.M, (int)a.K, a.epi);
 }
 
-template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA>
+template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, int R = 1>
 hipError_t launch_s(const GroupedArgs& a, int rows, dim3 grid, dim3 block, bool s_lds,
                     unsigned lds_a, unsigned lds_s) {
-  const unsigned lds_dma = A_DMA ? block.x / 64 * U * 4096u : 0u;
+  const unsigned lds_dma = A_DMA ? block.x / 64 * U * R * 4096u : 0u;
   if (s_lds)
-    return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, true>(a, rows, grid, block, lds_a + lds_s + lds_dma);
-  return launch_k<FMT, OUT_F32, U, A_LDS, FULL, A_DMA, false>(a, rows, grid, block, lds_a + lds_dma);
+    return launch_k<FMT, OUT_F32, U, R, A_LDS, FULL, A_DMA, true>(a, rows, grid, block, lds_a + lds_s + lds_dma);
+  return launch_k<FMT, OUT_F32, U, R, A_LDS, FULL, A_DMA, false>(a, rows, grid, block, lds_a + lds_dma);
 }
 
 // Rows per workgroup: 16 unless fewer make the workgroup count fill whole
@@ -1034,6 +1047,26 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
   const dim3 block(64 * waves);
   const bool a_dma = !a_lds && waves * U * 4096 <= 128 * 1024;
   const unsigned ls = (unsigned)lds_s;
+  // Two virtual waves per wave (same bits) when the launch has several
+  // rounds of workgroups and K is covered in one pass: measured on the
+  // decode chain's launches of thousands of workgroups, 404 -> 357 us per
+  // pass; launches of one or two rounds keep the full wave count (the decode
+  // GEMV's 512 workgroups: 5.7 us with it, 6.2 without).
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  const int KB = (int)((a.K / 32 + 3) / 4);
+  // (the staging loops cover kAStage / kSStage / kZStage items per thread:
+  // A and the windows must still fit with half the threads)
+  const int64_t half_threads = 32 * waves;
+  const bool half_fits = a_bytes <= (int64_t)kAStage * 16 * half_threads &&
+                         (!s_lds || ((16 * groups * SB + 6) / 4 <= kSStage * half_threads &&
+                                     (!has_zeros(FMT) || (16 * groups + 6) / 4 <= kZStage * half_threads)));
+  const bool halve = a_lds && half_fits && waves % 2 == 0 && waves * U >= KB &&
+                     wgs > 4 * (int64_t)device_cus();
+  if (halve) {
+    const dim3 half(block.x / 2);
+    if (full) return launch_s<FMT, OUT_F32, U, true, true, false, 2>(a, rows, grid, half, s_lds, lds_a, ls);
+    return launch_s<FMT, OUT_F32, U, true, false, false, 2>(a, rows, grid, half, s_lds, lds_a, ls);
+  }
   if (a_lds && full) return launch_s<FMT, OUT_F32, U, true, true, false>(a, rows, grid, block, s_lds, lds_a, ls);
   if (a_lds) return launch_s<FMT, OUT_F32, U, true, false, false>(a, rows, grid, block, s_lds, lds_a, ls);
   if (a_dma && full) return launch_s<FMT, OUT_F32, U, false, true, true>(a, rows, grid, block, s_lds, lds_a, ls);
