@@ -75,3 +75,38 @@ def int4_rounding_adversary(fmt, M, N, K, seed):
     case.scales[:] = sbits
     case.A[:] = case.A & np.uint16(0x7FFF)             # |a|: every product has the weight's sign
     return case
+
+
+def int4_cancellation_adversary(fmt, M, N, K, seed):
+    """An int4 case whose exact result is tiny beside the terms a kernel could
+    form on the way: every code of a group equals its zero point except one,
+    which is one step away, and that code meets the one small activation of
+    the group (2^-12) while the other activations are large (about 2^8).  The
+    exact sum is then a handful of small products, and a kernel that adds
+    sum(a * code) and sum(a * (-zero)) separately leaves fp32 rounding errors
+    of the large sums (about 2^-24 * 2^12) that exceed the gate by orders of
+    magnitude; a kernel that forms code - zero before multiplying is exact.
+    Scales are 1.0.  Returns an inputs.Case."""
+    import numpy as np
+    import oracle
+    from weight_only_bit_w4a16_amd import inputs
+
+    case = inputs.make_case(fmt, M, N, K, seed)
+    rng = np.random.default_rng(seed + 11)
+    G = oracle.GROUP[fmt]
+    ng = (K + G - 1) // G
+    z = np.full((N, ng), 8) if fmt == oracle.INT4_SYM else rng.integers(1, 15, size=(N, ng))
+    if case.zeros is not None:
+        case.zeros[:] = z.astype(np.uint8)
+    codes = np.repeat(z, G, axis=1)[:, :K].astype(np.int64)
+    # one position per group and row: code = zero +- 1, at the group's small activation
+    pos = np.minimum(np.arange(ng) * G + rng.integers(0, G, size=ng), K - 1)  # same for every row
+    step = rng.choice([-1, 1], size=(N, ng))
+    codes[:, pos] += step
+    codes = codes.astype(np.uint8)
+    case.packed[:] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    case.scales[:] = oracle.round_bf16(1.0)
+    a = (rng.standard_normal((M, K)) * 256.0).astype(np.float32)
+    a[:, pos] = np.float32(2.0 ** -12) * rng.choice([-1, 1], size=(M, ng))
+    case.A[:] = inputs.bf16_bits(a)
+    return case

@@ -115,3 +115,22 @@ def test_bf16_rounded_int4_weights_fail_the_gate_at_small_k_on_random_data():
                                 weights_bf16=True)
             worst = max(worst, oracle.gate_ratio(Cb, C, S, False))
     assert worst > 1.0, worst
+
+
+@pytest.mark.parametrize("fmt", [oracle.INT4_G128, oracle.INT4_SYM])
+def test_cancellation_adversary_is_tiny_beside_its_terms(fmt):
+    """The cancellation input: the exact result is a sum of a few 2^-12-sized
+    products while sum(a * code) is of order 2^8 * 15 * sqrt(K); any scheme
+    that rounds the two sums separately in fp32 misses the gate by orders of
+    magnitude (here emulated with fp32 products per group)."""
+    from conftest import int4_cancellation_adversary
+    M, N, K = 8, 32, 1024
+    case = int4_cancellation_adversary(fmt, M, N, K, seed=2)
+    C, S = _ref(case)
+    assert np.abs(C).max() <= K / 128 * 2.0 ** -12 and S.max() <= K / 128 * 2.0 ** -12
+    a = oracle.bf16_values(case.A).astype(np.float32)
+    w, _ = oracle.dequant(fmt, case.packed, case.scales, case.zeros, N, K)
+    z = (case.zeros if case.zeros is not None else np.full((N, K // 128), 8)).astype(np.float32)
+    z = np.repeat(z, 128, axis=1)
+    split = (a @ (w.astype(np.float32) + z).T) + (a @ (-z).T)   # two fp32 sums, then added
+    assert oracle.gate_ratio(split.astype(np.float64), C, S, False) > 10.0

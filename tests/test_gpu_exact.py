@@ -4,6 +4,10 @@
   where weights rounded to bf16 before the sum miss the gate by almost 2x
   (tests/conftest.py int4_rounding_adversary, fp32 output), and on random
   data at small K, where rounding errors do not average out;
+* int4 code - zero is formed before the multiply on every kernel: on data
+  whose exact result is tiny beside sum(a * code) and sum(a * zero)
+  (tests/conftest.py int4_cancellation_adversary), a kernel that sums the
+  two separately loses the result to fp32 rounding;
 * an e8m0 scale byte 0xFF (NaN) makes every output of its weight row NaN on
   every kernel variant, as it makes the oracle's weights NaN; all other
   outputs stay within the gate.
@@ -14,7 +18,7 @@ import torch
 
 import oracle
 import weight_only_bit_w4a16_amd as w4
-from conftest import int4_rounding_adversary
+from conftest import int4_cancellation_adversary, int4_rounding_adversary
 from weight_only_bit_w4a16_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -99,6 +103,38 @@ def test_int4_small_k_random(fmt, path, K):
         case = inputs.make_case(fmt, 64, 1024, K, seed)
         C = run(case, path)
         gate(C, case, False, f"int4 fmt {fmt} random {path} K={K} seed {seed}")
+
+
+CANCEL_CASES = [
+    ("skinny A in LDS", 1, 64, 3072, "skinny"),
+    ("skinny 16 rows", 16, 64, 2048, "skinny"),
+    ("skinny ring", 16, 48, 8192, "skinny"),
+    ("skinny stream", 1, 16384, 512, "auto"),
+    ("skinny many workgroups", 1, 12288, 1024, "skinny"),
+    ("mid ring", 64, 2048, 512, "mid"),
+    ("mid per-lane", 40, 64, 98304, "mid"),
+    ("tiled", 300, 256, 512, "tiled"),
+]
+
+
+@pytest.mark.parametrize("fmt", INT4)
+@pytest.mark.parametrize("what,M,N,K,path", CANCEL_CASES, ids=[c[0] for c in CANCEL_CASES])
+def test_int4_cancellation(fmt, what, M, N, K, path):
+    if what == "skinny stream" and fmt in (w4.INT4_G32, w4.INT4_G64):
+        pytest.skip("the streaming variant serves groups of 128 only")
+    case = int4_cancellation_adversary(fmt, M, N, K, seed=M + K + fmt)
+    print(f"[cancel] fmt {fmt} {what}: {M}x{N}x{K} path {path}", flush=True)
+    C = run(case, path)
+    if N * K > 20_000_000:
+        rng = np.random.default_rng(K)
+        mi, ni = rng.integers(0, M, 512), rng.integers(0, N, 512)
+        Cref, S = oracle.gemm_at(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K, mi, ni)
+        r = oracle.gate_ratio(C[mi, ni], Cref, S, False)
+    else:
+        Cref, S = oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
+        r = oracle.gate_ratio(C, Cref, S, False)
+    print(f"[gate] cancel fmt {fmt} {what}: max err/bound = {r:.3e}", flush=True)
+    assert r <= 1.0
 
 
 # ---- NaN e8m0 scales -------------------------------------------------------------

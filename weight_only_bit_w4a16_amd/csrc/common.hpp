@@ -240,45 +240,8 @@ __device__ __forceinline__ u32x4_t fp4x8_to_bf16_fscale(uint32_t q, float scale)
 
 // ---- int4 decoders -------------------------------------------------------------
 
-// 8 int4 codes (one dword, code k in nibble k) to their exact bf16 values in
-// natural k order.  The even-k and odd-k nibbles are masked into bytes, two
-// byte permutes put them back in k order (k0 k1 k2 k3 | k4 k5 k6 k7), and
-// each byte, read as the e4m3 value code * 2^-9, is converted with a scale of
-// 2^9, exactly, two codes per instruction: nine VALU operations per 8 codes.
-// Only compiler-visible instructions: a VALU write hidden in inline assembly
-// escapes the compiler's hazard checks, and an MFMA reading its result too
-// soon afterwards sees the register's old value.
-__device__ __forceinline__ u32x4_t int4x8_to_bf16_natural(uint32_t q) {
-  const uint32_t lo = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
-  const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
-  const uint32_t p0 = perm_b32(hi, lo, 0x05010400u);  // bytes k0 k1 k2 k3
-  const uint32_t p1 = perm_b32(hi, lo, 0x07030602u);  // bytes k4 k5 k6 k7
-  u32x4_t r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p0, 512.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p0, 512.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p1, 512.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p1, 512.0f, true));
-  return r;
-}
-
-// 8 int4 codes (one dword, code k in nibble k) to their exact bf16 values, in
-// the k order (0, 2, 4, 6, 1, 3, 5, 7).  A code c alone in a byte is the e4m3
-// value c * 2^-9 (subnormal for c < 8, first binade for c >= 8), so the scaled
-// fp8 conversion with a scale of 2^9 yields c exactly, two codes per
-// instruction: seven VALU operations per 8 codes.
-__device__ __forceinline__ u32x4_t int4x8_to_bf16_exact(uint32_t q) {
-  const uint32_t lo = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
-  const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
-  u32x4_t r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));
-  return r;
-}
-
 // 8 consecutive bf16 values (k order 0..7, two per dword) reordered to the k
-// order (0, 2, 4, 6, 1, 3, 5, 7) of int4x8_to_bf16_exact.
+// order (0, 2, 4, 6, 1, 3, 5, 7) of int4x8_minus_zero_even_odd.
 __device__ __forceinline__ u32x4_t bf16x8_even_odd(u32x4_t a) {
   u32x4_t r;
   r[0] = perm_b32(a[1], a[0], 0x05040100u);  // (a0, a2)
@@ -286,13 +249,6 @@ __device__ __forceinline__ u32x4_t bf16x8_even_odd(u32x4_t a) {
   r[2] = perm_b32(a[1], a[0], 0x07060302u);  // (a1, a3)
   r[3] = perm_b32(a[3], a[2], 0x07060302u);  // (a5, a7)
   return r;
-}
-
-// bf16 -z broadcast to 8 lanes' worth (exact for every zero byte, z <= 255).
-__device__ __forceinline__ u32x4_t int4_neg_zero(uint32_t z) {
-  const uint32_t h = __float_as_uint(-(float)z) >> 16;
-  const uint32_t d = h | (h << 16);
-  return u32x4_t{d, d, d, d};
 }
 
 // 8 int4 codes to bf16 weights (code - zero) * scale, each rounded once to
@@ -353,6 +309,23 @@ __device__ __forceinline__ u32x4_t int4x8_minus_zero(uint32_t q, float zf) {
   r[1] = pack_bf16x2(e0[1] - zf, o0[1] - zf);
   r[2] = pack_bf16x2(e1[0] - zf, o1[0] - zf);
   r[3] = pack_bf16x2(e1[1] - zf, o1[1] - zf);
+  return r;
+}
+
+// The same in the k order (0, 2, 4, 6, 1, 3, 5, 7) of an A copy stored in
+// even / odd order: the converter's pairs are used as they come.
+__device__ __forceinline__ u32x4_t int4x8_minus_zero_even_odd(uint32_t q, float zf) {
+  const uint32_t l = q & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
+  const uint32_t h = (q >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+  const f32x2_t e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, false);  // k0, k2
+  const f32x2_t e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, true);   // k4, k6
+  const f32x2_t o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 512.0f, false);  // k1, k3
+  const f32x2_t o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, 512.0f, true);   // k5, k7
+  u32x4_t r;
+  r[0] = pack_bf16x2(e0[0] - zf, e0[1] - zf);
+  r[1] = pack_bf16x2(e1[0] - zf, e1[1] - zf);
+  r[2] = pack_bf16x2(o0[0] - zf, o0[1] - zf);
+  r[3] = pack_bf16x2(o1[0] - zf, o1[1] - zf);
   return r;
 }
 

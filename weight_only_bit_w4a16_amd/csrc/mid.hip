@@ -15,18 +15,16 @@
 //   * A: the lane supplies row 16s + l%16 of row slice s over the same 32 k,
 //     loaded straight from memory (A is small and read once per workgroup, so
 //     it is served from L2);
-//   * int4: codes decode exactly in natural k order, and a second MFMA per
-//     step with the constant -zero fills a second accumulator with the same
-//     rounding sequence, so a k-block whose codes all equal the zero point
-//     cancels to exactly 0; the group scale multiplies once per k-block.
-//     fp4: the scale is applied exactly in the decode;
+//   * int4 with groups of 128: code - zero, exact in bf16, is formed per
+//     weight before the MFMA and the group scale multiplies once per k-block
+//     (groups of 32 / 64: the exact weight as bf16 hi + lo fragments); fp4:
+//     the scale is applied exactly in the decode;
 //   * scales (and zeros) of the workgroup's 32 rows are one contiguous block:
 //     copied once to LDS with coalesced dword loads when it fits the staging
 //     registers (S_LDS), else each lane loads its own with its weights.
 // That is the per-lane form.  The ring variant below (used whenever its LDS
 // fits) keeps the tile and the operand layouts but moves every operand by
-// global -> LDS copies, and decodes int4 with groups of 128 as the exact
-// code - zero (one MFMA chain, the scale once per k-block).
+// global -> LDS copies.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -216,7 +214,6 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
       // groups of 32 / 64: the exact weights as hi + lo fragments)
       u32x4_t b[2][4], bl[2][4];
       float sc[2];
-      u32x4_t nz[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = 16 * h + nl;
@@ -231,9 +228,8 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
             z = zraw[u][h];
           }
           sc[h] = bf16_bits_to_f32(sbits);
-          nz[h] = int4_neg_zero(z);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_natural(q[u][h][j]);
+          for (int j = 0; j < 4; ++j) b[h][j] = int4x8_minus_zero(q[u][h][j], (float)z);
         } else if constexpr (is_int4(FMT)) {
           // groups shorter than a k-block: the chunk's group, applied in the
           // decode, the exact weight (code - zero) * scale as hi + lo
@@ -273,14 +269,10 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
         for (int h = 0; h < 2; ++h) {
           if constexpr (is_int4_g128(FMT)) {
             f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
-            f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              dp = mfma16x16x32(a[j], b[h][j], dp);
-              dn = mfma16x16x32(a[j], nz[h], dn);
-            }
+            for (int j = 0; j < 4; ++j) dp = mfma16x16x32(a[j], b[h][j], dp);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[s][h][i] = __builtin_fmaf(sc[h], dp[i] + dn[i], acc[s][h][i]);
+            for (int i = 0; i < 4; ++i) acc[s][h][i] = __builtin_fmaf(sc[h], dp[i], acc[s][h][i]);
           } else if constexpr (is_int4(FMT)) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -458,9 +450,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
     // both column slices decoded once, to bf16 MFMA operands.  int4 with
     // groups of 128: code - zero, exact in bf16 (an integer in -255 .. 15),
     // one MFMA chain, the scale once per k-block (a k-block whose codes all
-    // equal the zero point contributes exactly 0); this costs 10 more VALU
-    // per 8 codes than the exact codes but half the MFMAs of the +-zero pair
-    // (measured 64 x 8192 x 3072: 13.5 -> 12.1 us)
+    // equal the zero point contributes exactly 0)
     // (int4 with groups of 32 / 64: the exact weights as hi + lo fragments)
     u32x4_t b[2][4], bl[2][4];
     float sc[2];
@@ -473,7 +463,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
         sc[h] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
         const float zf = (float)(has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[h][j] = int4x8_to_bf16_weights(q[j], 1.0f, zf);
+        for (int j = 0; j < 4; ++j) b[h][j] = int4x8_minus_zero(q[j], zf);
       } else if constexpr (is_int4(FMT)) {
         const int gi = r * groups + (cc >> GS);
         const float sv = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));

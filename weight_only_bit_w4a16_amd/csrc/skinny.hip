@@ -16,12 +16,11 @@
 //   * partial sums of the W waves are added through LDS at the end (split-K
 //     inside the workgroup: no workspace, no atomics, deterministic).
 // Decode per format:
-//   * int4: the codes become exact bf16 values through the scaled fp8
-//     converter -- in even / odd k order when A sits in LDS (A is stored in
-//     that order), else in natural k order; a second MFMA per step with the
-//     constant -zero fills a second accumulator; their sum is
-//     sum_k a_k (code_k - zero), which the group scale multiplies once per
-//     k-block (k-block = int4 group);
+//   * int4: code - zero becomes an exact bf16 value (the code through the
+//     scaled fp8 converter, the zero subtracted in fp32) -- in even / odd k
+//     order when A sits in LDS (A is stored in that order), else in natural
+//     k order; the group scale multiplies the sum once per k-block (k-block
+//     = int4 group of 128);
 //   * NVFP4: e2m1 -> fp32, times |e4m3 scale| (exact), -> bf16 (exact);
 //   * MXFP4: hardware e2m1 conversion scaled by 2^(E-127) (exact).
 #include <atomic>
@@ -66,11 +65,12 @@ using SkinnyGroupOf = SkinnyGroup<GROUPED ? kMaxGroup : 1>;
 // One k-block of 128 codes into acc: a[j] is the lane's A fragment of MFMA
 // step j (32 codes), q[j] its 8 codes of that step, sraw / zraw the raw scale
 // (and zero) bytes of the lane's chunk.
-//   int4 g128 (and symmetric): the +code and -zero products go to separate accumulators that
-//     follow the same rounding sequence, so a k-block whose codes all equal
-//     the zero point cancels to exactly 0.  EVEN_ODD: A sits in LDS in the
-//     even / odd k order of the shorter decode, and the codes convert in that
-//     order; otherwise in natural k order, like A.
+//   int4 g128 (and symmetric): code - zero, exact in bf16, is formed for
+//     each weight before the MFMA (a sum of a * code and a separate sum of
+//     a * zero would lose small results to the rounding of the two large
+//     sums), and the group scale multiplies the k-block's sum.  EVEN_ODD: A
+//     sits in LDS in even / odd k order and the codes convert in that order;
+//     otherwise in natural k order, like A.
 //   int4 g32 / g64: groups shorter than a k-block; the lane's chunk has one
 //     group, whose exact weights (code - zero) * scale are split into two
 //     bf16 fragments hi + lo (both exact) that feed two MFMAs, so the
@@ -81,20 +81,18 @@ template <int FMT, bool EVEN_ODD>
 __device__ __forceinline__ f32x4_t kblock_mac(const u32x4_t (&a)[4], const u32x4_t& q, uint32_t sraw,
                                               uint32_t zraw, f32x4_t acc) {
   if constexpr (is_int4_g128(FMT)) {
-    const u32x4_t nz = int4_neg_zero(zraw);
+    const float zf = (float)zraw;
     f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4_t b = EVEN_ODD ? int4x8_to_bf16_exact(q[j]) : int4x8_to_bf16_natural(q[j]);
+      const u32x4_t b = EVEN_ODD ? int4x8_minus_zero_even_odd(q[j], zf) : int4x8_minus_zero(q[j], zf);
       dp = mfma16x16x32(a[j], b, dp);
-      dn = mfma16x16x32(a[j], nz, dn);
     }
     const float s = bf16_bits_to_f32(sraw);
-    acc[0] = __builtin_fmaf(s, dp[0] + dn[0], acc[0]);
-    acc[1] = __builtin_fmaf(s, dp[1] + dn[1], acc[1]);
-    acc[2] = __builtin_fmaf(s, dp[2] + dn[2], acc[2]);
-    acc[3] = __builtin_fmaf(s, dp[3] + dn[3], acc[3]);
+    acc[0] = __builtin_fmaf(s, dp[0], acc[0]);
+    acc[1] = __builtin_fmaf(s, dp[1], acc[1]);
+    acc[2] = __builtin_fmaf(s, dp[2], acc[2]);
+    acc[3] = __builtin_fmaf(s, dp[3], acc[3]);
   } else if constexpr (is_int4(FMT)) {
     const float s = bf16_bits_to_f32(sraw);
     const float zf = (float)zraw;
@@ -796,21 +794,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(SkinnyGro
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[j] = src[j];
       if constexpr (is_int4_g128(FMT)) {
-        // codes exact (A is stored in the decoder's k order); the zero point
-        // goes through a second accumulator with the same rounding sequence,
-        // so a k-block whose codes all equal it cancels to exactly 0
+        // code - zero exact (in the even / odd k order A is stored in), the
+        // group scale on the k-block's sum
         const int gi = nl * groups + kb;
         const float s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
-        const u32x4_t nz = int4_neg_zero(has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero);
+        const float zf = (float)(has_zeros(FMT) ? (uint32_t)zb[gi] : kSymZero);
         f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t dn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dp = mfma16x16x32(a[j], int4x8_to_bf16_exact(T.q[u][j]), dp);
-          dn = mfma16x16x32(a[j], nz, dn);
-        }
+        for (int j = 0; j < 4; ++j) dp = mfma16x16x32(a[j], int4x8_minus_zero_even_odd(T.q[u][j], zf), dp);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(s, dp[i] + dn[i], acc[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(s, dp[i], acc[i]);
       } else if constexpr (FMT == kNvfp4) {
         const uint32_t sraw = *reinterpret_cast<const uint16_t*>(sb + nl * groups + 2 * c);
         const float s0 = e4m3_magnitude(sraw & 0xFFu);
