@@ -43,7 +43,10 @@
  *   W       bf16 (N, K)                     16-byte aligned (dequant output)
  * Shapes: M, N >= 0 (a zero extent is a valid call that enqueues nothing and
  * checks no pointer);
- * 0 < K <= 2^22, K % 32 == 0 (16-byte weight rows); M, N < 2^31.  Groups
+ * 0 < K <= 2^22, K % 16 == 0; M, N < 2^31.  K an odd multiple of 16 (rows of
+ * K/2 bytes only 8-byte aligned: the NVFP4 layout of page "Matmul2dFp4" with
+ * its (N, ceil(K/16)) scales) runs a separate, simpler kernel
+ * (W4A16_PATH_RAGGED) for every format, M and entry point.  Groups
  * start at k = 0 and run along K; when K is not a multiple of the group (int4
  * with groups of 128 or 64), the last group of each row is the shorter rest
  * and has its own scale (and zero), hence ceil(K/G) of them per row.
@@ -103,11 +106,14 @@ extern "C" {
 #define W4A16_PATH_TILED 0x2000
 #define W4A16_PATH_MID 0x3000
 #define W4A16_PATH_MASK 0x3000
+/* returned by w4a16_gemm_path (never a flag): the kernel for K % 32 == 16,
+ * which runs whatever PATH flag is given */
+#define W4A16_PATH_RAGGED 0x4000
 
 /* ---- status codes --------------------------------------------------------- */
 #define W4A16_OK 0
 #define W4A16_ERR_FORMAT (-1) /* unknown format or flag bits                 */
-#define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 32 != 0, M or N
+#define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 16 != 0, M or N
                                  >= 2^31, or K > 2^22                       */
 #define W4A16_ERR_NULL (-3)   /* a required pointer is NULL, or zeros is
                                  non-NULL for a format without zeros
@@ -211,7 +217,7 @@ typedef struct w4a16_batch_item {
   const void* zeros;  /* uint8 zeros for the int4 formats with zeros, else NULL */
   void* C;            /* (M, N) device array, bf16 or fp32                    */
   int64_t N;          /* output columns (weight rows), 0 <= N < 2^31          */
-  int64_t K;          /* inputs, 0 < K <= 2^22, K % 32 == 0                   */
+  int64_t K;          /* inputs, 0 < K <= 2^22, K % 16 == 0                   */
 } w4a16_batch_item;
 int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item* items,
                        void* stream);
@@ -224,8 +230,9 @@ int w4a16_dequant(int format, const void* packed, const void* scales,
                   const void* zeros, void* W, int64_t N, int64_t K, void* stream);
 
 /* Which kernel w4a16_gemm would launch for these arguments, without launching:
- * returns W4A16_PATH_SKINNY, W4A16_PATH_MID or W4A16_PATH_TILED, or a
- * negative status if the format / shape would be rejected.  Host-only. */
+ * returns W4A16_PATH_SKINNY, W4A16_PATH_MID, W4A16_PATH_TILED or
+ * W4A16_PATH_RAGGED, or a negative status if the format / shape would be
+ * rejected.  Host-only. */
 int w4a16_gemm_path(int format, int64_t M, int64_t N, int64_t K);
 
 /* Static, NUL-terminated description of a status code. */

@@ -97,6 +97,10 @@ def test_path_choice():
     assert w4.gemm_path(w4.INT4_G128, 1, 64, 128, "tiled") == "tiled"
     assert w4.gemm_path(w4.NVFP4, 1, 64, 128, "mid") == "mid"
     assert w4.gemm_path(w4.NVFP4, 4096, 64, 128, "mid") == "mid"
+    # K an odd multiple of 16: the ragged-K kernel, whatever the path flag
+    assert w4.gemm_path(w4.NVFP4, 1, 64, 48) == "ragged"
+    assert w4.gemm_path(w4.INT4_G128, 4096, 8192, 3088, "tiled") == "ragged"
+    assert w4.gemm_path(w4.MXFP4, 16, 64, 80, "skinny") == "ragged"
 
 
 # fake, aligned device addresses: every call below fails validation (or is a
@@ -110,16 +114,16 @@ def _gemm(fmt, A=PA, B=PB, S=PS, Z=PZ, C=PC, M=16, N=64, K=128):
 
 @pytest.mark.parametrize("fmt,M,N,K,expect", [
     (6, 16, 64, 128, w4.ERR_FORMAT),                          # unknown format
-    (w4.INT4_SYM, 16, 64, 100, w4.ERR_SHAPE),                 # K % 32
-    (w4.INT4_G64, 16, 64, 80, w4.ERR_SHAPE),                  # K % 32 (K % 64 may be 32)
-    (w4.INT4_G32, 16, 64, 48, w4.ERR_SHAPE),                  # K % 32
+    (w4.INT4_SYM, 16, 64, 100, w4.ERR_SHAPE),                 # K % 16
+    (w4.INT4_G64, 16, 64, 88, w4.ERR_SHAPE),                  # K % 16
+    (w4.INT4_G32, 16, 64, 40, w4.ERR_SHAPE),                  # K % 16
     (w4.INT4_G128 | 0x4000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
     (w4.INT4_G128 | 0x8000, 16, 64, 128, w4.ERR_FORMAT),      # unknown flag
     (w4.INT4_G128, -1, 64, 128, w4.ERR_SHAPE),
     (w4.INT4_G128, 16, -5, 128, w4.ERR_SHAPE),
     (w4.INT4_G128, 16, 64, 0, w4.ERR_SHAPE),
-    (w4.INT4_G128, 16, 64, 112, w4.ERR_SHAPE),                # K % 32 (K % 128 may be 32 .. 96)
-    (w4.NVFP4, 16, 64, 48, w4.ERR_SHAPE),                     # K % 32 for 16-byte rows
+    (w4.INT4_G128, 16, 64, 104, w4.ERR_SHAPE),                # K % 16
+    (w4.NVFP4, 16, 64, 24, w4.ERR_SHAPE),                     # K % 16 (a whole NVFP4 block)
     (w4.MXFP4, 16, 64, 2 ** 22 + 32, w4.ERR_SHAPE),
     (w4.MXFP4, 2 ** 31, 64, 64, w4.ERR_SHAPE),
 ])
@@ -198,11 +202,11 @@ def test_gemm_ex_validation_order_and_noops():
 def test_dequant_rejects_bad_arguments():
     lib = w4.load_library()
     assert lib.w4a16_dequant(w4.INT4_G128 | w4.OUT_F32, PB, PS, PZ, PC, 4, 128, None) == w4.ERR_FORMAT
-    assert lib.w4a16_dequant(w4.INT4_G128, PB, PS, PZ, PC, 4, 48, None) == w4.ERR_SHAPE
+    assert lib.w4a16_dequant(w4.INT4_G128, PB, PS, PZ, PC, 4, 40, None) == w4.ERR_SHAPE
     assert lib.w4a16_dequant(w4.INT4_G128, PB, PS, None, PC, 4, 128, None) == w4.ERR_NULL
     assert lib.w4a16_dequant(w4.MXFP4, PB, PS, PZ, PC, 4, 64, None) == w4.ERR_NULL
     assert lib.w4a16_dequant(w4.INT4_SYM, PB, PS, PZ, PC, 4, 128, None) == w4.ERR_NULL
-    assert lib.w4a16_dequant(w4.INT4_SYM, PB, PS, None, PC, 4, 80, None) == w4.ERR_SHAPE
+    assert lib.w4a16_dequant(w4.INT4_SYM, PB, PS, None, PC, 4, 88, None) == w4.ERR_SHAPE
     assert lib.w4a16_dequant(6, PB, PS, None, PC, 4, 128, None) == w4.ERR_FORMAT
     assert lib.w4a16_dequant(w4.MXFP4, PB, PS, None, ctypes.c_void_p(0x100008), 4, 64,
                              None) == w4.ERR_ALIGN
@@ -238,13 +242,13 @@ def _grouped(fmt, count=3, N=(64, 32, 48), M=1, K=128, A=PA, packed=True, scales
 @pytest.mark.parametrize("kw,expect", [
     (dict(fmt=6), w4.ERR_FORMAT),
     (dict(fmt=w4.INT4_SYM, zeros=True), w4.ERR_NULL),          # symmetric int4 takes no zeros
-    (dict(fmt=w4.INT4_SYM, K=200), w4.ERR_SHAPE),              # K % 32
+    (dict(fmt=w4.INT4_SYM, K=200), w4.ERR_SHAPE),              # K % 16
     (dict(fmt=w4.INT4_G128, count=0), w4.ERR_SHAPE),
-    (dict(fmt=w4.INT4_G64, K=80), w4.ERR_SHAPE),               # K % 32
+    (dict(fmt=w4.INT4_G64, K=88), w4.ERR_SHAPE),               # K % 16
     (dict(fmt=w4.INT4_G32, zeros=False), w4.ERR_NULL),
     (dict(fmt=w4.INT4_G128, count=9), w4.ERR_SHAPE),
-    (dict(fmt=w4.INT4_G128, K=112), w4.ERR_SHAPE),             # K % 32
-    (dict(fmt=w4.NVFP4, K=48), w4.ERR_SHAPE),                  # K % 32
+    (dict(fmt=w4.INT4_G128, K=104), w4.ERR_SHAPE),             # K % 16
+    (dict(fmt=w4.NVFP4, K=40), w4.ERR_SHAPE),                  # K % 16
     (dict(fmt=w4.NVFP4, N=(64, -1, 32)), w4.ERR_SHAPE),
     (dict(fmt=w4.NVFP4, Nnull=True), w4.ERR_NULL),
     (dict(fmt=w4.NVFP4, A=None), w4.ERR_NULL),
@@ -298,7 +302,7 @@ def _batched(fmt, n=3, M=1, items=None, bad=None, count=None):
     (dict(fmt=w4.MXFP4, count=-1), w4.ERR_SHAPE),
     (dict(fmt=w4.MXFP4, M=-1), w4.ERR_SHAPE),
     (dict(fmt=w4.MXFP4, items="null"), w4.ERR_NULL),
-    (dict(fmt=w4.NVFP4, bad=(1, "K", 48)), w4.ERR_SHAPE),      # K % 32
+    (dict(fmt=w4.NVFP4, bad=(1, "K", 40)), w4.ERR_SHAPE),      # K % 16
     (dict(fmt=w4.NVFP4, bad=(2, "K", 0)), w4.ERR_SHAPE),
     (dict(fmt=w4.NVFP4, bad=(0, "N", -1)), w4.ERR_SHAPE),
     (dict(fmt=w4.NVFP4, bad=(1, "A", None)), w4.ERR_NULL),

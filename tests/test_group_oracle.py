@@ -94,3 +94,21 @@ def test_ragged_last_group_is_the_shorter_rest():
     case = inputs.make_case(oracle.INT4_G64, 0, 2, 96, seed=15)
     with pytest.raises(ValueError):
         oracle.dequant(oracle.INT4_G64, case.packed, case.scales[:, :1], case.zeros[:, :1], 2, 96)
+
+@pytest.mark.parametrize("fmt", [oracle.INT4_G128, oracle.NVFP4, oracle.MXFP4, oracle.INT4_G32,
+                                 oracle.INT4_G64, oracle.INT4_SYM])
+def test_k_odd_multiple_of_16_is_a_prefix(fmt):
+    """K = 16 * odd (the NVFP4 layout's (N, ceil(K/16)) scales): a row of K
+    codes dequantises to the first K weights of the same row extended by 16
+    codes, with the same scales (and zeros) -- the short last group takes its
+    own group's scale, and nothing else moves."""
+    N, K = 5, 208   # 13 * 16
+    G = oracle.GROUP[fmt]
+    big = inputs.make_case(fmt, 1, N, K + 16, seed=7)
+    ng = (K + G - 1) // G
+    packed = big.packed[:, :K // 2].copy()
+    scales = big.scales[:, :ng].copy()
+    zeros = None if big.zeros is None else big.zeros[:, :ng].copy()
+    w, wb = oracle.dequant(fmt, packed, scales, zeros, N, K)
+    wbig, wbbig = oracle.dequant(fmt, big.packed, big.scales, big.zeros, N, K + 16)
+    assert np.array_equal(w, wbig[:, :K]) and np.array_equal(wb, wbbig[:, :K])

@@ -5,7 +5,7 @@
 accumulation.  Formats: ``INT4_G128`` (bf16 scale + uint8 zero per 128 k;
 ``INT4_G32`` / ``INT4_G64``: the same per 32 / 64 k; ``INT4_SYM``: bf16 scale
 per 128 k, zero point 8, no zero array), ``NVFP4`` (e2m1 codes, e4m3 scale per
-16 k), ``MXFP4`` (e2m1 codes, e8m0 scale per 32 k).  K is a multiple of 32;
+16 k), ``MXFP4`` (e2m1 codes, e8m0 scale per 32 k).  K is a multiple of 16;
 the last group of a row may be shorter than the group size.
 
 This module only marshals arguments to the C ABI declared in
@@ -30,6 +30,7 @@ INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64, INT4_SYM)  # bf16 scales
 ZERO_FORMATS = (INT4_G128, INT4_G32, INT4_G64)  # with a zero array (symmetric int4: zero point 8)
 OUT_BF16, OUT_F32 = 0x000, 0x100
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_MID = 0x0000, 0x1000, 0x2000, 0x3000
+PATH_RAGGED = 0x4000  # reported by gemm_path for K % 32 == 16 (never a flag)
 PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "mid": PATH_MID, "tiled": PATH_TILED}
 
 OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP, ERR_EPILOGUE = 0, -1, -2, -3, -4, -5, -6
@@ -105,11 +106,12 @@ def version() -> int:
 
 
 def gemm_path(fmt: int, M: int, N: int, K: int, path: str = "auto") -> str:
-    """Name of the kernel w4a16_gemm would launch ('skinny' or 'tiled')."""
+    """Name of the kernel w4a16_gemm would launch: 'skinny', 'mid', 'tiled' or
+    'ragged' (K % 32 == 16, whatever the path)."""
     rc = load_library().w4a16_gemm_path(int(fmt) | PATHS[path], M, N, K)
     if rc < 0:
         raise W4A16Error(rc, "w4a16_gemm_path")
-    return {PATH_SKINNY: "skinny", PATH_MID: "mid", PATH_TILED: "tiled"}[rc]
+    return {PATH_SKINNY: "skinny", PATH_MID: "mid", PATH_TILED: "tiled", PATH_RAGGED: "ragged"}[rc]
 
 
 # ---- argument checks (host side, before any pointer reaches the library) ----
@@ -141,8 +143,8 @@ def _check_weights(fmt, packed, scales, zeros, N, K, device):
     if fmt not in GROUP:
         raise ValueError(f"unknown format {fmt}")
     G = GROUP[fmt]
-    if K % 32:
-        raise ValueError(f"K={K} must be a multiple of 32")
+    if K % 16:
+        raise ValueError(f"K={K} must be a multiple of 16")
     groups = (K + G - 1) // G  # the last group may be shorter
     _check(packed, "packed", (N, K // 2), 1, device)
     _check(scales, "scales", (N, groups), 2 if fmt in INT4_FORMATS else 1, device)

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.cpp", "dequant.hip", "skinny.hip", "mid.hip", "tiled.hip"]
+SOURCES = ["api.cpp", "dequant.hip", "skinny.hip", "mid.hip", "tiled.hip", "ragged.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -33,7 +33,7 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
     return W4A16_ERR_FORMAT;
   }
   if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_SHAPE;
-  if (K % 32 != 0) return W4A16_ERR_SHAPE;  // the last group may be shorter than G
+  if (K % 16 != 0) return W4A16_ERR_SHAPE;  // the last group may be shorter than G
   if (M >= kMaxDim || N >= kMaxDim || K > kMaxK) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
@@ -52,7 +52,8 @@ int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_f
 // kernel when it would have fewer (narrow matrices: N = 1024, M = 64: 4.8 /
 // 15 / 51); with 256 or more large tiles the tiled kernel, except at M <= 48
 // (LM head 128256 x 3072, M = 32: 242 / 144 / 219).  N: the widest matrix.
-int choose_path(int format, int64_t M, int64_t N) {
+int choose_path(int format, int64_t M, int64_t N, int64_t K) {
+  if (K % 32 != 0) return W4A16_PATH_RAGGED;  // the only kernel for rows 8-byte aligned
   const int forced = format & W4A16_PATH_MASK;
   if (forced) return forced;
   if (M <= 16) return W4A16_PATH_SKINNY;
@@ -66,6 +67,7 @@ int choose_path(int format, int64_t M, int64_t N) {
 }
 
 hipError_t launch_path(int path, const w4a16::GemmArgs& a) {
+  if (path == W4A16_PATH_RAGGED) return w4a16::launch_ragged(a);
   if (path == W4A16_PATH_SKINNY) return w4a16::launch_skinny(a);
   if (path == W4A16_PATH_MID) return w4a16::launch_mid(a);
   return w4a16::launch_tiled(a);
@@ -82,7 +84,7 @@ const char* w4a16_strerror(int status) {
     case W4A16_OK: return "success";
     case W4A16_ERR_FORMAT: return "unknown weight format or flag bits";
     case W4A16_ERR_SHAPE:
-      return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^22 and K % 32 == 0 (and 1 <= count "
+      return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^22 and K % 16 == 0 (and 1 <= count "
              "<= W4A16_MAX_GROUP for a group)";
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for a format without zeros";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
@@ -97,7 +99,7 @@ const char* w4a16_strerror(int status) {
 int w4a16_gemm_path(int format, int64_t M, int64_t N, int64_t K) {
   const int rc = check_format_shape(format, M, N, K, true);
   if (rc != W4A16_OK) return rc;
-  return choose_path(format, M, N);
+  return choose_path(format, M, N, K);
 }
 
 int w4a16_gemm(int format, const void* A, const void* packed, const void* scales,
@@ -153,7 +155,7 @@ int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* sca
   a.N = N;
   a.K = K;
   a.stream = static_cast<hipStream_t>(stream);
-  return launch_path(choose_path(format, M, N), a) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+  return launch_path(choose_path(format, M, N, K), a) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
 int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* packed,
@@ -184,7 +186,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
 
   int64_t max_n = 0;
   for (int i = 0; i < count; ++i) max_n = N[i] > max_n ? N[i] : max_n;
-  const int path = choose_path(format, M, max_n);
+  const int path = choose_path(format, M, max_n, K);
   if (path == W4A16_PATH_SKINNY) {
     w4a16::GroupedArgs g = {};
     g.fmt = fmt;
@@ -260,9 +262,9 @@ int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item*
     a.N = it.N;
     a.K = it.K;
     a.stream = static_cast<hipStream_t>(stream);
-    return launch_path(choose_path(fmt, M, it.N), a);
+    return launch_path(choose_path(fmt, M, it.N, it.K), a);
   };
-  if (choose_path(fmt, M, 1) != W4A16_PATH_SKINNY) {
+  if (choose_path(fmt, M, 1, 32) != W4A16_PATH_SKINNY) {
     // larger M: every item is its own mid or tiled launch
     for (int i = 0; i < count; ++i)
       if (items[i].N > 0 && single(items[i]) != hipSuccess) return W4A16_ERR_HIP;
@@ -275,8 +277,14 @@ int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item*
   // output equals w4a16_gemm's for it, bit for bit.
   std::vector<int> order;
   order.reserve((size_t)count);
-  for (int i = 0; i < count; ++i)
-    if (items[i].N > 0) order.push_back(i);
+  for (int i = 0; i < count; ++i) {
+    if (items[i].N == 0) continue;
+    if (items[i].K % 32 != 0) {  // the ragged-K kernel, one launch per item
+      if (single(items[i]) != hipSuccess) return W4A16_ERR_HIP;
+      continue;
+    }
+    order.push_back(i);
+  }
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
     return items[x].K != items[y].K ? items[x].K < items[y].K : items[x].N < items[y].N;
   });

@@ -88,4 +88,8 @@ hipError_t launch_mid(const GemmArgs& a);
 // large M: LDS-staged tiles, decode into MFMA B fragments.
 hipError_t launch_tiled(const GemmArgs& a);
 
+// K an odd multiple of 16 (rows of K/2 bytes only 8-byte aligned), any M:
+// 4-byte weight loads, one MFMA per 32-code step.
+hipError_t launch_ragged(const GemmArgs& a);
+
 }  // namespace w4a16
