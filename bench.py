@@ -11,17 +11,18 @@ metric, each with its own roofline fraction: the tiny int4 GEMM (M = 16), the
 NVFP4 M = 16 GEMM, the compute-bound MXFP4 M = 4096 GEMM (TFLOP/s) and the
 197-GEMV decode chain of a 3B decoder.
 
-Timing.  Warm-up: the W requested steps, then whole passes over every
-rotating weight copy until at least two passes and 50 ms of GPU work have run
-(first touch of each copy, clock ramp).  Then a spin kernel fills the stream
-so that the K timed launches run back to back, with about 1 ms of untimed
-steps queued right behind it (the spin idles the GPU, whose clocks would
-otherwise still be ramping for the first timed steps); HIP events on the
-launch stream bracket the K steps (from 500 steps on they split them into 5
-equal repeats, whose median per-step time is reported beside the mean).  `ms_per_step` = total / K, and
-the roofline's `achieved` uses the same mean duration per launch.  The decode
-chain is captured once as a HIP graph and replayed (its eager time and the
-time of 197 single launches are reported too).
+Timing.  The K timed steps are captured into one HIP graph (a decode step is
+graph-captured in serving) and replayed once between two HIP events on the
+launch stream, after a warm-up of the W requested steps and whole passes over
+every rotating weight copy (first touch of each copy, clock ramp), a replay,
+and about 1 ms of untimed replays queued behind a queue-fill spin (the spin
+idles the GPU).  `ms_per_step` = the replay's time / K, and the roofline's
+`achieved` uses the same mean duration per launch.  The same K steps are also
+timed as eager launches (a spin kernel first fills the stream so that they run
+back to back; from 500 steps on, the events split them into 5 repeats whose
+median is reported) and reported as eager_ms_per_step.  The decode chain is
+one batched call per step, timed the same way, with its layer-grouped and
+single-launch forms beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -88,9 +89,10 @@ KERNEL_SOURCES = {
 
 
 def traffic_from_profile(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    profiles/traffic_<kernel>_<workload>.txt (lines "key value"), or None when
-    there is none or the kernel's source changed since the counters were taken."""
+    """HBM bytes per launch (per pass for the decode chain) from the committed
+    rocprofv3 counter summary profiles/traffic_<kernel>_<workload>.txt (lines
+    "key value"), or None when there is none or the kernel's source changed
+    since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
@@ -102,7 +104,8 @@ def traffic_from_profile(kernel, workload):
                 rec[parts[0]] = parts[1]
     if rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
         return None
-    return int(float(rec["hbm_bytes_per_launch"]))
+    # per launch, or per pass for the decode chain (one batched call)
+    return int(float(rec.get("hbm_bytes_per_launch", rec.get("hbm_bytes_per_step"))))
 
 
 def cpu_model():
@@ -290,6 +293,37 @@ def main():
         per = [ev[j].elapsed_time(ev[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(parts)]
         return ev[0].elapsed_time(ev[parts]), per
 
+    def timed_graph(calls_per_step, steps, warmup):
+        """The same steps captured into ONE HIP graph of exactly `steps`
+        steps (step i runs calls_per_step[i % len]); after the eager warm-up
+        and a replay, the graph is replayed untimed (about 1 ms of work,
+        behind the queue-fill spin) and then once between two HIP events.
+        Returns the timed replay's ms."""
+        nrot = len(calls_per_step)
+        for i in range(max(warmup, nrot)):
+            for c in calls_per_step[i % nrot]:
+                c()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                for c in calls_per_step[i % nrot]:
+                    c()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        once_ms = (time.perf_counter() - t0) * 1e3
+        pre = max(1, min(200, math.ceil(1.0 / max(once_ms, 1e-3))))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(cyc_per_ms * (0.05 * pre + 5.0)))
+        for _ in range(pre):
+            g.replay()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
     def measure_single(fmt, M, N, K, out, steps, warmup, epilogue=None):
         """One GEMM workload timed over `steps` launches that rotate over
         enough distinct weight copies (>= 1 GiB together) that every launch
@@ -312,13 +346,14 @@ def main():
             sr = s if r == 0 else s.clone()
             zr = z if (r == 0 or z is None) else z.clone()
             calls.append([w4.PreparedGemm(fmt, A, pr, sr, zr, C, path=args.path, **epi)])
-        total, per = timed(calls, steps, warmup)
+        eager, per = timed(calls, steps, warmup)
+        total = timed_graph(calls, steps, warmup)
         kernel = calls[0][0].kernel
         del calls, C
         progress(f"{w4.FORMAT_NAMES[fmt]} M={M} N={N} K={K}: {total / steps * 1e3:.3f} us per launch "
-                 f"({kernel}, {steps} steps)")
-        return {"case": case, "ms": total / steps, "median_ms": statistics.median(per),
-                "copies": copies, "kernel": kernel}
+                 f"(graph), {eager / steps * 1e3:.3f} eager ({kernel}, {steps} steps)")
+        return {"case": case, "ms": total / steps, "eager_ms": eager / steps,
+                "eager_median_ms": statistics.median(per), "copies": copies, "kernel": kernel}
 
     def single_entry(name, steps, warmup):
         fmt, M, N, K, out = WORKLOADS[name]
@@ -326,7 +361,9 @@ def main():
         wbytes, tbytes = algorithmic_bytes(fmt, M, N, K, out)
         e = {"workload": name, "format": w4.FORMAT_NAMES[fmt], "M": M, "N": N, "K": K, "out": out,
              "kernel": r["kernel"], "steps": steps, "weight_copies": r["copies"],
-             "ms_per_step": round(r["ms"], 6), "median_ms_per_step": round(r["median_ms"], 6)}
+             "timing": "hip_graph_replay", "ms_per_step": round(r["ms"], 6),
+             "eager_ms_per_step": round(r["eager_ms"], 6),
+             "eager_median_ms_per_step": round(r["eager_median_ms"], 6)}
         if M > 16:
             e["tflops"] = round(2.0 * M * N * K / (r["ms"] * 1e-3) / 1e12, 1)
             e["roofline"] = mfma_roofline(2 * M * N * K, r["ms"], r["kernel"], name)
@@ -370,17 +407,18 @@ def main():
         blaunches = batched_launches(shapes)
         esteps = max(1, steps // 10)
         eager_ms = timed([[bcall]], esteps, warmup)[0] / esteps
-        layer_ms = timed([gcalls], steps, warmup, graph=True)[0] / steps
-        ungrouped_ms = timed([calls], steps, warmup, graph=True)[0] / steps if ungrouped else None
-        total_ms, per = timed([[bcall]], steps, warmup, graph=True)
+        lsteps = max(1, min(steps, 50))  # graphs of 113 / 197 launches per step
+        layer_ms = timed_graph([gcalls], lsteps, warmup) / lsteps
+        ungrouped_ms = timed_graph([calls], lsteps, warmup) / lsteps if ungrouped else None
+        total_ms = timed_graph([[bcall]], steps, warmup)
         ms = total_ms / steps
+        per = [ms]
         progress(f"decode chain: {ms * 1e3:.1f} us per pass (batched, graph), eager {eager_ms * 1e3:.1f} us, "
                  f"layer-grouped {layer_ms * 1e3:.1f} us")
         e = {"workload": CHAIN, "matrices": len(calls), "M": 1, "format": "int4_g128", "out": "bf16",
              "call": "w4a16_gemm_batched", "launches_per_step": blaunches,
              "grouping": "independent GEMVs: one launch per (K, N) and 32 matrices",
              "timing": "hip_graph_replay", "steps": steps, "ms_per_step": round(ms, 6),
-             "median_ms_per_step": round(statistics.median(per), 6),
              "eager_ms_per_step": round(eager_ms, 4),
              "layer_grouped_launches_per_step": len(gcalls),
              "layer_grouping": "per layer [q,k,v] [o] [gate,up] [down], then [lm_head] (w4a16_gemm_grouped)",
@@ -410,7 +448,8 @@ def main():
             tbytes += N * 2 + M * N * (4 if out == "f32" else 2)
         config = {"workload": args.workload, "format": w4.FORMAT_NAMES[fmt], "M": M, "N": N, "K": K,
                   "out": out, "weight_copies": r["copies"], "kernel": r["kernel"],
-                  "median_ms_per_step": round(r["median_ms"], 6)}
+                  "timing": "hip_graph_replay", "eager_ms_per_step": round(r["eager_ms"], 6),
+                  "eager_median_ms_per_step": round(r["eager_median_ms"], 6)}
         if args.epilogue:
             config["epilogue"] = {"bias": "bf16", "residual": out, "beta": 1.0,
                                   "activation": args.epilogue}
