@@ -163,6 +163,9 @@ def main():
     ap.add_argument("--epilogue", default=None, choices=["none", "relu", "silu", "gelu_tanh"],
                     help="single-GEMM workloads: fuse a bf16 bias, a residual (beta = 1) and this "
                          "activation into the GEMM (w4a16_gemm_ex); their bytes count as traffic")
+    ap.add_argument("--prepacked", action="store_true",
+                    help="time the weights in the library's prepacked layout (w4a16_prepack, untimed; "
+                         "K % 128 == 0) instead of the row-major one")
     ap.add_argument("--copies", type=int, default=0,
                     help="distinct weight copies to rotate over (0: enough for >= 1 GiB)")
     ap.add_argument("--side-steps", type=int, default=300,
@@ -343,6 +346,8 @@ def main():
         calls = []
         for r in range(copies):
             pr = p if r == 0 else p.clone()
+            if args.prepacked:
+                pr = w4.prepack(pr)
             sr = s if r == 0 else s.clone()
             zr = z if (r == 0 or z is None) else z.clone()
             calls.append([w4.PreparedGemm(fmt, A, pr, sr, zr, C, path=args.path, **epi)])
@@ -387,6 +392,8 @@ def main():
         for i, (_, n, k) in enumerate(shapes):
             case = inputs.make_case(0, 1, n, k, inputs.chain_seed(0, i))
             A, p, s, z = to_dev(case)
+            if args.prepacked:
+                p = w4.prepack(p)
             dev_w.append((p, s, z))
             dev_a.append(A)
             calls.append(w4.PreparedGemm(0, A, p, s, z, out[:, :n], path=args.path))
@@ -417,6 +424,7 @@ def main():
                  f"layer-grouped {layer_ms * 1e3:.1f} us")
         e = {"workload": CHAIN, "matrices": len(calls), "M": 1, "format": "int4_g128", "out": "bf16",
              "call": "w4a16_gemm_batched", "launches_per_step": blaunches,
+             "weights": "prepacked" if args.prepacked else "row-major",
              "grouping": "independent GEMVs: one launch per (K, N) and 32 matrices",
              "timing": "hip_graph_replay", "steps": steps, "ms_per_step": round(ms, 6),
              "eager_ms_per_step": round(eager_ms, 4),
@@ -447,6 +455,7 @@ def main():
         if args.epilogue:  # + bias (bf16) + residual (C's dtype)
             tbytes += N * 2 + M * N * (4 if out == "f32" else 2)
         config = {"workload": args.workload, "format": w4.FORMAT_NAMES[fmt], "M": M, "N": N, "K": K,
+                  "weights": "prepacked" if args.prepacked else "row-major",
                   "out": out, "weight_copies": r["copies"], "kernel": r["kernel"],
                   "timing": "hip_graph_replay", "eager_ms_per_step": round(r["eager_ms"], 6),
                   "eager_median_ms_per_step": round(r["eager_median_ms"], 6)}

@@ -33,7 +33,8 @@
  * Memory: every pointer is a DEVICE pointer owned by the caller; the library
  * never allocates, frees or keeps them.  All arrays are row-major and dense:
  *   A       bf16  (M, K)                    16-byte aligned
- *   packed  uint8 (N, K/2)                  16-byte aligned
+ *   packed  uint8 (N, K/2)                  16-byte aligned (or prepacked:
+ *           see w4a16_prepack)
  *   scales  int4: bf16 (N, ceil(K/G)), G = 128 / 32 / 64 (128 for INT4_SYM)   2-byte aligned
  *           NVFP4: e4m3 bytes (N, K/16)     2-byte aligned
  *           MXFP4: e8m0 bytes (N, K/32)
@@ -90,6 +91,9 @@ extern "C" {
 
 #define W4A16_OUT_BF16 0x000 /* C is bf16, rounded to nearest even (default) */
 #define W4A16_OUT_F32 0x100  /* C is fp32                                    */
+/* `packed` is in the prepacked layout (see w4a16_prepack), K % 128 == 0; taken
+ * by every GEMM entry point, w4a16_dequant and w4a16_gemm_path */
+#define W4A16_PREPACKED 0x400
 
 /* Kernel choice for w4a16_gemm.  AUTO picks the skinny (split-K, register
  * decode) kernel for M <= 16.  Above that, while the LDS-tiled MFMA kernel
@@ -123,10 +127,11 @@ extern "C" {
 #define W4A16_ERR_EPILOGUE (-6) /* unknown activation, nonzero reserved field,
                                    or a residual that overlaps C without
                                    being C                                  */
+#define W4A16_ERR_OVERLAP (-7)  /* w4a16_prepack's output overlaps its input */
 
 /* C = A . dequant(packed, scales, zeros)^T, accumulated in fp32.
  * format = W4A16_INT4_G128 | W4A16_NVFP4 | W4A16_MXFP4, optionally OR-ed with
- * W4A16_OUT_F32 and one W4A16_PATH_* flag.  C is fully overwritten.
+ * W4A16_OUT_F32, W4A16_PREPACKED and one W4A16_PATH_* flag.  C is fully overwritten.
  * Accuracy: |C - C_exact| <= 2e-3 * sum_k |A[m,k] W[n,k]| + 1e-6 per element,
  * plus 2^-8 |C_exact| when C is bf16 (C_exact: exact weights, exact sum). */
 int w4a16_gemm(int format, const void* A, const void* packed, const void* scales,
@@ -206,13 +211,13 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
  * read during the call only; every entry follows w4a16_gemm's layout,
  * alignment and zeros rules; entries with N == 0 are skipped and their
  * pointers not checked.  `format`: a weight format, optionally OR-ed with
- * W4A16_OUT_F32 (no W4A16_PATH_* flag).  count == 0 or M == 0 enqueues
+ * W4A16_OUT_F32 and W4A16_PREPACKED (no W4A16_PATH_* flag).  count == 0 or M == 0 enqueues
  * nothing.  Errors: as w4a16_gemm, every item is checked before anything is
  * enqueued (W4A16_ERR_SHAPE also for count < 0); a launch failure
  * (W4A16_ERR_HIP) may leave the call's earlier launches enqueued. */
 typedef struct w4a16_batch_item {
   const void* A;      /* bf16 (M, K) device array, 16-byte aligned            */
-  const void* packed; /* uint8 (N, K/2) device array, 16-byte aligned         */
+  const void* packed; /* uint8 (N, K/2) device array (or prepacked), 16-byte aligned */
   const void* scales; /* per the format, as for w4a16_gemm                    */
   const void* zeros;  /* uint8 zeros for the int4 formats with zeros, else NULL */
   void* C;            /* (M, N) device array, bf16 or fp32                    */
@@ -224,10 +229,36 @@ int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item*
 
 /* W = dequant(packed, scales, zeros) as bf16 (N, K): each weight's exact value
  * rounded once to nearest even (bit-exact; fp4 weights are exact in bf16 at
- * normal scale ranges).  `format` takes only the format bits.  A checking
- * path: the GEMM never materialises W. */
+ * normal scale ranges).  `format` takes the format bits and W4A16_PREPACKED.
+ * A checking path: the GEMM never materialises W. */
 int w4a16_dequant(int format, const void* packed, const void* scales,
                   const void* zeros, void* W, int64_t N, int64_t K, void* stream);
+
+/* ---- prepacked weights ------------------------------------------------------
+ * Page "megakernel_int4_weight_decode.py", contract section: weights may be
+ * repacked once, untimed, when the model is built -- interleaved, pre-ordered
+ * for the matrix instruction's fragments, with the scales in a stream of their
+ * own -- as long as no bf16 copy of the weights is materialised.  This
+ * library's repacking moves whole 16-byte pieces of a packed row (32 codes,
+ * nibble order unchanged) into the order in which the lanes of an MFMA
+ * 16x16x32 weight fragment read them; scales and zeros keep their layout (they
+ * already are arrays of their own, read once per group).  The prepacked array,
+ * of w4a16_prepacked_bytes(N, K) = ceil(N/16) * 16 * K/2 bytes, holds for
+ * t < ceil(N/16), b < K/128, l < 64, i < 16:
+ *     out[((t * (K/128) + b) * 64 + l) * 16 + i]
+ *         = packed[(16t + l % 16) * K/2 + 64 b + 16 (l / 16) + i]
+ * (zero for rows 16t + l % 16 >= N): tiles of 16 rows, and in a tile one
+ * 1-KB block per 128 codes, which a wave of the decode kernels loads as one
+ * contiguous kilobyte (the row-major layout spreads it over 16 rows).  Every
+ * entry point taking `packed` accepts this layout with W4A16_PREPACKED in
+ * `format` and gives bit-identical results to the row-major layout.
+ * Requires K % 128 == 0 (else W4A16_ERR_SHAPE); the prepacked array is
+ * 16-byte aligned like `packed`.
+ * w4a16_prepacked_bytes returns the size, or a negative status for a bad
+ * shape.  w4a16_prepack enqueues the reordering on `stream` (host-side
+ * checks as w4a16_gemm; `out` must not overlap `packed`: W4A16_ERR_OVERLAP). */
+int64_t w4a16_prepacked_bytes(int64_t N, int64_t K);
+int w4a16_prepack(const void* packed, void* out, int64_t N, int64_t K, void* stream);
 
 /* Which kernel w4a16_gemm would launch for these arguments, without launching:
  * returns W4A16_PATH_SKINNY, W4A16_PATH_MID, W4A16_PATH_TILED or

@@ -30,7 +30,8 @@ def test_library_exports_every_declared_function():
     lib = w4.load_library()
     names = _header_functions()
     assert set(names) == {"w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped", "w4a16_gemm_batched",
-                          "w4a16_dequant", "w4a16_gemm_path", "w4a16_strerror", "w4a16_version"}
+                          "w4a16_dequant", "w4a16_gemm_path", "w4a16_strerror", "w4a16_version",
+                          "w4a16_prepack", "w4a16_prepacked_bytes"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -43,10 +44,12 @@ def test_python_constants_match_header():
     assert d["W4A16_INT4_G32"] == w4.INT4_G32 and d["W4A16_INT4_G64"] == w4.INT4_G64
     assert d["W4A16_INT4_SYM"] == w4.INT4_SYM
     assert d["W4A16_OUT_F32"] == w4.OUT_F32
+    assert d["W4A16_PREPACKED"] == w4.PREPACKED
     assert d["W4A16_PATH_SKINNY"] == w4.PATH_SKINNY
     assert d["W4A16_PATH_TILED"] == w4.PATH_TILED
     assert d["W4A16_PATH_MID"] == w4.PATH_MID
-    for code in ("OK", "ERR_FORMAT", "ERR_SHAPE", "ERR_NULL", "ERR_ALIGN", "ERR_HIP", "ERR_EPILOGUE"):
+    for code in ("OK", "ERR_FORMAT", "ERR_SHAPE", "ERR_NULL", "ERR_ALIGN", "ERR_HIP", "ERR_EPILOGUE",
+                 "ERR_OVERLAP"):
         assert d["W4A16_" + code] == getattr(w4, code)
     assert d["W4A16_MAX_GROUP"] == w4.MAX_GROUP
     for name in ("NONE", "RELU", "SILU", "GELU_TANH"):
@@ -60,9 +63,9 @@ def test_epilogue_struct_layout():
 
 
 def test_version_and_strerror():
-    assert w4.version() == 105
+    assert w4.version() == 106
     for code in (w4.OK, w4.ERR_FORMAT, w4.ERR_SHAPE, w4.ERR_NULL, w4.ERR_ALIGN, w4.ERR_HIP,
-                 w4.ERR_EPILOGUE):
+                 w4.ERR_EPILOGUE, w4.ERR_OVERLAP):
         assert w4.strerror(code) != "unknown status"
     assert w4.strerror(12345) == "unknown status"
 
@@ -324,3 +327,48 @@ def test_batched_empty_calls_check_no_pointer():
     # an item with N = 0 is skipped unchecked; the others still are
     arr_ok = _batched(w4.NVFP4, n=1, bad=(0, "N", 0))
     assert arr_ok == w4.OK
+
+
+# ---- prepacked weights ------------------------------------------------------------
+
+def test_prepacked_bytes():
+    lib = w4.load_library()
+    assert lib.w4a16_prepacked_bytes(1, 128) == 16 * 64          # one 16-row tile, one 1-KB block
+    assert lib.w4a16_prepacked_bytes(16, 384) == 16 * 192
+    assert lib.w4a16_prepacked_bytes(17, 256) == 32 * 128        # two tiles, the second padded
+    assert lib.w4a16_prepacked_bytes(8192, 3072) == 8192 * 1536
+    assert lib.w4a16_prepacked_bytes(0, 128) == 0
+    assert lib.w4a16_prepacked_bytes(16, 64) == w4.ERR_SHAPE      # K % 128
+    assert lib.w4a16_prepacked_bytes(16, 160) == w4.ERR_SHAPE
+    assert lib.w4a16_prepacked_bytes(-1, 128) == w4.ERR_SHAPE
+    assert lib.w4a16_prepacked_bytes(16, 2 ** 22 + 128) == w4.ERR_SHAPE
+
+
+def test_prepack_host_checks():
+    lib = w4.load_library()
+    P, O = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)
+    assert lib.w4a16_prepack(P, O, 16, 64, None) == w4.ERR_SHAPE
+    assert lib.w4a16_prepack(P, O, -1, 128, None) == w4.ERR_SHAPE
+    assert lib.w4a16_prepack(None, O, 16, 128, None) == w4.ERR_NULL
+    assert lib.w4a16_prepack(P, None, 16, 128, None) == w4.ERR_NULL
+    assert lib.w4a16_prepack(ctypes.c_void_p(0x100008), O, 16, 128, None) == w4.ERR_ALIGN
+    assert lib.w4a16_prepack(P, ctypes.c_void_p(0x900004), 16, 128, None) == w4.ERR_ALIGN
+    # 16 x 64 bytes from 0x100000: an output starting inside (or ending inside) overlaps
+    assert lib.w4a16_prepack(P, ctypes.c_void_p(0x100200), 16, 128, None) == w4.ERR_OVERLAP
+    assert lib.w4a16_prepack(P, ctypes.c_void_p(0x100000 - 512), 16, 128, None) == w4.ERR_OVERLAP
+    assert lib.w4a16_prepack(None, None, 0, 128, None) == w4.OK  # nothing to move
+
+
+def test_prepacked_flag_checks():
+    lib = w4.load_library()
+    pre = w4.PREPACKED
+    # K % 128 for every entry point that takes the flag
+    assert _gemm(w4.INT4_G128 | pre, K=192) == w4.ERR_SHAPE
+    assert _gemm(w4.INT4_G128 | pre, K=256, M=0) == w4.OK
+    assert lib.w4a16_gemm_path(w4.MXFP4 | pre, 1, 64, 96) == w4.ERR_SHAPE
+    for M, N, K in [(1, 8192, 3072), (64, 2048, 3072), (4096, 8192, 3072), (300, 256, 512)]:
+        assert lib.w4a16_gemm_path(w4.MXFP4 | pre, M, N, K) == lib.w4a16_gemm_path(w4.MXFP4, M, N, K)
+    assert lib.w4a16_dequant(w4.NVFP4 | pre, PB, PS, None, PA, 64, 96, None) == w4.ERR_SHAPE
+    assert lib.w4a16_dequant(w4.NVFP4 | pre | w4.OUT_F32, PB, PS, None, PA, 64, 128, None) == w4.ERR_FORMAT
+    item = w4.BatchItem(PA.value, PB.value, PS.value, None, PC.value, 64, 160)
+    assert lib.w4a16_gemm_batched(w4.MXFP4 | pre, 1, 1, ctypes.byref(item), None) == w4.ERR_SHAPE

@@ -29,11 +29,12 @@ FORMAT_NAMES = {INT4_G128: "int4_g128", NVFP4: "nvfp4", MXFP4: "mxfp4",
 INT4_FORMATS = (INT4_G128, INT4_G32, INT4_G64, INT4_SYM)  # bf16 scales
 ZERO_FORMATS = (INT4_G128, INT4_G32, INT4_G64)  # with a zero array (symmetric int4: zero point 8)
 OUT_BF16, OUT_F32 = 0x000, 0x100
+PREPACKED = 0x400  # packed weights in the prepacked layout (w4a16_prepack)
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_MID = 0x0000, 0x1000, 0x2000, 0x3000
 PATH_RAGGED = 0x4000  # reported by gemm_path for K % 32 == 16 (never a flag)
 PATHS = {"auto": PATH_AUTO, "skinny": PATH_SKINNY, "mid": PATH_MID, "tiled": PATH_TILED}
 
-OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP, ERR_EPILOGUE = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_FORMAT, ERR_SHAPE, ERR_NULL, ERR_ALIGN, ERR_HIP, ERR_EPILOGUE, ERR_OVERLAP = 0, -1, -2, -3, -4, -5, -6, -7
 MAX_GROUP = 8  # members of one w4a16_gemm_grouped call
 
 # fused epilogue: C = act(alpha * (A . W^T) + bias[n]) + beta * residual[m, n]
@@ -88,6 +89,10 @@ def load_library():
     lib.w4a16_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
     lib.w4a16_dequant.restype = I
     lib.w4a16_gemm_path.argtypes = [I, I64, I64, I64]
+    lib.w4a16_prepacked_bytes.restype = I64
+    lib.w4a16_prepacked_bytes.argtypes = [I64, I64]
+    lib.w4a16_prepack.restype = I
+    lib.w4a16_prepack.argtypes = [P, P, I64, I64, P]
     lib.w4a16_gemm_path.restype = I
     lib.w4a16_strerror.argtypes = [I]
     lib.w4a16_strerror.restype = ctypes.c_char_p
@@ -139,6 +144,44 @@ def _check(t, name, shape, itemsize, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+class PrepackedWeights:
+    """Packed weights (N, K/2) in the library's prepacked layout (made by
+    :func:`prepack`): ``data`` is the uint8 buffer of ceil(N/16)*16 rows.
+    Pass it wherever ``packed`` is taken (scales and zeros are unchanged)."""
+
+    def __init__(self, data: torch.Tensor, N: int, K: int):
+        self.data, self.N, self.K = data, int(N), int(K)
+        self.shape = (self.N, self.K // 2)  # the logical packed shape
+        self.device = data.device
+        self.is_cuda = data.is_cuda
+
+
+def _weights_view(packed):
+    """(tensor passed to the library, logical rows N, PREPACKED flag or 0)."""
+    if isinstance(packed, PrepackedWeights):
+        return packed.data, packed.N, PREPACKED
+    return packed, packed.shape[0], 0
+
+
+def prepack(packed: torch.Tensor, stream=None) -> PrepackedWeights:
+    """The prepacked layout of row-major packed weights (N, K/2), K % 128 == 0
+    (asynchronous, on ``stream``)."""
+    if not isinstance(packed, torch.Tensor) or not packed.is_cuda:
+        raise ValueError("packed must be a GPU tensor")
+    N, K2 = packed.shape
+    K = 2 * K2
+    _check(packed, "packed", (N, K2), 1, packed.device)
+    nbytes = load_library().w4a16_prepacked_bytes(N, K)
+    if nbytes < 0:
+        raise W4A16Error(int(nbytes), "w4a16_prepacked_bytes")
+    rows = (N + 15) // 16 * 16
+    out = torch.empty((rows, K2), dtype=torch.uint8, device=packed.device)
+    rc = load_library().w4a16_prepack(_ptr(packed), _ptr(out), N, K, _stream_handle(stream))
+    if rc != OK:
+        raise W4A16Error(rc, "w4a16_prepack")
+    return PrepackedWeights(out, N, K)
+
+
 def _check_weights(fmt, packed, scales, zeros, N, K, device):
     if fmt not in GROUP:
         raise ValueError(f"unknown format {fmt}")
@@ -146,7 +189,12 @@ def _check_weights(fmt, packed, scales, zeros, N, K, device):
     if K % 16:
         raise ValueError(f"K={K} must be a multiple of 16")
     groups = (K + G - 1) // G  # the last group may be shorter
-    _check(packed, "packed", (N, K // 2), 1, device)
+    if isinstance(packed, PrepackedWeights):
+        if packed.K != K or packed.N != N:
+            raise ValueError(f"prepacked weights are {packed.N} x {packed.K}, expected {N} x {K}")
+        _check(packed.data, "packed", ((N + 15) // 16 * 16, K // 2), 1, device)
+    else:
+        _check(packed, "packed", (N, K // 2), 1, device)
     _check(scales, "scales", (N, groups), 2 if fmt in INT4_FORMATS else 1, device)
     if fmt in ZERO_FORMATS:
         if zeros is None:
@@ -188,7 +236,7 @@ def gemm(fmt: int, A: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
         raise ValueError("A must be a GPU tensor")
     device = A.device
     M, K = A.shape
-    N = packed.shape[0]
+    wt, N, pre = _weights_view(packed)
     _check(A, "A", (M, K), 2, device)
     _check_weights(fmt, packed, scales, zeros, N, K, device)
     if out is None:
@@ -196,14 +244,14 @@ def gemm(fmt: int, A: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("out must be bf16 or fp32")
     _check(out, "out", (M, N), out.element_size(), device)
-    flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path]
+    flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path] | pre
     ep = _epilogue(bias, residual, alpha, beta, activation, out, M, N, device)
     lib = load_library()
     if ep is None:
-        rc = lib.w4a16_gemm(int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales),
+        rc = lib.w4a16_gemm(int(fmt) | flags, _ptr(A), _ptr(wt), _ptr(scales),
                             _ptr(zeros), _ptr(out), M, N, K, _stream_handle(stream))
     else:
-        rc = lib.w4a16_gemm_ex(int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales),
+        rc = lib.w4a16_gemm_ex(int(fmt) | flags, _ptr(A), _ptr(wt), _ptr(scales),
                                _ptr(zeros), _ptr(out), M, N, K, ctypes.byref(ep),
                                _stream_handle(stream))
     if rc != OK:
@@ -221,7 +269,7 @@ def _grouped_args(fmt, A, weights, outs, out_dtype):
     M, K = A.shape
     _check(A, "A", (M, K), 2, device)
     if outs is None:
-        outs = [torch.empty((M, w[0].shape[0]), dtype=out_dtype, device=device) for w in weights]
+        outs = [torch.empty((M, _weights_view(w[0])[1]), dtype=out_dtype, device=device) for w in weights]
     if len(outs) != len(weights):
         raise ValueError("one output per weight matrix")
     dt = outs[0].dtype
@@ -230,13 +278,17 @@ def _grouped_args(fmt, A, weights, outs, out_dtype):
     n = len(weights)
     arr = lambda: (ctypes.c_void_p * n)()
     P, S, Z, Cs, Ns = arr(), arr(), arr(), arr(), (ctypes.c_int64 * n)()
+    pres = set()
     for i, ((packed, scales, zeros), out) in enumerate(zip(weights, outs)):
-        N = packed.shape[0]
+        wt, N, pre = _weights_view(packed)
+        pres.add(pre)
         _check_weights(fmt, packed, scales, zeros, N, K, device)
         _check(out, f"out[{i}]", (M, N), out.element_size(), device)
-        P[i], S[i], Cs[i], Ns[i] = packed.data_ptr(), scales.data_ptr(), out.data_ptr(), N
+        P[i], S[i], Cs[i], Ns[i] = wt.data_ptr(), scales.data_ptr(), out.data_ptr(), N
         Z[i] = zeros.data_ptr() if zeros is not None else None
-    flags = OUT_F32 if dt == torch.float32 else OUT_BF16
+    if len(pres) > 1:
+        raise ValueError("a group's weights must all be prepacked or all row-major")
+    flags = (OUT_F32 if dt == torch.float32 else OUT_BF16) | pres.pop()
     zarr = Z if fmt in ZERO_FORMATS else None
     return flags, outs, (P, S, zarr, Cs, Ns), (M, K)
 
@@ -260,7 +312,7 @@ class PreparedGroupedGemm:
     def __init__(self, fmt: int, A, weights, outs, path: str = "auto"):
         flags, outs, arrays, (M, K) = _grouped_args(fmt, A, weights, outs, torch.bfloat16)
         self.tensors = (A, list(weights), outs)
-        self.kernel = gemm_path(fmt, M, int(arrays[4][0]), K, path)
+        self.kernel = gemm_path(fmt | (flags & PREPACKED), M, int(arrays[4][0]), K, path)
         self._fn = load_library().w4a16_gemm_grouped
         self._args = (int(fmt) | flags | PATHS[path], _ptr(A), len(weights), *arrays, M, K)
 
@@ -276,7 +328,7 @@ def _batched_args(fmt, items, outs, out_dtype):
     if not items:
         return (OUT_F32 if out_dtype == torch.float32 else OUT_BF16), [], (BatchItem * 1)(), 0
     if outs is None:
-        outs = [torch.empty((A.shape[0], packed.shape[0]), dtype=out_dtype, device=A.device)
+        outs = [torch.empty((A.shape[0], _weights_view(packed)[1]), dtype=out_dtype, device=A.device)
                 for A, packed, _, _ in items]
     if len(outs) != len(items):
         raise ValueError("one output per item")
@@ -285,6 +337,7 @@ def _batched_args(fmt, items, outs, out_dtype):
         raise ValueError("outputs must all be bf16 or all fp32")
     M = items[0][0].shape[0]
     arr = (BatchItem * len(items))()
+    pres = set()
     for i, ((A, packed, scales, zeros), out) in enumerate(zip(items, outs)):
         if not A.is_cuda:
             raise ValueError(f"A[{i}] must be a GPU tensor")
@@ -292,13 +345,16 @@ def _batched_args(fmt, items, outs, out_dtype):
         if A.dim() != 2 or A.shape[0] != M:
             raise ValueError(f"A[{i}] must have the batch's M = {M} rows")
         K = A.shape[1]
-        N = packed.shape[0]
+        wt, N, pre = _weights_view(packed)
+        pres.add(pre)
         _check(A, f"A[{i}]", (M, K), 2, device)
         _check_weights(fmt, packed, scales, zeros, N, K, device)
         _check(out, f"out[{i}]", (M, N), out.element_size(), device)
-        arr[i] = BatchItem(A.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+        arr[i] = BatchItem(A.data_ptr(), wt.data_ptr(), scales.data_ptr(),
                            None if zeros is None else zeros.data_ptr(), out.data_ptr(), N, K)
-    flags = OUT_F32 if dt == torch.float32 else OUT_BF16
+    if len(pres) > 1:
+        raise ValueError("a batch's weights must all be prepacked or all row-major")
+    flags = (OUT_F32 if dt == torch.float32 else OUT_BF16) | pres.pop()
     return flags, outs, arr, M
 
 
@@ -321,7 +377,7 @@ class PreparedBatchedGemm:
         items = list(items)
         flags, outs, arr, M = _batched_args(fmt, items, outs, torch.bfloat16)
         self.tensors = (items, outs)
-        self.kernel = gemm_path(fmt, M, int(arr[0].N), int(arr[0].K)) if items else None
+        self.kernel = gemm_path(fmt | (flags & PREPACKED), M, int(arr[0].N), int(arr[0].K)) if items else None
         self._fn = load_library().w4a16_gemm_batched
         self._args = (int(fmt) | flags, M, len(outs), arr)
 
@@ -338,13 +394,13 @@ def dequant(fmt: int, packed: torch.Tensor, scales: torch.Tensor,
     if not packed.is_cuda:
         raise ValueError("packed must be a GPU tensor")
     device = packed.device
-    N, K2 = packed.shape
-    K = 2 * K2
+    wt, N, pre = _weights_view(packed)
+    K = 2 * packed.shape[1]
     _check_weights(fmt, packed, scales, zeros, N, K, device)
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=device)
     _check(out, "out", (N, K), 2, device)
-    rc = load_library().w4a16_dequant(int(fmt), _ptr(packed), _ptr(scales), _ptr(zeros),
+    rc = load_library().w4a16_dequant(int(fmt) | pre, _ptr(wt), _ptr(scales), _ptr(zeros),
                                       _ptr(out), N, K, _stream_handle(stream))
     if rc != OK:
         raise W4A16Error(rc, "w4a16_dequant")
@@ -365,18 +421,18 @@ class PreparedGemm:
                  activation="none"):
         device = A.device
         M, K = A.shape
-        N = packed.shape[0]
+        wt, N, pre = _weights_view(packed)
         _check(A, "A", (M, K), 2, device)
         _check_weights(fmt, packed, scales, zeros, N, K, device)
         _check(out, "out", (M, N), out.element_size(), device)
         if out.dtype not in (torch.bfloat16, torch.float32):
             raise ValueError("out must be bf16 or fp32")
         self.tensors = (A, packed, scales, zeros, out, bias, residual)
-        flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path]
-        self.kernel = gemm_path(fmt, M, N, K, path)
+        flags = (OUT_F32 if out.dtype == torch.float32 else OUT_BF16) | PATHS[path] | pre
+        self.kernel = gemm_path(fmt | pre, M, N, K, path)
         self._ep = _epilogue(bias, residual, alpha, beta, activation, out, M, N, device)
         lib = load_library()
-        self._args = (int(fmt) | flags, _ptr(A), _ptr(packed), _ptr(scales), _ptr(zeros),
+        self._args = (int(fmt) | flags, _ptr(A), _ptr(wt), _ptr(scales), _ptr(zeros),
                       _ptr(out), M, N, K)
         if self._ep is None:
             self._fn = lib.w4a16_gemm

@@ -23,17 +23,17 @@ bool has_zeros(int fmt) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // format, flags and shape checks shared by w4a16_gemm and w4a16_gemm_path
+// (W4A16_PREPACKED is accepted everywhere; allow_flags adds the output type
+// and the kernel choice)
 int check_format_shape(int format, int64_t M, int64_t N, int64_t K, bool allow_flags) {
   const int fmt = format & W4A16_FORMAT_MASK;
   const int flags = format & ~W4A16_FORMAT_MASK;
   if (fmt > W4A16_INT4_SYM) return W4A16_ERR_FORMAT;
-  if (allow_flags) {
-    if (flags & ~(W4A16_OUT_F32 | W4A16_PATH_MASK)) return W4A16_ERR_FORMAT;
-  } else if (flags) {
-    return W4A16_ERR_FORMAT;
-  }
+  const int allowed = W4A16_PREPACKED | (allow_flags ? (W4A16_OUT_F32 | W4A16_PATH_MASK) : 0);
+  if (flags & ~allowed) return W4A16_ERR_FORMAT;
   if (M < 0 || N < 0 || K <= 0) return W4A16_ERR_SHAPE;
   if (K % 16 != 0) return W4A16_ERR_SHAPE;  // the last group may be shorter than G
+  if ((format & W4A16_PREPACKED) && K % 128 != 0) return W4A16_ERR_SHAPE;  // whole 1-KB blocks
   if (M >= kMaxDim || N >= kMaxDim || K > kMaxK) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
@@ -77,7 +77,7 @@ hipError_t launch_path(int path, const w4a16::GemmArgs& a) {
 
 extern "C" {
 
-int w4a16_version(void) { return 105; }
+int w4a16_version(void) { return 106; }
 
 const char* w4a16_strerror(int status) {
   switch (status) {
@@ -89,6 +89,7 @@ const char* w4a16_strerror(int status) {
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for a format without zeros";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
     case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case W4A16_ERR_OVERLAP: return "the output of w4a16_prepack overlaps its input";
     case W4A16_ERR_EPILOGUE:
       return "bad epilogue: unknown activation, nonzero reserved field, or a residual that "
              "overlaps C without being C";
@@ -146,6 +147,7 @@ int w4a16_gemm_ex(int format, const void* A, const void* packed, const void* sca
   a.epi = epi;
   a.fmt = fmt;
   a.out_f32 = out_f32;
+  a.pre = (format & W4A16_PREPACKED) != 0;
   a.A = static_cast<const uint16_t*>(A);
   a.packed = static_cast<const uint8_t*>(packed);
   a.scales = scales;
@@ -191,6 +193,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     w4a16::GroupedArgs g = {};
     g.fmt = fmt;
     g.out_f32 = out_f32;
+    g.pre = (format & W4A16_PREPACKED) != 0;
     for (int i = 0; i < count; ++i) {
       if (N[i] == 0) continue;
       g.A[g.count] = static_cast<const uint16_t*>(A);
@@ -213,6 +216,7 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
     a.epi = w4a16::Epilogue{};
     a.fmt = fmt;
     a.out_f32 = out_f32;
+    a.pre = (format & W4A16_PREPACKED) != 0;
     a.A = static_cast<const uint16_t*>(A);
     a.packed = static_cast<const uint8_t*>(packed[i]);
     a.scales = scales[i];
@@ -230,14 +234,18 @@ int w4a16_gemm_grouped(int format, const void* A, int count, const void* const* 
 int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item* items, void* stream) {
   // format and flags (output dtype only: the kernel is chosen per launch)
   const int fmt = format & W4A16_FORMAT_MASK;
-  if (fmt > W4A16_INT4_SYM || (format & ~(W4A16_FORMAT_MASK | W4A16_OUT_F32))) return W4A16_ERR_FORMAT;
+  if (fmt > W4A16_INT4_SYM || (format & ~(W4A16_FORMAT_MASK | W4A16_OUT_F32 | W4A16_PREPACKED)))
+    return W4A16_ERR_FORMAT;
   if (count < 0 || M < 0) return W4A16_ERR_SHAPE;
   if (count > 0 && !items) return W4A16_ERR_NULL;
   const bool out_f32 = (format & W4A16_OUT_F32) != 0;
+  const bool pre = (format & W4A16_PREPACKED) != 0;
   // every item is checked before anything is enqueued
   int rc = W4A16_OK;
   for (int i = 0; i < count; ++i)
-    if ((rc = check_format_shape(fmt, M, items[i].N, items[i].K, false)) != W4A16_OK) return rc;
+    if ((rc = check_format_shape(fmt | (format & W4A16_PREPACKED), M, items[i].N, items[i].K, false)) !=
+        W4A16_OK)
+      return rc;
   if (M == 0) return W4A16_OK;
   for (int i = 0; i < count; ++i) {
     const w4a16_batch_item& it = items[i];
@@ -253,6 +261,7 @@ int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item*
     a.epi = w4a16::Epilogue{};
     a.fmt = fmt;
     a.out_f32 = out_f32;
+    a.pre = pre;
     a.A = static_cast<const uint16_t*>(it.A);
     a.packed = static_cast<const uint8_t*>(it.packed);
     a.scales = it.scales;
@@ -301,6 +310,7 @@ int w4a16_gemm_batched(int format, int64_t M, int count, const w4a16_batch_item*
       w4a16::GroupedArgs g = {};
       g.fmt = fmt;
       g.out_f32 = out_f32;
+      g.pre = pre;
       for (size_t j = 0; j < n; ++j) {
         const w4a16_batch_item& it = items[order[c + j]];
         g.A[g.count] = static_cast<const uint16_t*>(it.A);
@@ -334,7 +344,29 @@ int w4a16_dequant(int format, const void* packed, const void* scales, const void
   const hipError_t e = w4a16::launch_dequant(fmt, static_cast<const uint8_t*>(packed), scales,
                                              static_cast<const uint8_t*>(zeros),
                                              static_cast<uint16_t*>(W), N, K,
+                                             (format & W4A16_PREPACKED) != 0,
                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int64_t w4a16_prepacked_bytes(int64_t N, int64_t K) {
+  const int rc = check_format_shape(W4A16_INT4_G128 | W4A16_PREPACKED, 0, N, K, false);
+  if (rc != W4A16_OK) return rc;
+  return ((N + 15) / 16) * 16 * (K / 2);
+}
+
+int w4a16_prepack(const void* packed, void* out, int64_t N, int64_t K, void* stream) {
+  const int rc = check_format_shape(W4A16_INT4_G128 | W4A16_PREPACKED, 0, N, K, false);
+  if (rc != W4A16_OK) return rc;
+  if (N == 0) return W4A16_OK;  // nothing is read or written
+  if (!packed || !out) return W4A16_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(out, 16)) return W4A16_ERR_ALIGN;
+  // the output must not overlap the input (the copy gathers across rows)
+  const uintptr_t p0 = (uintptr_t)packed, o0 = (uintptr_t)out;
+  const uintptr_t in_bytes = (uintptr_t)(N * (K / 2)), out_bytes = (uintptr_t)(((N + 15) / 16) * 16 * (K / 2));
+  if (p0 < o0 + out_bytes && o0 < p0 + in_bytes) return W4A16_ERR_OVERLAP;
+  const hipError_t e = w4a16::launch_prepack(static_cast<const uint8_t*>(packed), static_cast<uint8_t*>(out),
+                                             N, K, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 

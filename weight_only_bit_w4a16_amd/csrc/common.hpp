@@ -104,6 +104,21 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+
+// ---- weight layouts ------------------------------------------------------------
+// Byte offset of 16-byte chunk c (codes 32c .. 32c+31) of weight row r, counted
+// from a row that is a multiple of 16, in one of the two layouts of the packed
+// weights:
+//   row-major (as given): rowb = K/2 bytes per row;
+//   prepacked: 16-row tiles, and in a tile one 1-KB block per 128 codes
+//     (4 chunks of each of the 16 rows), chunk c of row r at slot
+//     (r % 16) + 16 (c % 4) of block c / 4 -- the order in which the lanes of
+//     an MFMA 16x16x32 weight fragment read them, so that a wave's 16-byte
+//     loads of one block are one contiguous kilobyte.
+__device__ __forceinline__ uint32_t wchunk(uint32_t r, uint32_t c, uint32_t rowb, bool pre) {
+  return pre ? (r >> 4) * (rowb << 4) + (c >> 2) * 1024u + ((r & 15u) + 16u * (c & 3u)) * 16u
+             : r * rowb + c * 16u;
+}
 __device__ __forceinline__ u32x4_t buf_load_b128(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

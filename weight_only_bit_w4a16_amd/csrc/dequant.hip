@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       const void* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros,
                                                       uint16_t* __restrict__ W, int64_t N,
-                                                      int64_t K) {
+                                                      int64_t K, int pre) {
   const int64_t chunks_per_row = K / 32;
   const int64_t total = N * chunks_per_row;
   constexpr int G = FormatTraits<FMT>::kGroup;
@@ -76,7 +76,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t n = i / chunks_per_row;
     const int64_t c = i - n * chunks_per_row;
-    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(packed + n * (K / 2) + c * 16);
+    // (prepacked: chunk c of row n at slot n % 16 + 16 (c % 4) of the tile's
+    // 1-KB block c / 4)
+    const int64_t src = pre ? (n >> 4) * 16 * (K / 2) + (c >> 2) * 1024 + ((n & 15) + 16 * (c & 3)) * 16
+                            : n * (K / 2) + c * 16;
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(packed + src);
     u32x4_t out[4];
     if constexpr (is_int4(FMT)) {
       const int64_t g = (c * 32) / G;
@@ -123,7 +127,7 @@ hipError_t launch_dequant16(const uint8_t* packed, const void* scales, const uin
 }  // namespace
 
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, const uint8_t* zeros,
-                          uint16_t* W, int64_t N, int64_t K, hipStream_t stream) {
+                          uint16_t* W, int64_t N, int64_t K, bool pre, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   if (K % 32 != 0) {
     switch (fmt) {
@@ -142,23 +146,52 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, co
   switch (fmt) {
     case kInt4:
       return launch_kernel(dequant_kernel<kInt4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           packed, scales, zeros, W, N, K);
+                           packed, scales, zeros, W, N, K, pre ? 1 : 0);
     case kNvfp4:
       return launch_kernel(dequant_kernel<kNvfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           packed, scales, zeros, W, N, K);
+                           packed, scales, zeros, W, N, K, pre ? 1 : 0);
     case kInt4G32:
       return launch_kernel(dequant_kernel<kInt4G32>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           packed, scales, zeros, W, N, K);
+                           packed, scales, zeros, W, N, K, pre ? 1 : 0);
     case kInt4G64:
       return launch_kernel(dequant_kernel<kInt4G64>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           packed, scales, zeros, W, N, K);
+                           packed, scales, zeros, W, N, K, pre ? 1 : 0);
     case kInt4Sym:
       return launch_kernel(dequant_kernel<kInt4Sym>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           packed, scales, zeros, W, N, K);
+                           packed, scales, zeros, W, N, K, pre ? 1 : 0);
     default:
       return launch_kernel(dequant_kernel<kMxfp4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           packed, scales, zeros, W, N, K);
+                           packed, scales, zeros, W, N, K, pre ? 1 : 0);
   }
+}
+
+// ---- prepacking ------------------------------------------------------------------
+// One thread per 16-byte chunk of the output, in output order (contiguous
+// stores; each 1-KB block gathers 64 bytes from each of 16 rows).  Rows past
+// N (the last tile's padding) become zero bytes.
+namespace {
+__global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict__ packed,
+                                                      uint8_t* __restrict__ out, int64_t N, int64_t K) {
+  const int64_t rowb = K / 2, kblocks = K / 128;
+  const int64_t total = ((N + 15) / 16) * kblocks * 64;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t l = i & 63, blk = i >> 6;
+    const int64_t t = blk / kblocks, b = blk - t * kblocks;
+    const int64_t n = 16 * t + (l & 15), c = 4 * b + (l >> 4);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (n < N) v = *reinterpret_cast<const u32x4_t*>(packed + n * rowb + c * 16);
+    *reinterpret_cast<u32x4_t*>(out + i * 16) = v;
+  }
+}
+}  // namespace
+
+hipError_t launch_prepack(const uint8_t* packed, uint8_t* out, int64_t N, int64_t K, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int64_t total = ((N + 15) / 16) * (K / 128) * 64;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;  // grid-stride loop covers the rest
+  return launch_kernel(prepack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, packed, out, N, K);
 }
 
 }  // namespace w4a16

@@ -43,6 +43,7 @@ struct Epilogue {
 struct GemmArgs {
   int fmt;        // 0 int4 g128, 1 NVFP4, 2 MXFP4
   bool out_f32;   // C is fp32 (else bf16)
+  bool pre;       // packed is in the prepacked layout (K % 128 == 0)
   const uint16_t* A;
   const uint8_t* packed;
   const void* scales;
@@ -60,6 +61,7 @@ constexpr int kMaxGroup = 32;
 struct GroupedArgs {
   int fmt;
   bool out_f32;
+  bool pre;   // every member's weights in the prepacked layout
   int count;  // 1 .. kMaxGroup, every member with N[i] > 0
   const uint16_t* A[kMaxGroup];
   const uint8_t* packed[kMaxGroup];
@@ -73,7 +75,10 @@ struct GroupedArgs {
 };
 
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, const uint8_t* zeros,
-                          uint16_t* W, int64_t N, int64_t K, hipStream_t stream);
+                          uint16_t* W, int64_t N, int64_t K, bool pre, hipStream_t stream);
+
+// the prepacked layout of row-major packed weights (N, K/2), K % 128 == 0
+hipError_t launch_prepack(const uint8_t* packed, uint8_t* out, int64_t N, int64_t K, hipStream_t stream);
 
 // M <= 16 per 16-row slice: split-K over the waves of a workgroup, weights
 // decoded in registers.

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
                                                                const void* __restrict__ scales,
                                                                const uint8_t* __restrict__ zeros,
                                                                void* __restrict__ C, int M, int N, int K,
-                                                               Epilogue epi) {
+                                                               int pre, Epilogue epi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -159,8 +159,9 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
     if constexpr (has_zeros(FMT)) zr = make_rsrc(z_base, (uint32_t)(rows * groups));
   }
 
-  // weight rows past N, A rows past M and chunks past K read as 0
-  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  // weight rows past N, A rows past M and chunks past K read as 0 (the
+  // prepacked layout's tiles of 16 rows end in zero bytes past N)
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)(pre ? (rows + 15) & ~15 : rows) * rowb);
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
 
   f32x4_t acc[MS][2];
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(64 * kMidMaxWaves) void mid_kernel(const uint16_t* 
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t r = (uint32_t)(16 * h + nl);
-        q[u][h] = buf_load_b128(wr, ok ? r * rowb + (uint32_t)c * 16u : kBufferOOB);
+        q[u][h] = buf_load_b128(wr, ok ? wchunk(r, (uint32_t)c, rowb, pre != 0) : kBufferOOB);
         if constexpr (!S_LDS) {
           if constexpr (is_int4(FMT)) {
             // groups of 128: the k-block's group for every chunk, also past
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
                                                                     const void* __restrict__ scales,
                                                                     const uint8_t* __restrict__ zeros,
                                                                     void* __restrict__ C, int M, int N, int K,
-                                                                    Epilogue epi) {
+                                                                    int pre, Epilogue epi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int W = kMidRingWaves;
   constexpr int CPK = 4 * MS + 2;  // copies per k-block
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
   const int rows = min(kMidCols, N - n0);
   const int arows = min(16 * MS, M - m0);
 
-  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)(pre ? (rows + 15) & ~15 : rows) * rowb);
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
   const uint32_t s_cap = mid_ring_window((uint32_t)(kMidCols * groups * SB));
   const uint32_t z_cap = has_zeros(FMT) ? mid_ring_window((uint32_t)(kMidCols * groups)) : 0u;
@@ -413,10 +414,11 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int wrow = 16 * t + (lane >> 2), wch = lane & 3;
+      // (prepacked: lane -> row 16t + l%16, chunk l/16: one contiguous kilobyte)
+      const int wrow = 16 * t + (pre ? (lane & 15) : (lane >> 2)), wch = pre ? (lane >> 4) : (lane & 3);
       const bool okw = FULL || kb * 4 + wch < KC;
       lds_dma_b128(wr, slot + (uint32_t)MS * 4096u + (uint32_t)t * 1024u,
-                   okw ? (uint32_t)wrow * rowb + (uint32_t)kb * 64u + (uint32_t)wch * 16u : kBufferOOB);
+                   okw ? wchunk((uint32_t)wrow, (uint32_t)(kb * 4 + wch), rowb, pre != 0) : kBufferOOB);
     }
   };
   auto ring_wait = [&](int later) {
@@ -457,7 +459,8 @@ __global__ __launch_bounds__(64 * kMidRingWaves) void mid_ring_kernel(const uint
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = 16 * h + nl;
-      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(slot + MS * 4096 + (r * 4 + g) * 16);
+      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(
+          slot + MS * 4096 + h * 1024 + (pre ? nl + 16 * g : nl * 4 + g) * 16);
       if constexpr (is_int4_g128(FMT)) {
         const int gi = r * groups + kb;
         sc[h] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + 2 * gi));
@@ -579,7 +582,7 @@ hipError_t launch_v(const GemmArgs& a, const MidPlan& p) {
     const hipError_t e =
         launch_kernel(mid_kernel<FMT, OUT_F32, U, MS, S_LDS>, grid, dim3(64 * p.waves), p.lds, a.stream,
                       a.A + m * a.K, a.packed, a.scales, a.zeros, static_cast<uint8_t*>(a.C) + m * a.N * es,
-                      (int)rows, (int)a.N, (int)a.K, epi);
+                      (int)rows, (int)a.N, (int)a.K, a.pre ? 1 : 0, epi);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -611,10 +614,12 @@ hipError_t launch_ring(const GemmArgs& a, unsigned lds) {
     const hipError_t e =
         full ? launch_kernel(mid_ring_kernel<FMT, OUT_F32, MS, D, true>, grid, dim3(64 * kMidRingWaves), lds,
                              a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
-                             static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi)
+                             static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K,
+                             a.pre ? 1 : 0, epi)
              : launch_kernel(mid_ring_kernel<FMT, OUT_F32, MS, D, false>, grid, dim3(64 * kMidRingWaves), lds,
                              a.stream, a.A + m * a.K, a.packed, a.scales, a.zeros,
-                             static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K, epi);
+                             static_cast<uint8_t*>(a.C) + m * a.N * es, (int)rows, (int)a.N, (int)a.K,
+                             a.pre ? 1 : 0, epi);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

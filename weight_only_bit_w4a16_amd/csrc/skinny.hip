@@ -57,7 +57,8 @@ struct SkinnyMember {
 template <int CAP>
 struct SkinnyGroup {
   SkinnyMember m[CAP];  // one member's fields are contiguous
-  int rows;  // weight rows (output columns) per workgroup, 1 .. 16
+  int rows;  // weight rows (output columns) per workgroup, 1 .. 16 (16 when prepacked)
+  int pre;   // the weights are in the prepacked layout
 };
 template <bool GROUPED>
 using SkinnyGroupOf = SkinnyGroup<GROUPED ? kMaxGroup : 1>;
@@ -243,7 +244,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
   const int arows = min(16, M - m0);
 
   const uint32_t rowb = (uint32_t)(K >> 1);
-  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  // (prepacked: the whole 16-row tile, whose rows past N are zero bytes)
+  const bool pre = grp.pre != 0;
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)(pre ? 16 : rows) * rowb);
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
   const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n0 * groups * SB,
                               (uint32_t)(rows * groups * SB));
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
       const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
-      q[u] = buf_load_b128(wr, ok ? (uint32_t)nl * rowb + (uint32_t)c * 16u : kBufferOOB);
+      q[u] = buf_load_b128(wr, ok ? wchunk((uint32_t)nl, (uint32_t)c, rowb, pre) : kBufferOOB);
       if constexpr (!A_LDS && !A_DMA) {
         const uint32_t aoff = ((uint32_t)nl * (uint32_t)K + (uint32_t)c * 32u) * 2u;
 #pragma unroll
@@ -551,7 +554,8 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(SkinnyGroup
   const int arows = min(16, M - m0);
 
   const uint32_t rowb = (uint32_t)(K >> 1);
-  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)rows * rowb);
+  const bool pre = grp.pre != 0;
+  const rsrc_t wr = make_rsrc(packed + (int64_t)n0 * rowb, (uint32_t)(pre ? 16 : rows) * rowb);
   const rsrc_t ar = make_rsrc(A + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
 
   const uint32_t s_cap = ring_window_cap(16u * (uint32_t)groups * SB);
@@ -594,10 +598,11 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(SkinnyGroup
       lds_dma_b128(ar, slot + (uint32_t)r4 * 1024u,
                    ok ? ((uint32_t)r * (uint32_t)K + (uint32_t)kb * 128u + 8u * (uint32_t)ch) * 2u : kBufferOOB);
     }
-    const int wrow = lane >> 2, wch = lane & 3;
+    // (prepacked: lane -> row l%16, chunk l/16: one contiguous kilobyte)
+    const int wrow = pre ? (lane & 15) : (lane >> 2), wch = pre ? (lane >> 4) : (lane & 3);
     const bool okw = FULL || kb * 4 + wch < chunks;
     lds_dma_b128(wr, slot + 4096u,
-                 okw ? (uint32_t)wrow * rowb + (uint32_t)kb * 64u + (uint32_t)wch * 16u : kBufferOOB);
+                 okw ? wchunk((uint32_t)wrow, (uint32_t)(kb * 4 + wch), rowb, pre) : kBufferOOB);
   };
   const int first = nk < D ? nk : D;
   for (int i = 0; i < first; ++i) issue(i);
@@ -623,7 +628,7 @@ __global__ __launch_bounds__(64 * kRingVirt) void skinny_ring_kernel(SkinnyGroup
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       a[j] = *reinterpret_cast<const u32x4_t*>(slot + nl * 256 + (((4 * g + j) ^ nl) * 16));
-    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(slot + 4096 + (nl * 4 + g) * 16);
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(slot + 4096 + (pre ? nl + 16 * g : nl * 4 + g) * 16);
     // this lane's scale (and zero) bytes; past K the weights and A are zero,
     // so any finite scale will do
     const int c = kb * 4 + g;
@@ -753,12 +758,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_stream_kernel(SkinnyGro
       const rsrc_t zs = window(T.zeros + (int64_t)T.n0 * groups, (uint32_t)(T.rows * groups), S.zdelta, S.zwords);
       S.z = buf_load_b32(zs, (uint32_t)tid < S.zwords ? (uint32_t)tid * 4u : kBufferOOB);
     }
-    // weights: rows past the tile's last read as zeros (descriptor range)
-    const rsrc_t wr = make_rsrc(packed + (int64_t)T.n0 * rowb, (uint32_t)T.rows * rowb);
+    // weights: rows past the tile's last read as zeros (descriptor range;
+    // prepacked: the whole 16-row tile, zero bytes past N)
+    const rsrc_t wr = make_rsrc(packed + (int64_t)T.n0 * rowb,
+                                (uint32_t)(grp.pre && live ? 16 : T.rows) * rowb);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = kw + u;
-      T.q[u] = buf_load_b128(wr, kb < KB ? (uint32_t)nl * rowb + (uint32_t)(kb * 4 + g) * 16u : kBufferOOB);
+      T.q[u] = buf_load_b128(wr, kb < KB ? wchunk((uint32_t)nl, (uint32_t)(kb * 4 + g), rowb, grp.pre != 0)
+                                         : kBufferOOB);
     }
     // keep the batch in flight: no load may sink towards its use
     __builtin_amdgcn_sched_barrier(0);
@@ -917,6 +925,7 @@ SkinnyGroup<CAP> skinny_group(const GroupedArgs& a, int rows) {
     grp.m[i].N = (int)a.N[i];
   }
   grp.rows = rows;
+  grp.pre = a.pre ? 1 : 0;
   return grp;
 }
 dim3 skinny_grid(const GroupedArgs& a, int rows) {
@@ -950,6 +959,7 @@ hipError_t launch_s(const GroupedArgs& a, int rows, dim3 grid, dim3 block, bool 
 // overhead).
 int skinny_rows(const GroupedArgs& a) {
   int rows = 16;
+  if (a.pre) return rows;  // the prepacked layout comes in tiles of 16 rows
   const int64_t r_min = (12288 + a.K / 2 - 1) / (a.K / 2);
   double best = -1.0;
   for (int r = 16; r >= (r_min > 4 ? (int)(r_min < 16 ? r_min : 16) : 4); --r) {
@@ -1206,6 +1216,7 @@ hipError_t launch_skinny(const GemmArgs& a) {
   GroupedArgs g = {};
   g.fmt = a.fmt;
   g.out_f32 = a.out_f32;
+  g.pre = a.pre;
   g.A[0] = a.A;
   g.count = 1;
   g.packed[0] = a.packed;

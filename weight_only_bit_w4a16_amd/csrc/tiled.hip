@@ -153,7 +153,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
                                                               const void* __restrict__ scales,
                                                               const uint8_t* __restrict__ zeros,
                                                               void* __restrict__ C, int M, int N,
-                                                              int K, Epilogue epi) {
+                                                              int K, int pre, Epilogue epi) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
   constexpr int kABytes = CFG::kABytes, kBBytes = CFG::kBBytes;
   using L = Layout<FMT, CFG>;
@@ -180,8 +180,10 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
   // Buffer descriptors over this workgroup's rows: rows past M / N read as 0.
   const uint32_t arow_b = (uint32_t)K * 2u, brow_b = (uint32_t)K >> 1;
   const int brows = min(BN, N - n_base);
+  // (prepacked: whole 16-row tiles, zero bytes past N)
+  const int brows_read = pre ? min(BN, ((N + 15) & ~15) - n_base) : brows;
   const rsrc_t ar = make_rsrc(A + (int64_t)m_base * K, (uint32_t)min(BM, M - m_base) * arow_b);
-  const rsrc_t br = make_rsrc(packed + (int64_t)n_base * brow_b, (uint32_t)brows * brow_b);
+  const rsrc_t br = make_rsrc(packed + (int64_t)n_base * brow_b, (uint32_t)brows_read * brow_b);
   constexpr int SB = is_int4(FMT) ? 2 : 1;
   const rsrc_t sr = make_rsrc(reinterpret_cast<const uint8_t*>(scales) + (int64_t)n_base * groups * SB,
                               (uint32_t)(brows * groups * SB));
@@ -206,15 +208,17 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     a_k[i] = 8 * c;
   }
   // B block: slot q = 64 bb + lane -> row q / 2, which holds half h = (q & 1) ^ ((row >> 2) & 1)
+  // (k-tile j: chunk 2j + h of the row, at wchunk(row, 2j + h) = wchunk(row, h) + j * b_step)
   uint32_t b_src[CFG::kBBlocks];
   int b_k[CFG::kBBlocks];
 #pragma unroll
   for (int i = 0; i < CFG::kBBlocks; ++i) {
     const int q = 64 * (wave * CFG::kBBlocks + i) + lane;
     const int row = q >> 1, h = (q & 1) ^ ((row >> 2) & 1);
-    b_src[i] = (uint32_t)row * brow_b + (uint32_t)h * 16u;
+    b_src[i] = wchunk((uint32_t)row, (uint32_t)h, brow_b, pre != 0);
     b_k[i] = 32 * h;
   }
+  const uint32_t b_step = pre ? 512u : 32u;
 
   // issue the copies of k-tile kt into stage st (CFG::kGroupOps per wave)
   auto issue = [&](int kt, int st) {
@@ -227,8 +231,7 @@ __global__ __launch_bounds__(CFG::kThreads) void tiled_kernel(const uint16_t* __
     const uint32_t b_lds = lds0 + L::kBOff + st * kBBytes + wave * CFG::kBBlocks * 1024;
 #pragma unroll
     for (int i = 0; i < CFG::kBBlocks; ++i)
-      lds_dma_b128(br, b_lds + i * 1024,
-                   k0 + b_k[i] < K ? b_src[i] + (uint32_t)(k0 >> 1) : kBufferOOB);
+      lds_dma_b128(br, b_lds + i * 1024, k0 + b_k[i] < K ? b_src[i] + (uint32_t)kt * b_step : kBufferOOB);
   };
 
   // issue the copies of scale tile u into buffer u & 1 (L::kSBlocks per wave):
@@ -564,7 +567,7 @@ hipError_t launch_cfg(const GemmArgs& a) {
   const int64_t tiles = ((a.N + CFG::BN - 1) / CFG::BN) * ((a.M + CFG::BM - 1) / CFG::BM);
   return launch_kernel(tiled_kernel<FMT, OUT_F32, CFG>, dim3((unsigned)tiles), dim3(CFG::kThreads), 0,
                        a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K,
-                       a.epi);
+                       a.pre ? 1 : 0, a.epi);
 }
 
 template <int FMT, bool OUT_F32>
