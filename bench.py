@@ -355,10 +355,34 @@ def main():
         total = timed_graph(calls, steps, warmup)
         kernel = calls[0][0].kernel
         del calls, C
+        vendor_ms = None
+        if M > 16 and not epilogue:
+            # context for the compute-bound shape: the platform's own dense bf16
+            # GEMM (torch.matmul -> hipBLASLt) on the same shape, with the
+            # weights already dequantised to bf16 (no 4-bit decode at all)
+            W = w4.dequant(fmt, p, s, z)
+            Wt = W.t().contiguous()
+            Cv = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            vsteps = max(1, min(steps, 200))
+            vendor_ms = timed_graph([[lambda: torch.matmul(A, Wt, out=Cv)]], vsteps, warmup) / vsteps
+            del W, Wt, Cv
+            progress(f"  dense bf16 torch.matmul, same shape: {vendor_ms * 1e3:.3f} us per launch (graph)")
         progress(f"{w4.FORMAT_NAMES[fmt]} M={M} N={N} K={K}: {total / steps * 1e3:.3f} us per launch "
                  f"(graph), {eager / steps * 1e3:.3f} eager ({kernel}, {steps} steps)")
         return {"case": case, "ms": total / steps, "eager_ms": eager / steps,
-                "eager_median_ms": statistics.median(per), "copies": copies, "kernel": kernel}
+                "eager_median_ms": statistics.median(per), "copies": copies, "kernel": kernel,
+                "vendor_ms": vendor_ms}
+
+    def vendor_entry(r, M, N, K):
+        """The dense bf16 GEMM beside a compute-bound workload (context only)."""
+        if r.get("vendor_ms") is None:
+            return None
+        return {"what": "torch.matmul (hipBLASLt) of bf16 A and the dequantised bf16 weights, same "
+                        "shape, graph-timed like the workload: the platform's dense GEMM with no "
+                        "4-bit decode (context, not the baseline)",
+                "ms_per_step": round(r["vendor_ms"], 6),
+                "tflops": round(2.0 * M * N * K / (r["vendor_ms"] * 1e-3) / 1e12, 1),
+                "w4a16_speedup": round(r["vendor_ms"] / r["ms"], 3)}
 
     def single_entry(name, steps, warmup):
         fmt, M, N, K, out = WORKLOADS[name]
@@ -372,6 +396,7 @@ def main():
         if M > 16:
             e["tflops"] = round(2.0 * M * N * K / (r["ms"] * 1e-3) / 1e12, 1)
             e["roofline"] = mfma_roofline(2 * M * N * K, r["ms"], r["kernel"], name)
+            e["dense_bf16_gemm"] = vendor_entry(r, M, N, K)
         else:
             e["weight_gbs"] = round(wbytes / (r["ms"] * 1e-3) / 1e9, 1)
             e["roofline"] = hbm_roofline(tbytes, r["ms"], r["kernel"], name)
@@ -465,6 +490,7 @@ def main():
         if M > 16:
             value, unit = 2.0 * M * N * K / (ms * 1e-3) / 1e12, "TFLOP/s"
             roof = mfma_roofline(2 * M * N * K, ms, r["kernel"], args.workload, traffic=not args.epilogue)
+            config["dense_bf16_gemm"] = vendor_entry(r, M, N, K)
         else:
             value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
             roof = hbm_roofline(tbytes, ms, r["kernel"], args.workload, traffic=not args.epilogue)
