@@ -176,6 +176,11 @@ def main():
                     help="decode chain: skip timing the 197 ungrouped launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bounds", action="store_true",
+                    help="only measure the bounds the kernels are compared with, with the measurement "
+                         "kernels of libw4a16_probe.so: the empty-launch floor, a plain read of the decode "
+                         "GEMV's weight bytes and of 256 MiB, the MFMA rate of a matrix-only loop, and a "
+                         "split-K hand-off between workgroups; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 10 times (reference "
                          "kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -237,6 +242,83 @@ def main():
         return 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
 
     cyc_per_ms = spin_cycles_per_ms()
+
+    def measure_bounds():
+        """The bounds of the design doc's measurements, from libw4a16_probe.so."""
+        import ctypes
+        from weight_only_bit_w4a16_amd import _build
+        if not os.path.exists(_build.PROBE_LIB):
+            raise SystemExit(f"{_build.PROBE_LIB} is missing: build first (__graft_entry__.build())")
+        lib = ctypes.CDLL(_build.PROBE_LIB)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.w4a16_probe_empty.argtypes = [P, P]
+        lib.w4a16_probe_read.argtypes = [P, I64, I, I, P, P]
+        lib.w4a16_probe_mfma.argtypes = [I, I, I, P, P]
+        lib.w4a16_probe_handoff.argtypes = [P, P, P, I, I, I, P]
+        st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        sink = torch.zeros(16, dtype=torch.int32, device=dev)
+
+        def call(fn, *a):
+            def f():
+                rc = fn(*a, st())
+                if rc != 0:
+                    raise RuntimeError(f"probe call failed: {rc}")
+            return f
+
+        out = {}
+        steps = 1000
+        out["empty_launch_us"] = round(timed_graph([[call(lib.w4a16_probe_empty, sink.data_ptr())]], steps, 50)
+                                       / steps * 1e3, 3)
+        progress(f"bounds: empty launch {out['empty_launch_us']} us per graph node")
+        shapes = [(256, 1), (512, 1), (768, 1), (768, 2), (1024, 2), (1024, 4), (512, 8)]
+        for name, nbytes in (("decode_gemv_weight_bytes", algorithmic_bytes(0, 1, 8192, 3072, "bf16")[0] // 16 * 16),
+                             ("read_256MiB", 256 << 20)):
+            copies = max(1, math.ceil((1 << 30) / nbytes)) + 1
+            bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+            best = None
+            nst = 400 if nbytes < (64 << 20) else 40
+            for thr, per in shapes:
+                calls = [[call(lib.w4a16_probe_read, b.data_ptr(), nbytes, thr, per, sink.data_ptr())] for b in bufs]
+                us = timed_graph(calls, nst, 10) / nst * 1e3
+                if best is None or us < best[0]:
+                    best = (us, thr, per)
+            del bufs
+            out[name] = {"bytes": nbytes, "best_us": round(best[0], 3), "threads": best[1], "loads_per_thread": best[2],
+                         "tb_per_s": round(nbytes / (best[0] * 1e-6) / 1e12, 3)}
+            progress(f"bounds: plain read of {nbytes} B: {best[0]:.3f} us ({out[name]['tb_per_s']} TB/s)")
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        iters = 20000
+        f = call(lib.w4a16_probe_mfma, cus, 512, iters, sink.data_ptr())
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        flops = cus * 8 * iters * 8 * 16384.0
+        out["mfma_only"] = {"workgroups": cus, "waves_per_workgroup": 8, "ms": round(ms, 3),
+                            "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        progress(f"bounds: MFMA-only loop {out['mfma_only']['tflops']} TFLOP/s")
+        groups = 64
+        hand = {}
+        for slices in (2, 4):
+            scratch = torch.zeros(groups * slices * 768, dtype=torch.float32, device=dev)
+            counters = torch.zeros(groups, dtype=torch.int32, device=dev)
+            o = torch.zeros(groups * 768, dtype=torch.float32, device=dev)
+            for mode, mname in ((0, "partials_only"), (1, "fence_per_workgroup"), (2, "fence_per_thread"),
+                                (3, "second_kernel")):
+                c = call(lib.w4a16_probe_handoff, scratch.data_ptr(), counters.data_ptr(), o.data_ptr(),
+                         groups, slices, mode)
+                hand[f"{slices}_slices_{mname}_us"] = round(timed_graph([[c]], 200, 10) / 200 * 1e3, 3)
+            torch.cuda.synchronize()
+            if int(counters.abs().sum().item()) != 0:
+                raise RuntimeError("hand-off counters not left at zero")
+        out["splitk_handoff"] = dict(workgroups_per_slice=groups, **hand)
+        progress(f"bounds: split-K hand-off {hand}")
+        return {"bounds": out, "device": torch.cuda.get_device_name(dev)}
+
 
     def timed(calls_per_step, steps, warmup, graph=False, min_warm_ms=50.0):
         """Time `steps` steps; step i runs the prepared calls
@@ -326,6 +408,10 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
+
+    if args.bounds:
+        print(json.dumps(measure_bounds()))
+        return
 
     def measure_single(fmt, M, N, K, out, steps, warmup, epilogue=None):
         """One GEMM workload timed over `steps` launches that rotate over

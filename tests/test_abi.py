@@ -372,3 +372,39 @@ def test_prepacked_flag_checks():
     assert lib.w4a16_dequant(w4.NVFP4 | pre | w4.OUT_F32, PB, PS, None, PA, 64, 128, None) == w4.ERR_FORMAT
     item = w4.BatchItem(PA.value, PB.value, PS.value, None, PC.value, 64, 160)
     assert lib.w4a16_gemm_batched(w4.MXFP4 | pre, 1, 1, ctypes.byref(item), None) == w4.ERR_SHAPE
+
+
+# ---- the measurement kernels (libw4a16_probe.so, bench.py --bounds) ----------------
+
+def _probe_lib():
+    from weight_only_bit_w4a16_amd import _build
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.w4a16_probe_read.argtypes = [P, I64, I, I, P, P]
+    lib.w4a16_probe_mfma.argtypes = [I, I, I, P, P]
+    lib.w4a16_probe_handoff.argtypes = [P, P, P, I, I, I, P]
+    return lib
+
+
+def test_probe_library_exports_its_header():
+    text = open(os.path.join(ROOT, "include", "w4a16_probe.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(w4a16_probe_\w+)\s*\(", text, re.M)))
+    assert names == ["w4a16_probe_empty", "w4a16_probe_handoff", "w4a16_probe_mfma", "w4a16_probe_read"]
+    lib = _probe_lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_probe_host_checks():
+    lib = _probe_lib()
+    p, s = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    bad = -2
+    assert lib.w4a16_probe_read(None, 1024, 256, 1, s, None) == bad
+    assert lib.w4a16_probe_read(p, 1000, 256, 1, s, None) == bad          # bytes % 16
+    assert lib.w4a16_probe_read(p, 1024, 100, 1, s, None) == bad          # threads % 64
+    assert lib.w4a16_probe_read(p, 1024, 256, 3, s, None) == bad          # loads per thread
+    assert lib.w4a16_probe_read(ctypes.c_void_p(0x100008), 1024, 256, 1, s, None) == bad
+    assert lib.w4a16_probe_mfma(0, 256, 10, s, None) == bad
+    assert lib.w4a16_probe_mfma(1, 2048, 10, s, None) == bad
+    assert lib.w4a16_probe_handoff(p, p, p, 4, 2, 4, None) == bad          # mode
+    assert lib.w4a16_probe_handoff(p, None, p, 4, 2, 1, None) == bad

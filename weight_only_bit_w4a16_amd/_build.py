@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
+PROBE_LIB = os.path.join(PKG, "libw4a16_probe.so")  # measurement kernels (bench.py --bounds)
+PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["api.cpp", "dequant.hip", "skinny.hip", "mid.hip", "tiled.hip", "ragged.hip"]
 ARCH = "gfx950"
 
@@ -45,14 +47,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(lib: str, objs) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 4) -> str:
+    """Build libw4a16.so (the GEMM library) and libw4a16_probe.so (the
+    measurement kernels); returns the GEMM library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(LIB, objs[:len(SOURCES)])
+    _link(PROBE_LIB, objs[len(SOURCES):])
     return LIB
 
 
