@@ -117,8 +117,9 @@ extern "C" {
 /* ---- status codes --------------------------------------------------------- */
 #define W4A16_OK 0
 #define W4A16_ERR_FORMAT (-1) /* unknown format or flag bits                 */
-#define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 16 != 0, M or N
-                                 >= 2^31, or K > 2^22                       */
+#define W4A16_ERR_SHAPE (-2)  /* negative M/N, K <= 0, K % 16 != 0 (K % 128
+                                 != 0 with W4A16_PREPACKED), M or N >= 2^31,
+                                 or K > 2^22                                */
 #define W4A16_ERR_NULL (-3)   /* a required pointer is NULL, or zeros is
                                  non-NULL for a format without zeros
                                  (INT4_SYM, NVFP4, MXFP4)                   */

@@ -84,8 +84,8 @@ const char* w4a16_strerror(int status) {
     case W4A16_OK: return "success";
     case W4A16_ERR_FORMAT: return "unknown weight format or flag bits";
     case W4A16_ERR_SHAPE:
-      return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^22 and K % 16 == 0 (and 1 <= count "
-             "<= W4A16_MAX_GROUP for a group)";
+      return "bad shape: need 0 <= M, N < 2^31, 0 < K <= 2^22 and K % 16 == 0 (K % 128 == 0 for "
+             "prepacked weights; 1 <= count <= W4A16_MAX_GROUP for a group)";
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for a format without zeros";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
     case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
