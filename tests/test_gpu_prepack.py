@@ -144,3 +144,52 @@ def test_grouped_and_batched_prepacked():
         assert same_bits(g, r)
     with pytest.raises(ValueError):
         w4.gemm_grouped(fmt, A, [weights[0], pweights[1]])
+
+
+def _random_cases(n=60, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        fmt = FORMATS[rng.integers(len(FORMATS))]
+        M = int(rng.choice([1, 2, 5, 8, 16, 17, 33, 64, 130, 300]))
+        N = int(rng.integers(1, 601))
+        K = 128 * int(rng.integers(1, 33))
+        if M * N * K > 12_000_000:
+            continue
+        out.append((fmt, M, N, K, ["auto", "skinny", "mid", "tiled"][rng.integers(4)], bool(rng.integers(2)),
+                    len(out)))
+    return out
+
+
+@pytest.mark.parametrize("fmt,M,N,K,path,f32,i", _random_cases())
+def test_random_shapes_prepacked_equal_row_major(fmt, M, N, K, path, f32, i):
+    odt = torch.float32 if f32 else torch.bfloat16
+    print(f"[prepack random {i}] fmt {fmt} {M}x{N}x{K} path {path} -> "
+          f"{w4.gemm_path(fmt | w4.PREPACKED, M, N, K, path)} out {odt}", flush=True)
+    case = inputs.make_case(fmt, M, N, K, seed=9000 + i)
+    A, p, s, z = to_dev(case)
+    ref = w4.gemm(fmt, A, p, s, z, out_dtype=odt, path=path)
+    got = w4.gemm(fmt, A, w4.prepack(p), s, z, out_dtype=odt, path=path)
+    torch.cuda.synchronize()
+    assert same_bits(got, ref)
+
+
+def test_prepacked_batched_graph_replay():
+    fmt, K = w4.INT4_G128, 3072
+    cases = [inputs.make_case(fmt, 1, n, K, 60 + i) for i, n in enumerate([1024, 1024, 3072, 8192])]
+    items = [(A, w4.prepack(p), s, z) for A, p, s, z in (to_dev(c) for c in cases)]
+    eager = w4.gemm_batched(fmt, items)
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    call = w4.PreparedBatchedGemm(fmt, items, outs)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert same_bits(o, e), rep
