@@ -282,6 +282,28 @@ def test_gemm_int4_any_zero_byte(path, M, K):
         check_gate(C, Cref, S, odt == torch.bfloat16, f"int4 zeros 0..255 {M}x{N}x{K} {path} {odt}")
 
 
+@pytest.mark.parametrize("path,M,N,K", [
+    ("skinny", 1, 96, 512), ("skinny", 16, 72, 8192), ("mid", 40, 96, 512),
+    ("tiled", 40, 96, 512), ("tiled", 300, 257, 224), ("auto", 5, 40, 48)])
+def test_gemm_nvfp4_negative_scale_bytes(path, M, N, K):
+    """NVFP4 scale bytes with the sign bit set on a random half: the scale
+    enters by magnitude (the NVFP4 dequantisation writes |scale|), so the
+    result matches the oracle and equals, bit for bit, the run with every
+    sign bit clear."""
+    case = inputs.make_case(w4.NVFP4, M, N, K, seed=21 + M + K)
+    rng = np.random.default_rng(22 + M)
+    pos = case.scales.copy()
+    case.scales |= (rng.integers(0, 2, size=pos.shape, dtype=np.uint8) << 7).astype(np.uint8)
+    assert (case.scales >= 0x80).any() and (case.scales < 0x80).any()
+    Cref, S = oracle.gemm(w4.NVFP4, case.A, case.packed, case.scales, None, M, N, K)
+    for odt in (torch.float32, torch.bfloat16):
+        C = run_gemm(case, odt, path)
+        check_gate(C, Cref, S, odt == torch.bfloat16, f"nvfp4 signed scales {M}x{N}x{K} {path}")
+        neg_bits = C.copy()
+        case_pos = inputs.Case(case.fmt, M, N, K, case.A, case.packed, pos, None)
+        assert np.array_equal(run_gemm(case_pos, odt, path), neg_bits)
+
+
 def test_gemm_zero_extent():
     case = inputs.make_case(w4.MXFP4, 0, 64, 64, seed=0)
     A, p, s, _ = to_dev(case)
