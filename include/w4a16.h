@@ -62,7 +62,12 @@
  * Errors: every argument is checked on the host BEFORE anything is enqueued;
  * a failed check returns its code and enqueues nothing.  A launch failure
  * reported by the HIP runtime for the call's own launch returns W4A16_ERR_HIP
- * (an earlier error of the calling thread is neither reported nor cleared).
+ * (an earlier error of the calling thread is neither reported nor cleared);
+ * so does a launch whose grid would exceed 2^32 - 1 work-items along one
+ * dimension (refused before it is enqueued): only weight matrices of more
+ * than 2^26 rows (output columns) can reach that, on the kernels that give
+ * every 16 to 64 rows a workgroup of their own (K % 128 != 0, int4 groups of
+ * 32 / 64, or more than 16 rows of A).
  *
  * Threads: the library's only global state is a cache of device properties
  * (compute units per device, resident workgroups per kernel), filled on first
@@ -124,7 +129,9 @@ extern "C" {
                                  non-NULL for a format without zeros
                                  (INT4_SYM, NVFP4, MXFP4)                   */
 #define W4A16_ERR_ALIGN (-4)  /* a pointer violates its alignment           */
-#define W4A16_ERR_HIP (-5)    /* the HIP runtime rejected a launch          */
+#define W4A16_ERR_HIP (-5)    /* the HIP runtime rejected a launch, or its
+                                 grid would exceed 2^32 - 1 work-items along
+                                 a dimension                                */
 #define W4A16_ERR_EPILOGUE (-6) /* unknown activation, nonzero reserved field,
                                    or a residual that overlaps C without
                                    being C                                  */

@@ -107,3 +107,44 @@ def test_prepacked_max_k():
     Cp = w4.gemm(fmt, A, w4.prepack(p), s, z)
     torch.cuda.synchronize()
     assert torch.equal(C.view(torch.int16), Cp.view(torch.int16))
+
+
+# ---- the widest weight matrices: the grid limit ------------------------------------
+
+def _wide_operands(N, K, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    A = torch.randn((1, K), generator=g, device=DEV).to(torch.bfloat16)
+    packed = torch.randint(0, 256, (N, K // 2), generator=g, device=DEV, dtype=torch.uint8)
+    scales = (127 + torch.randint(-4, 5, (N, (K + 31) // 32), generator=g, device=DEV)).to(torch.uint8)
+    return A, packed, scales
+
+
+def test_widest_matrix_below_grid_limit():
+    """K = 16 (the ragged-K kernel, one workgroup of 256 work-items per 64
+    rows): 2^30 - 64 rows is the widest grid below 2^32 work-items; sampled
+    rows, the first and the last against the oracle."""
+    N, K = (1 << 30) - 64, 16
+    A, packed, scales = _wide_operands(N, K, 71)
+    C = w4.gemm(w4.MXFP4, A, packed, scales, None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(72)
+    rows = np.unique(np.concatenate([rng.integers(0, N, 62), [0, N - 1]]))
+    idx = torch.from_numpy(rows).to(DEV)
+    a = A.view(torch.int16).cpu().numpy().view(np.uint16)
+    p = packed[idx].cpu().numpy()
+    s = scales[idx].cpu().numpy()
+    Cref, S = oracle.gemm(w4.MXFP4, a, p, s, None, 1, len(rows), K)
+    check(C[0, idx].double().cpu().numpy()[None, :], Cref, S, False, f"N = 2^30 - 64, K = {K}")
+
+
+def test_grid_limit_refused_before_launch():
+    """2^30 rows at K = 16 would need 2^32 work-items along the grid: the call
+    returns W4A16_ERR_HIP without launching, and C is left untouched."""
+    N, K = 1 << 30, 16
+    A, packed, scales = _wide_operands(N, K, 73)
+    C = torch.full((1, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.gemm(w4.MXFP4, A, packed, scales, None, out=C)
+    assert e.value.status == w4.ERR_HIP
+    torch.cuda.synchronize()
+    assert bool((C == 7.0).all())

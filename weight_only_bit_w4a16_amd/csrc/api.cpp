@@ -88,7 +88,9 @@ const char* w4a16_strerror(int status) {
              "prepacked weights; 1 <= count <= W4A16_MAX_GROUP for a group)";
     case W4A16_ERR_NULL: return "a required pointer is NULL, or zeros is non-NULL for a format without zeros";
     case W4A16_ERR_ALIGN: return "a pointer violates its alignment requirement";
-    case W4A16_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case W4A16_ERR_HIP:
+      return "the HIP runtime rejected a kernel launch, or its grid would exceed 2^32 - 1 work-items "
+             "along a dimension";
     case W4A16_ERR_OVERLAP: return "the output of w4a16_prepack overlaps its input";
     case W4A16_ERR_EPILOGUE:
       return "bad epilogue: unknown activation, nonzero reserved field, or a residual that "

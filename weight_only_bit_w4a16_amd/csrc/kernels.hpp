@@ -15,11 +15,17 @@ namespace w4a16 {
 // Enqueue `kernel` on `stream` and return the status of this launch itself
 // (hipLaunchKernel's own result: an earlier, unrelated error of the calling
 // thread is neither reported nor cleared).  The arguments are converted to
-// the kernel's parameter types and passed by address.
+// the kernel's parameter types and passed by address.  A grid whose
+// work-items along one dimension exceed 2^32 - 1 (the dispatch packet's
+// 32-bit sizes) is refused here, before any launch.
 template <typename... Params, typename... Args>
 inline hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, unsigned lds,
                                 hipStream_t stream, Args&&... args) {
   static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  constexpr uint64_t kMaxItems = 0xFFFFFFFFull;
+  if ((uint64_t)grid.x * block.x > kMaxItems || (uint64_t)grid.y * block.y > kMaxItems ||
+      (uint64_t)grid.z * block.z > kMaxItems)
+    return hipErrorInvalidConfiguration;
   std::tuple<std::decay_t<Params>...> vals(std::forward<Args>(args)...);
   void* ptrs[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
   std::apply([&ptrs](auto&... v) {

@@ -565,6 +565,7 @@ using CfgSmall = TileCfg<2, 2, 4, 4>;
 template <int FMT, bool OUT_F32, class CFG>
 hipError_t launch_cfg(const GemmArgs& a) {
   const int64_t tiles = ((a.N + CFG::BN - 1) / CFG::BN) * ((a.M + CFG::BM - 1) / CFG::BM);
+  if (tiles > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;  // (the grid counts tiles in 32 bits)
   return launch_kernel(tiled_kernel<FMT, OUT_F32, CFG>, dim3((unsigned)tiles), dim3(CFG::kThreads), 0,
                        a.stream, a.A, a.packed, a.scales, a.zeros, a.C, (int)a.M, (int)a.N, (int)a.K,
                        a.pre ? 1 : 0, a.epi);
