@@ -244,7 +244,8 @@ def main():
     cyc_per_ms = spin_cycles_per_ms()
 
     def measure_bounds():
-        """The bounds of the design doc's measurements, from libw4a16_probe.so."""
+        """The bounds the kernels are compared with: launch floor, read and MFMA ceilings and the
+        split-K hand-off, measured by the kernels of libw4a16_probe.so."""
         import ctypes
         from weight_only_bit_w4a16_amd import _build
         if not os.path.exists(_build.PROBE_LIB):
