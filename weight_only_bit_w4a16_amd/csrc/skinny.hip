@@ -197,6 +197,12 @@ __device__ __forceinline__ void skinny_store(const f32x4_t* red, int waves, int 
 // straight into a private LDS region (asynchronous global -> LDS copies of
 // contiguous 256-byte row pieces) instead of per-lane A loads.
 // GROUPED: more than one member, blockIdx.z (a single GEMM reads member 0).
+// PRIV (int4 groups of 128, few A rows; A_LDS, S_LDS and A_DMA off): each
+// wave copies into an LDS region of its own exactly what it reads -- the A
+// rows of its k-blocks (even / odd k order, plus a zero row) and the scales
+// and zeros of its 16 rows and k-blocks -- so no workgroup barrier precedes
+// the arithmetic (the wave's LDS writes and reads are ordered by themselves).
+// The operands and their order are those of the A_LDS route: same bits.
 // R: virtual waves per wave.  The split of K is into virtual waves of U
 // k-blocks each (virtual wave v sums k-blocks v U .. v U + U - 1, and the
 // partial sums are added in v order); a wave computes R consecutive virtual
@@ -204,9 +210,11 @@ __device__ __forceinline__ void skinny_store(const f32x4_t* red, int waves, int 
 // many workgroups set to 2 (half the waves per workgroup, so more of them
 // fit a CU and more weight loads are in flight); R = 2 needs K covered in
 // one pass.
-template <int FMT, bool OUT_F32, int U, int R, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED>
+template <int FMT, bool OUT_F32, int U, int R, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED,
+          bool PRIV = false>
 __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GROUPED> grp, int M, int K,
                                                                 Epilogue epi) {
+  static_assert(!PRIV || (is_int4_g128(FMT) && !A_LDS && !S_LDS && !A_DMA), "private staging");
   constexpr int UR = U * R;  // k-blocks per wave and pass
   // the group member whose columns this workgroup computes: its fields come
   // in one scalar load round trip at a workgroup-uniform offset
@@ -265,6 +273,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
   const uint32_t a_dma_off = S_LDS ? z_off + z_cap : s_off;
   const uint32_t a_wave = lds_address(a_lds) + a_dma_off +
                           (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (uint32_t)(UR * 4096);
+  // PRIV: this wave's region (priv_bytes, the launcher's skinny_priv_bytes):
+  // A rows 0 .. am (row arows of the slice is zeros) x UR k-blocks x 256
+  // bytes, then 16 x UR bf16 scales and 16 x UR zero bytes, entry r * UR + u
+  const uint32_t priv_a = (uint32_t)(am + 1) * (uint32_t)UR * 256u;
+  const uint32_t priv_bytes = (priv_a + 16u * UR * 3u + 15u) & ~15u;
+  uint8_t* const priv = a_lds + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * priv_bytes;
+  constexpr int kPS = 2;                   // 16-byte A pieces per lane
+  constexpr int kPE = (16 * UR + 63) / 64;  // scale / zero entries per lane
+  u32x4_t pst[kPS];
+  uint32_t pss[kPE], pzs[kPE];
   uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
   // staging loads are issued only by waves that hold some in-range slot
   // (a wave whose first slot is past the block skips the instruction)
@@ -337,10 +355,33 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
   // row it reads); pass p covers k-blocks [(p * waves + wave) * UR, +UR).
   auto valid = [&](int kb, int c) { return FULL ? (kb < KB) : (kb < KB && c < chunks); };
   auto issue = [&](int kbase) {
+    if constexpr (PRIV) {
+      // A piece i of lane l: qi = l + 64 i = (r * UR + u) * 16 + p -> row r,
+      // k-block kbase + u, bytes 16 p .. of its 256 (launcher: arows * UR <= 8)
+#pragma unroll
+      for (int i = 0; i < kPS; ++i) {
+        const int qi = lane + 64 * i;
+        const int r = qi / (UR * 16), u = (qi / 16) % UR, p = qi % 16;
+        const int kb = kbase + u;
+        const bool ok = r < arows && kb < KB && (FULL || kb * 128 + p * 8 < K);
+        pst[i] = buf_load_b128(ar, ok ? ((uint32_t)r * (uint32_t)K + (uint32_t)kb * 128u + (uint32_t)p * 8u) * 2u
+                                      : kBufferOOB);
+      }
+      // scale and zero entry e = r * UR + u: row r, k-block kbase + u (its group)
+#pragma unroll
+      for (int i = 0; i < kPE; ++i) {
+        const int e = lane + 64 * i;
+        const int kb = kbase + e % UR;
+        const bool ok = e < 16 * UR && kb < KB;
+        const uint32_t gi = (uint32_t)((e / UR) * groups + kb);
+        pss[i] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
+        pzs[i] = has_zeros(FMT) ? buf_load_b8(zr, ok ? gi : kBufferOOB) : kSymZero;
+      }
+    }
     // scales first: vmcnt retires in issue order, so the first k-block's
     // arithmetic then waits only for its own weights
 #pragma unroll
-    for (int u = 0; u < (S_LDS ? 0 : UR); ++u) {
+    for (int u = 0; u < (S_LDS || PRIV ? 0 : UR); ++u) {
       const int kb = kbase + u;
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
@@ -384,7 +425,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
       const int c = kb * 4 + g;
       const bool ok = valid(kb, c);
       q[u] = buf_load_b128(wr, ok ? wchunk((uint32_t)nl, (uint32_t)c, rowb, pre) : kBufferOOB);
-      if constexpr (!A_LDS && !A_DMA) {
+      if constexpr (!A_LDS && !A_DMA && !PRIV) {
         const uint32_t aoff = ((uint32_t)nl * (uint32_t)K + (uint32_t)c * 32u) * 2u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[u][j] = buf_load_b128(ar, ok ? aoff + 16u * j : kBufferOOB);
@@ -400,10 +441,38 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
     // the copies are invisible to the compiler's own waits: wait for all of
     // this pass's loads (whatever order they were issued in)
     if constexpr (A_DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (PRIV) {
+      // this wave's region: its A pieces (even / odd k order), the zero row,
+      // its scales and zeros; read back below by the same wave only
+#pragma unroll
+      for (int i = 0; i < kPS; ++i) {
+        const int qi = lane + 64 * i;
+        if (qi < arows * UR * 16)
+          reinterpret_cast<u32x4_t*>(priv)[qi] = bf16x8_even_odd(pst[i]);
+      }
+      for (int qi = lane; qi < UR * 16; qi += 64)
+        reinterpret_cast<u32x4_t*>(priv + (uint32_t)arows * UR * 256u)[qi] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < kPE; ++i) {
+        const int e = lane + 64 * i;
+        if (e < 16 * UR) {
+          reinterpret_cast<uint16_t*>(priv + priv_a)[e] = (uint16_t)pss[i];
+          (priv + priv_a + 32u * UR)[e] = (uint8_t)pzs[i];
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       const int kb = kbase + u;
       if (FULL && kb >= KB) break;  // wave-uniform: nothing was loaded
+      if constexpr (PRIV) {
+        // row arow of the region (arows: the zero row), chunk g of k-block u
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(priv + ((uint32_t)arow * UR + u) * 256u + g * 64u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[u][j] = src[j];
+        sraw[u] = reinterpret_cast<const uint16_t*>(priv + priv_a)[nl * UR + u];
+        zraw[u] = (priv + priv_a + 32u * UR)[nl * UR + u];
+      }
       if constexpr (A_DMA) {
         const uint8_t* src = a_lds + a_dma_off + (size_t)wave * (UR * 4096) + u * 4096 + nl * 256;
 #pragma unroll
@@ -438,7 +507,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
           sraw[u] = sb[nl * groups + (ok ? c : 0)];
         }
       }
-      acc[u / U] = kblock_mac<FMT, A_LDS>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc[u / U]);
+      acc[u / U] = kblock_mac<FMT, A_LDS || PRIV>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc[u / U]);
     }
   };
 
@@ -943,6 +1012,21 @@ hipError_t launch_k(const GroupedArgs& a, int rows, dim3 grid, dim3 block, unsig
                        a.stream, skinny_group<1>(a, rows), (int)a.M, (int)a.K, a.epi);
 }
 
+// the private-staging route (PRIV): LDS = waves x this wave region
+uint32_t skinny_priv_bytes(int64_t M, int UR) {
+  const uint32_t am = (uint32_t)(M < 16 ? M : 16);
+  return ((am + 1u) * (uint32_t)UR * 256u + 16u * (uint32_t)UR * 3u + 15u) & ~15u;
+}
+template <int FMT, bool OUT_F32, int U, int R, bool FULL>
+hipError_t launch_priv(const GroupedArgs& a, int rows, dim3 grid, dim3 block) {
+  const unsigned lds = block.x / 64 * skinny_priv_bytes(a.M, U * R);
+  if (a.count > 1)
+    return launch_kernel(skinny_kernel<FMT, OUT_F32, U, R, false, FULL, false, false, true, true>, grid, block, lds,
+                         a.stream, skinny_group<kMaxGroup>(a, rows), (int)a.M, (int)a.K, a.epi);
+  return launch_kernel(skinny_kernel<FMT, OUT_F32, U, R, false, FULL, false, false, false, true>, grid, block, lds,
+                       a.stream, skinny_group<1>(a, rows), (int)a.M, (int)a.K, a.epi);
+}
+
 template <int FMT, bool OUT_F32, int U, bool A_LDS, bool FULL, bool A_DMA, int R = 1>
 hipError_t launch_s(const GroupedArgs& a, int rows, dim3 grid, dim3 block, bool s_lds,
                     unsigned lds_a, unsigned lds_s) {
@@ -1026,6 +1110,26 @@ template <int FMT, bool OUT_F32, int U>
 hipError_t launch_u(const GroupedArgs& a, int waves) {
   const int rows = skinny_rows(a);
   const dim3 grid = skinny_grid(a, rows);
+  // int4 with groups of 128 and at most 8 A rows x k-blocks per wave: private
+  // staging, no barrier before the arithmetic (same bits as the A_LDS route);
+  // two virtual waves per wave as below when that still holds
+  if constexpr (is_int4_g128(FMT)) {
+    const int64_t prow = a.M < 16 ? a.M : 16;
+    if (prow * U <= 8) {
+      const int KBp = (int)((a.K / 32 + 3) / 4);
+      const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+      const bool full = a.K % 128 == 0;
+      const bool halve = prow * U * 2 <= 8 && waves % 2 == 0 && waves * U >= KBp && wgs > 4 * (int64_t)device_cus();
+      if (halve) {
+        const dim3 half(64 * waves / 2);
+        return full ? launch_priv<FMT, OUT_F32, U, 2, true>(a, rows, grid, half)
+                    : launch_priv<FMT, OUT_F32, U, 2, false>(a, rows, grid, half);
+      }
+      const dim3 block(64 * waves);
+      return full ? launch_priv<FMT, OUT_F32, U, 1, true>(a, rows, grid, block)
+                  : launch_priv<FMT, OUT_F32, U, 1, false>(a, rows, grid, block);
+    }
+  }
   // stage A in LDS when the workgroup's A slice fits its staging registers
   const int64_t arows = a.M < 16 ? a.M : 16;
   const int64_t a_bytes = arows * a.K * 2;
