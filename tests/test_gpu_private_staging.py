@@ -1,0 +1,51 @@
+"""Private staging of the skinny kernel (int4 with groups of 128, at most 8 A
+rows x k-blocks per wave): each wave copies its own A pieces, scales and
+zeros to LDS and starts without a workgroup barrier.  The streaming variant
+(>= 1024 tiles of 16 columns) stages A and the scale windows once per
+workgroup instead; both feed the same operands in the same order, so the
+columns of a wide launch and those of a narrow launch of its first rows agree
+bit for bit.  Also against the oracle, with ragged K and a partial last tile.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_bit_w4a16_amd as w4
+from weight_only_bit_w4a16_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def to_dev(case):
+    A = torch.from_numpy(case.A.view(np.int16)).to(DEV).view(torch.bfloat16)
+    packed = torch.from_numpy(case.packed).to(DEV)
+    scales = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
+    zeros = torch.from_numpy(case.zeros).to(DEV) if case.zeros is not None else None
+    return A, packed, scales, zeros
+
+
+@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.INT4_SYM])
+@pytest.mark.parametrize("M,K", [(1, 3072), (2, 1024), (1, 8192), (4, 512), (3, 1280)])
+def test_private_staging_equals_streaming_variant(fmt, M, K):
+    N, n = 16384, 4096
+    case = inputs.make_case(fmt, M, N, K, seed=81 + M + K)
+    A, p, s, z = to_dev(case)
+    wide = w4.gemm(fmt, A, p, s, z)  # 1024 tiles: the streaming variant
+    narrow = w4.gemm(fmt, A, p[:n], s[:n], None if z is None else z[:n])  # one-tile, private staging
+    torch.cuda.synchronize()
+    assert torch.equal(wide[:, :n].view(torch.int16), narrow.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(w4.INT4_G128, 1, 1000, 3104), (w4.INT4_G128, 2, 77, 4064),
+                                       (w4.INT4_SYM, 1, 333, 2080), (w4.INT4_G128, 4, 129, 544)])
+def test_private_staging_against_oracle(fmt, M, N, K):
+    case = inputs.make_case(fmt, M, N, K, seed=91 + N)
+    A, p, s, z = to_dev(case)
+    Cref, S = oracle.gemm(fmt, case.A, case.packed, case.scales, case.zeros, M, N, K)
+    for odt in (torch.float32, torch.bfloat16):
+        C = w4.gemm(fmt, A, p, s, z, out_dtype=odt).double().cpu().numpy()
+        r = oracle.gate_ratio(C, Cref, S, odt == torch.bfloat16)
+        print(f"[gate] private staging fmt {fmt} {M}x{N}x{K} {odt}: {r:.3e}", flush=True)
+        assert r <= 1.0
