@@ -327,6 +327,67 @@ __device__ __forceinline__ u32x4_t int4x8_minus_zero(uint32_t q, float zf) {
   return r;
 }
 
+// ---- int4 through fp16 ---------------------------------------------------------
+// An integer code - zero in -255 .. 15 is exact in fp16 as well, and fp16
+// has packed arithmetic: with the code in the low mantissa bits of 0x6400
+// (1024.0) the fp16 value is 1024 + code, and one packed fp16 subtraction of
+// 1024 + zero (both in [1024, 1280), exact) leaves code - zero exactly.  That
+// is 11 VALU instructions per 8 codes (3 shifts, 4 bit-field inserts, 4 packed
+// subtractions) against the 19 of the fp32 route above.  The A operand is
+// then fp16 too, exact for a bf16 value that is 0, inf, or of magnitude in
+// [2^-17, 65504] (8 significant bits; fp16 subnormals keep 8 bits down to
+// 2^-17).  The products equal those of the bf16 route, and gfx950's MFMA
+// sums the 32 products of a step and the accumulator to the same bits
+// whatever the slot order and operand type (measured over 2^20 outputs of
+// four chained steps with exact products, slots permuted within each 8).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// mask and bias of the bit-field inserts, held in VGPRs (register operands)
+struct F16Consts {
+  uint32_t mask, bias;
+};
+__device__ __forceinline__ F16Consts f16_consts() {
+  F16Consts c{0x000F000Fu, 0x64006400u};
+  asm volatile("" : "+v"(c.mask), "+v"(c.bias));
+  return c;
+}
+// the fp16 pair (1024 + zero, 1024 + zero), zero a byte 0 .. 255
+__device__ __forceinline__ uint32_t f16_zero_pair(uint32_t zero) {
+  const uint32_t h = 0x6400u | zero;
+  return h | (h << 16);
+}
+__device__ __forceinline__ uint32_t f16x2_minus(uint32_t x, f16x2_t z) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, x) - z);
+}
+// 8 int4 codes (k = 0 .. 7, low nibble first) to code - zero in fp16, exact,
+// in the k order (0, 4, 1, 5, 2, 6, 3, 7): the dword of codes k, k + 4 takes
+// the nibbles at bits 4k and 4k + 16.
+__device__ __forceinline__ u32x4_t int4x8_minus_zero_f16(uint32_t q, F16Consts c, uint32_t zpair) {
+  const f16x2_t z = __builtin_bit_cast(f16x2_t, zpair);
+  const uint32_t bias = c.bias & ~c.mask;
+  const uint32_t r0 = f16x2_minus((q & c.mask) | bias, z);
+  const uint32_t r1 = f16x2_minus(((q >> 4) & c.mask) | bias, z);
+  const uint32_t r2 = f16x2_minus(((q >> 8) & c.mask) | bias, z);
+  const uint32_t r3 = f16x2_minus(((q >> 12) & c.mask) | bias, z);
+  return u32x4_t{r0, r1, r2, r3};
+}
+// 8 bf16 values (k = 0 .. 7) to fp16 in the k order of int4x8_minus_zero_f16;
+// `exact` is cleared unless every value converts exactly (a NaN clears it)
+__device__ __forceinline__ u32x4_t bf16x8_to_f16_k04(u32x4_t a, bool& exact) {
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) f[k] = __uint_as_float(k & 1 ? a[k >> 1] & 0xFFFF0000u : a[k >> 1] << 16);
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(f[k], f[k + 4]);
+    exact = exact && (float)h[0] == f[k] && (float)h[1] == f[k + 4];
+    r[k] = __builtin_bit_cast(uint32_t, h);
+  }
+  return u32x4_t{r[0], r[1], r[2], r[3]};
+}
+
 // The same in the k order (0, 2, 4, 6, 1, 3, 5, 7) of an A copy stored in
 // even / odd order: the converter's pairs are used as they come.
 __device__ __forceinline__ u32x4_t int4x8_minus_zero_even_odd(uint32_t q, float zf) {
@@ -402,6 +463,11 @@ __device__ __forceinline__ float residual_at(const void* res, int64_t mn) {
 // and B use the same one.
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t d) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), d, 0, 0, 0);
+}
+// the same with fp16 operands
+__device__ __forceinline__ f32x4_t mfma16x16x32_f16(u32x4_t a, u32x4_t b, f32x4_t d) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), d,
+                                                0, 0, 0);
 }
 
 }  // namespace w4a16

@@ -119,6 +119,25 @@ __device__ __forceinline__ f32x4_t kblock_mac(const u32x4_t (&a)[4], const u32x4
   return acc;
 }
 
+// kblock_mac for int4 with groups of 128 on fp16 operands: a[j] from an fp16
+// A copy in the k order (0, 4, 1, 5, 2, 6, 3, 7) per 8, the codes to code -
+// zero in fp16 in the same order (both exact: the same products as the bf16
+// route, summed by the MFMA to the same bits), the group scale on the fp32
+// sum.
+__device__ __forceinline__ f32x4_t kblock_mac_f16(const u32x4_t (&a)[4], const u32x4_t& q, uint32_t sraw,
+                                                  uint32_t zraw, f32x4_t acc, F16Consts fc) {
+  const uint32_t zp = f16_zero_pair(zraw);
+  f32x4_t dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dp = mfma16x16x32_f16(a[j], int4x8_minus_zero_f16(q[j], fc, zp), dp);
+  const float s = bf16_bits_to_f32(sraw);
+  acc[0] = __builtin_fmaf(s, dp[0], acc[0]);
+  acc[1] = __builtin_fmaf(s, dp[1], acc[1]);
+  acc[2] = __builtin_fmaf(s, dp[2], acc[2]);
+  acc[3] = __builtin_fmaf(s, dp[3], acc[3]);
+  return acc;
+}
+
 // The split-K sum over the waves' partials red[w * 64 + lane] (w = 0 ..
 // waves-1, in order) and the store of this workgroup's outputs, plain or
 // through the fused epilogue; run by wave 0.  Lane (nl, g) holds rows
@@ -202,7 +221,12 @@ __device__ __forceinline__ void skinny_store(const f32x4_t* red, int waves, int 
 // rows of its k-blocks (even / odd k order, plus a zero row) and the scales
 // and zeros of its 16 rows and k-blocks -- so no workgroup barrier precedes
 // the arithmetic (the wave's LDS writes and reads are ordered by themselves).
-// The operands and their order are those of the A_LDS route: same bits.
+// The operands and their order are those of the A_LDS route: same bits.  With
+// one virtual wave per wave (R = 1), a wave whose A pieces are all exact in
+// fp16 stores them as fp16 and decodes on the fp16 route (kblock_mac_f16, 11
+// instead of 19 VALU per 8 codes; the same bits), the others as bf16.  (With
+// R = 2 the second route's registers cost a wave of occupancy, measured
+// slower: decode chain +4 %.)
 // R: virtual waves per wave.  The split of K is into virtual waves of U
 // k-blocks each (virtual wave v sums k-blocks v U .. v U + U - 1, and the
 // partial sums are added in v order); a wave computes R consecutive virtual
@@ -437,6 +461,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
   };
 
   const int arow = nl < arows ? nl : arows;  // row arows of the LDS copy is zeros
+  constexpr bool kF16 = PRIV && R == 1;  // the fp16 route
+  bool w16 = false;  // kF16: this wave's A copy is fp16 (set per pass, wave-uniform)
+  const F16Consts fc = f16_consts();
   auto compute = [&](int kbase) {
     // the copies are invisible to the compiler's own waits: wait for all of
     // this pass's loads (whatever order they were issued in)
@@ -444,11 +471,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
     if constexpr (PRIV) {
       // this wave's region: its A pieces (even / odd k order), the zero row,
       // its scales and zeros; read back below by the same wave only
+      // fp16 when every A value of this wave converts exactly (wave-uniform)
+      u32x4_t ph[kPS];
+      if constexpr (kF16) {
+        bool exact = true;
+#pragma unroll
+        for (int i = 0; i < kPS; ++i)
+          if (lane + 64 * i < arows * UR * 16) ph[i] = bf16x8_to_f16_k04(pst[i], exact);
+        w16 = __ballot(!exact) == 0;
+      }
 #pragma unroll
       for (int i = 0; i < kPS; ++i) {
         const int qi = lane + 64 * i;
         if (qi < arows * UR * 16)
-          reinterpret_cast<u32x4_t*>(priv)[qi] = bf16x8_even_odd(pst[i]);
+          reinterpret_cast<u32x4_t*>(priv)[qi] = (kF16 && w16) ? ph[i] : bf16x8_even_odd(pst[i]);
       }
       for (int qi = lane; qi < UR * 16; qi += 64)
         reinterpret_cast<u32x4_t*>(priv + (uint32_t)arows * UR * 256u)[qi] = u32x4_t{0u, 0u, 0u, 0u};
@@ -507,7 +543,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
           sraw[u] = sb[nl * groups + (ok ? c : 0)];
         }
       }
-      acc[u / U] = kblock_mac<FMT, A_LDS || PRIV>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc[u / U]);
+      if (kF16 && w16)
+        acc[u / U] = kblock_mac_f16(a[u], q[u], sraw[u], zraw[u], acc[u / U], fc);
+      else
+        acc[u / U] = kblock_mac<FMT, A_LDS || PRIV>(a[u], q[u], sraw[u], is_int4(FMT) ? zraw[u] : 0u, acc[u / U]);
     }
   };
 
