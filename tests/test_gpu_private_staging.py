@@ -49,3 +49,28 @@ def test_private_staging_against_oracle(fmt, M, N, K):
         r = oracle.gate_ratio(C, Cref, S, odt == torch.bfloat16)
         print(f"[gate] private staging fmt {fmt} {M}x{N}x{K} {odt}: {r:.3e}", flush=True)
         assert r <= 1.0
+
+
+@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.INT4_SYM])
+def test_private_staging_fp16_and_bf16_routes_in_one_launch(fmt):
+    """A values outside fp16's exact range (huge, tiny, NaN-free) in some
+    waves' k-ranges: those waves take the bf16 route, the others the fp16 one;
+    the result still equals the streaming variant bit for bit and the oracle."""
+    M, N, n, K = 1, 16384, 4096, 3072
+    case = inputs.make_case(fmt, M, N, K, seed=97)
+    bits = case.A.copy()
+    to_bf16 = lambda x: np.array([x], np.float32).view(np.uint32)[0] >> 16
+    bits[0, 5] = to_bf16(1.5e30)      # k-block 0: wave 0's range
+    bits[0, 700] = to_bf16(3.0e-30)   # k-block 5: wave 2's range (2 k-blocks per wave)
+    bits[0, 2900] = to_bf16(-70000.0)  # k-block 22: past fp16's largest value
+    case.A[:] = bits
+    A, p, s, z = to_dev(case)
+    wide = w4.gemm(fmt, A, p, s, z, out_dtype=torch.float32)
+    narrow = w4.gemm(fmt, A, p[:n], s[:n], None if z is None else z[:n], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(wide[:, :n].view(torch.int32), narrow.view(torch.int32))
+    zn = None if case.zeros is None else case.zeros[:n]
+    Cref, S = oracle.gemm(fmt, case.A, case.packed[:n], case.scales[:n], zn, M, n, K)
+    r = oracle.gate_ratio(narrow.double().cpu().numpy(), Cref, S, False)
+    print(f"[gate] mixed fp16 / bf16 routes fmt {fmt}: {r:.3e}", flush=True)
+    assert r <= 1.0
