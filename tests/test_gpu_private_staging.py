@@ -1,5 +1,5 @@
-"""Private staging of the skinny kernel (int4 with groups of 128, at most 8 A
-rows x k-blocks per wave): each wave copies its own A pieces, scales and
+"""Private staging of the skinny kernel (int4 with groups of 128 and the fp4
+formats, at most 8 A rows x k-blocks per wave): each wave copies its own A pieces, scales and
 zeros to LDS and starts without a workgroup barrier.  The streaming variant
 (>= 1024 tiles of 16 columns) stages A and the scale windows once per
 workgroup instead; both feed the same operands in the same order, so the
@@ -21,12 +21,15 @@ DEV = torch.device("cuda", 0)
 def to_dev(case):
     A = torch.from_numpy(case.A.view(np.int16)).to(DEV).view(torch.bfloat16)
     packed = torch.from_numpy(case.packed).to(DEV)
-    scales = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
+    if case.fmt in w4.INT4_FORMATS:
+        scales = torch.from_numpy(case.scales.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        scales = torch.from_numpy(case.scales).to(DEV)
     zeros = torch.from_numpy(case.zeros).to(DEV) if case.zeros is not None else None
     return A, packed, scales, zeros
 
 
-@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.INT4_SYM])
+@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.INT4_SYM, w4.NVFP4, w4.MXFP4])
 @pytest.mark.parametrize("M,K", [(1, 3072), (2, 1024), (1, 8192), (4, 512), (3, 1280)])
 def test_private_staging_equals_streaming_variant(fmt, M, K):
     N, n = 16384, 4096
@@ -39,7 +42,9 @@ def test_private_staging_equals_streaming_variant(fmt, M, K):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [(w4.INT4_G128, 1, 1000, 3104), (w4.INT4_G128, 2, 77, 4064),
-                                       (w4.INT4_SYM, 1, 333, 2080), (w4.INT4_G128, 4, 129, 544)])
+                                       (w4.INT4_SYM, 1, 333, 2080), (w4.INT4_G128, 4, 129, 544),
+                                       (w4.NVFP4, 1, 500, 8224), (w4.MXFP4, 2, 300, 3104),
+                                       (w4.NVFP4, 4, 77, 544), (w4.MXFP4, 1, 1000, 8192)])
 def test_private_staging_against_oracle(fmt, M, N, K):
     case = inputs.make_case(fmt, M, N, K, seed=91 + N)
     A, p, s, z = to_dev(case)

@@ -234,11 +234,15 @@ __device__ __forceinline__ void skinny_store(const f32x4_t* red, int waves, int 
 // many workgroups set to 2 (half the waves per workgroup, so more of them
 // fit a CU and more weight loads are in flight); R = 2 needs K covered in
 // one pass.
+// (PRIV, one virtual wave per wave, U = 2: at least 6 waves per SIMD, so that
+// two workgroups of up to 12 waves share a CU -- one register more halves
+// that, measured on the decode GEMV)
 template <int FMT, bool OUT_F32, int U, int R, bool A_LDS, bool FULL, bool S_LDS, bool A_DMA, bool GROUPED,
           bool PRIV = false>
-__global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GROUPED> grp, int M, int K,
-                                                                Epilogue epi) {
-  static_assert(!PRIV || (is_int4_g128(FMT) && !A_LDS && !S_LDS && !A_DMA), "private staging");
+__global__ __launch_bounds__(64 * kMaxWaves)
+__attribute__((amdgpu_waves_per_eu(PRIV && R == 1 && U == 2 ? 6 : 1)))
+void skinny_kernel(SkinnyGroupOf<GROUPED> grp, int M, int K, Epilogue epi) {
+  static_assert(!PRIV || ((is_int4_g128(FMT) || !is_int4(FMT)) && !A_LDS && !S_LDS && !A_DMA), "private staging");
   constexpr int UR = U * R;  // k-blocks per wave and pass
   // the group member whose columns this workgroup computes: its fields come
   // in one scalar load round trip at a workgroup-uniform offset
@@ -300,11 +304,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
   // PRIV: this wave's region (priv_bytes, the launcher's skinny_priv_bytes):
   // A rows 0 .. am (row arows of the slice is zeros) x UR k-blocks x 256
   // bytes, then 16 x UR bf16 scales and 16 x UR zero bytes, entry r * UR + u
+  // scale entries per row and k-block: the group (int4) or each chunk's scale (fp4)
+  constexpr int kSC = is_int4(FMT) ? 1 : 4;
+  constexpr int kNE = 16 * UR * kSC;  // entries of a wave: e = (r * UR + u) * kSC + chunk
   const uint32_t priv_a = (uint32_t)(am + 1) * (uint32_t)UR * 256u;
-  const uint32_t priv_bytes = (priv_a + 16u * UR * 3u + 15u) & ~15u;
+  const uint32_t priv_bytes = (priv_a + (uint32_t)kNE * 3u + 15u) & ~15u;
   uint8_t* const priv = a_lds + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * priv_bytes;
   constexpr int kPS = 2;                   // 16-byte A pieces per lane
-  constexpr int kPE = (16 * UR + 63) / 64;  // scale / zero entries per lane
+  constexpr int kPE = (kNE + 63) / 64;  // scale / zero entries per lane
   u32x4_t pst[kPS];
   uint32_t pss[kPE], pzs[kPE];
   uint32_t s_delta = 0, z_delta = 0, s_words = 0, z_words = 0;
@@ -391,15 +398,25 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
         pst[i] = buf_load_b128(ar, ok ? ((uint32_t)r * (uint32_t)K + (uint32_t)kb * 128u + (uint32_t)p * 8u) * 2u
                                       : kBufferOOB);
       }
-      // scale and zero entry e = r * UR + u: row r, k-block kbase + u (its group)
+      // scale (and zero) entry e = (r * UR + u) * kSC + h: row r, k-block
+      // kbase + u, its group (int4) or chunk h's scale(s) (fp4: NVFP4 the
+      // chunk's two e4m3 bytes, MXFP4 its e8m0 byte)
 #pragma unroll
       for (int i = 0; i < kPE; ++i) {
         const int e = lane + 64 * i;
-        const int kb = kbase + e % UR;
-        const bool ok = e < 16 * UR && kb < KB;
-        const uint32_t gi = (uint32_t)((e / UR) * groups + kb);
-        pss[i] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
-        pzs[i] = has_zeros(FMT) ? buf_load_b8(zr, ok ? gi : kBufferOOB) : kSymZero;
+        const int r = e / (UR * kSC), kb = kbase + (e / kSC) % UR, c = kb * 4 + e % kSC;
+        const bool ok = e < kNE && kb < KB && (is_int4(FMT) || FULL || c < chunks);
+        if constexpr (is_int4(FMT)) {
+          const uint32_t gi = (uint32_t)(r * groups + kb);
+          pss[i] = buf_load_b16(sr, ok ? gi * 2u : kBufferOOB);
+          pzs[i] = has_zeros(FMT) ? buf_load_b8(zr, ok ? gi : kBufferOOB) : kSymZero;
+        } else if constexpr (FMT == kNvfp4) {
+          pss[i] = buf_load_b16(sr, ok ? (uint32_t)(r * groups + 2 * c) : kBufferOOB);
+          pzs[i] = 0u;
+        } else {
+          pss[i] = buf_load_b8(sr, ok ? (uint32_t)(r * groups + c) : kBufferOOB);
+          pzs[i] = 0u;
+        }
       }
     }
     // scales first: vmcnt retires in issue order, so the first k-block's
@@ -461,7 +478,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
   };
 
   const int arow = nl < arows ? nl : arows;  // row arows of the LDS copy is zeros
-  constexpr bool kF16 = PRIV && R == 1;  // the fp16 route
+  constexpr bool kF16 = PRIV && R == 1 && is_int4_g128(FMT);  // the fp16 route
   bool w16 = false;  // kF16: this wave's A copy is fp16 (set per pass, wave-uniform)
   const F16Consts fc = f16_consts();
   auto compute = [&](int kbase) {
@@ -471,29 +488,35 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
     if constexpr (PRIV) {
       // this wave's region: its A pieces (even / odd k order), the zero row,
       // its scales and zeros; read back below by the same wave only
-      // fp16 when every A value of this wave converts exactly (wave-uniform)
-      u32x4_t ph[kPS];
+      // fp16 when every A value of this wave converts exactly (wave-uniform):
+      // the fp16 pieces are written as they are converted, and rewritten in
+      // bf16 when some value did not convert (the wave's LDS writes land in
+      // order)
       if constexpr (kF16) {
         bool exact = true;
 #pragma unroll
-        for (int i = 0; i < kPS; ++i)
-          if (lane + 64 * i < arows * UR * 16) ph[i] = bf16x8_to_f16_k04(pst[i], exact);
+        for (int i = 0; i < kPS; ++i) {
+          const int qi = lane + 64 * i;
+          if (qi < arows * UR * 16) reinterpret_cast<u32x4_t*>(priv)[qi] = bf16x8_to_f16_k04(pst[i], exact);
+        }
         w16 = __ballot(!exact) == 0;
       }
+      if (!(kF16 && w16)) {
 #pragma unroll
-      for (int i = 0; i < kPS; ++i) {
-        const int qi = lane + 64 * i;
-        if (qi < arows * UR * 16)
-          reinterpret_cast<u32x4_t*>(priv)[qi] = (kF16 && w16) ? ph[i] : bf16x8_even_odd(pst[i]);
+        for (int i = 0; i < kPS; ++i) {
+          const int qi = lane + 64 * i;
+          if (qi < arows * UR * 16)
+            reinterpret_cast<u32x4_t*>(priv)[qi] = is_int4_g128(FMT) ? bf16x8_even_odd(pst[i]) : pst[i];
+        }
       }
       for (int qi = lane; qi < UR * 16; qi += 64)
         reinterpret_cast<u32x4_t*>(priv + (uint32_t)arows * UR * 256u)[qi] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < kPE; ++i) {
         const int e = lane + 64 * i;
-        if (e < 16 * UR) {
+        if (e < kNE) {
           reinterpret_cast<uint16_t*>(priv + priv_a)[e] = (uint16_t)pss[i];
-          (priv + priv_a + 32u * UR)[e] = (uint8_t)pzs[i];
+          (priv + priv_a + 2u * kNE)[e] = (uint8_t)pzs[i];
         }
       }
     }
@@ -506,8 +529,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void skinny_kernel(SkinnyGroupOf<GR
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(priv + ((uint32_t)arow * UR + u) * 256u + g * 64u);
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[u][j] = src[j];
-        sraw[u] = reinterpret_cast<const uint16_t*>(priv + priv_a)[nl * UR + u];
-        zraw[u] = (priv + priv_a + 32u * UR)[nl * UR + u];
+        const int e = (nl * UR + u) * kSC + (kSC == 4 ? g : 0);
+        sraw[u] = reinterpret_cast<const uint16_t*>(priv + priv_a)[e];
+        zraw[u] = (priv + priv_a + 2u * kNE)[e];
       }
       if constexpr (A_DMA) {
         const uint8_t* src = a_lds + a_dma_off + (size_t)wave * (UR * 4096) + u * 4096 + nl * 256;
@@ -1052,13 +1076,13 @@ hipError_t launch_k(const GroupedArgs& a, int rows, dim3 grid, dim3 block, unsig
 }
 
 // the private-staging route (PRIV): LDS = waves x this wave region
-uint32_t skinny_priv_bytes(int64_t M, int UR) {
+uint32_t skinny_priv_bytes(int64_t M, int UR, int sc) {
   const uint32_t am = (uint32_t)(M < 16 ? M : 16);
-  return ((am + 1u) * (uint32_t)UR * 256u + 16u * (uint32_t)UR * 3u + 15u) & ~15u;
+  return ((am + 1u) * (uint32_t)UR * 256u + 16u * (uint32_t)(UR * sc) * 3u + 15u) & ~15u;
 }
 template <int FMT, bool OUT_F32, int U, int R, bool FULL>
 hipError_t launch_priv(const GroupedArgs& a, int rows, dim3 grid, dim3 block) {
-  const unsigned lds = block.x / 64 * skinny_priv_bytes(a.M, U * R);
+  const unsigned lds = block.x / 64 * skinny_priv_bytes(a.M, U * R, is_int4(FMT) ? 1 : 4);
   if (a.count > 1)
     return launch_kernel(skinny_kernel<FMT, OUT_F32, U, R, false, FULL, false, false, true, true>, grid, block, lds,
                          a.stream, skinny_group<kMaxGroup>(a, rows), (int)a.M, (int)a.K, a.epi);
@@ -1149,10 +1173,10 @@ template <int FMT, bool OUT_F32, int U>
 hipError_t launch_u(const GroupedArgs& a, int waves) {
   const int rows = skinny_rows(a);
   const dim3 grid = skinny_grid(a, rows);
-  // int4 with groups of 128 and at most 8 A rows x k-blocks per wave: private
-  // staging, no barrier before the arithmetic (same bits as the A_LDS route);
-  // two virtual waves per wave as below when that still holds
-  if constexpr (is_int4_g128(FMT)) {
+  // int4 with groups of 128 and fp4, at most 8 A rows x k-blocks per wave:
+  // private staging, no barrier before the arithmetic (same bits as the
+  // A_LDS route); two virtual waves per wave as below when that still holds
+  if constexpr (is_int4_g128(FMT) || !is_int4(FMT)) {
     const int64_t prow = a.M < 16 ? a.M : 16;
     if (prow * U <= 8) {
       const int KBp = (int)((a.K / 32 + 3) / 4);
