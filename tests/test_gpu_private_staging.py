@@ -79,3 +79,32 @@ def test_private_staging_fp16_and_bf16_routes_in_one_launch(fmt):
     r = oracle.gate_ratio(narrow.double().cpu().numpy(), Cref, S, False)
     print(f"[gate] mixed fp16 / bf16 routes fmt {fmt}: {r:.3e}", flush=True)
     assert r <= 1.0
+
+
+@pytest.mark.parametrize("fmt", [w4.INT4_G128, w4.INT4_SYM])
+@pytest.mark.parametrize("N,K", [(4096, 3072), (3072, 8192)])
+def test_private_staging_two_virtual_waves_equal_one(fmt, N, K):
+    """A batched launch of 8 GEMVs has more than four rounds of workgroups, so
+    each wave runs two virtual waves of the K split; a single GEMV of the same
+    shape keeps one per wave.  Both sum the same k-blocks in the same order,
+    so every member equals its single launch bit for bit -- also when some
+    members' A holds values outside fp16's exact range (those waves take the
+    bf16 route, the others may take the fp16 one)."""
+    items, cases = [], []
+    for i in range(8):
+        case = inputs.make_case(fmt, 1, N, K, seed=300 + i)
+        if i % 2:
+            to_bf16 = lambda x: np.array([x], np.float32).view(np.uint32)[0] >> 16
+            case.A[0, (997 * i) % K] = to_bf16(2.5e-31 if i % 4 == 1 else -1.0e9)
+        cases.append(case)
+        items.append(to_dev(case))
+    outs = w4.gemm_batched(fmt, items, out_dtype=torch.float32)
+    singles = [w4.gemm(fmt, A, p, s, z, out_dtype=torch.float32) for A, p, s, z in items]
+    torch.cuda.synchronize()
+    for i, (o, s1) in enumerate(zip(outs, singles)):
+        assert torch.equal(o.view(torch.int32), s1.view(torch.int32)), f"member {i}"
+    c = cases[1]
+    Cref, S = oracle.gemm(fmt, c.A, c.packed, c.scales, c.zeros, 1, N, K)
+    r = oracle.gate_ratio(outs[1].double().cpu().numpy(), Cref, S, False)
+    print(f"[gate] two virtual waves fmt {fmt} {N}x{K}: {r:.3e}", flush=True)
+    assert r <= 1.0
