@@ -1184,6 +1184,16 @@ hipError_t launch_u(const GroupedArgs& a, int waves) {
       const bool full = a.K % 128 == 0;
       const bool halve = prow * U * 2 <= 8 && waves % 2 == 0 && waves * U >= KBp && wgs > 4 * (int64_t)device_cus();
       if (halve) {
+        // int4 at M = 1 with 12 or 16 waves: four virtual waves per wave
+        // (8 k-blocks of loads in flight per lane), measured on the decode
+        // chain's K = 3072 launches
+        if constexpr (U == 2 && is_int4_g128(FMT)) {
+          if (prow * U * 4 <= 8 && waves % 4 == 0) {
+            const dim3 quarter(64 * waves / 4);
+            return full ? launch_priv<FMT, OUT_F32, U, 4, true>(a, rows, grid, quarter)
+                        : launch_priv<FMT, OUT_F32, U, 4, false>(a, rows, grid, quarter);
+          }
+        }
         const dim3 half(64 * waves / 2);
         return full ? launch_priv<FMT, OUT_F32, U, 2, true>(a, rows, grid, half)
                     : launch_priv<FMT, OUT_F32, U, 2, false>(a, rows, grid, half);
